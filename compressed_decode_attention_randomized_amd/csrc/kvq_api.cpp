@@ -1,0 +1,129 @@
+// extern "C" entry points of libkvq: host-side validation, then one launch on
+// the caller's stream.  Nothing here allocates or synchronises.
+#include <stdint.h>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool is_lm(int32_t f) { return f == KVQ_LM2 || f == KVQ_LM3 || f == KVQ_LM4; }
+
+kvq_status check_cache(const kvq_cache *c, const char *fn) {
+  using kvq::fail;
+  if (!c) return fail(KVQ_EINVAL, "%s: cache is NULL", fn);
+  if (c->batch < 1 || c->kv_heads < 1 || c->capacity < 0)
+    return fail(KVQ_EINVAL, "%s: bad cache shape batch=%d kv_heads=%d capacity=%d", fn, c->batch, c->kv_heads,
+                c->capacity);
+  if (!kvq::valid_head_dim(c->head_dim))
+    return fail(KVQ_EUNSUPPORTED, "%s: head_dim=%d (built: 64, 128, 256)", fn, c->head_dim);
+  if (!kvq::format_bits(c->k_format)) return fail(KVQ_EINVAL, "%s: bad k_format %d", fn, c->k_format);
+  if (!is_lm(c->v_format)) return fail(KVQ_EINVAL, "%s: v_format %d is not a Lloyd-Max format", fn, c->v_format);
+  if (!c->k_codes || !c->v_codes || !c->v_norms || !c->signs || !c->v_centroids)
+    return fail(KVQ_EINVAL, "%s: NULL cache buffer", fn);
+  if (is_lm(c->k_format) && (!c->k_norms || !c->k_centroids))
+    return fail(KVQ_EINVAL, "%s: Lloyd-Max keys need k_norms and k_centroids", fn);
+  if (!aligned(c->k_codes, 16) || !aligned(c->v_codes, 16))
+    return fail(KVQ_EINVAL, "%s: code buffers must be 16-byte aligned", fn);
+  if (!aligned(c->k_norms, 2) || !aligned(c->v_norms, 2) || !aligned(c->signs, 8))
+    return fail(KVQ_EINVAL, "%s: norms must be 2-byte and signs 8-byte aligned", fn);
+  if (c->near_len < 0 || (c->near_len > 0 && (!c->near_k || !c->near_v)))
+    return fail(KVQ_EINVAL, "%s: near tier needs near_k and near_v", fn);
+  if (c->near_len > 0 && (!aligned(c->near_k, 16) || !aligned(c->near_v, 16)))
+    return fail(KVQ_EINVAL, "%s: near tier buffers must be 16-byte aligned", fn);
+  if (c->reserved != 0) return fail(KVQ_EINVAL, "%s: reserved field must be 0", fn);
+  return KVQ_OK;
+}
+
+kvq_status hip_status(hipError_t e, const char *fn) {
+  if (e != hipSuccess) return kvq::fail(KVQ_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_quantize_append(const kvq_cache *cache, const void *k, const void *v, int32_t dtype,
+                               int32_t start_pos, int32_t n_new, hipStream_t stream) {
+  const char *fn = "kvq_quantize_append";
+  kvq::clear_error();
+  kvq_status st = check_cache(cache, fn);
+  if (st != KVQ_OK) return st;
+  if (dtype != KVQ_F32 && dtype != KVQ_F16) return kvq::fail(KVQ_EINVAL, "%s: dtype %d", fn, dtype);
+  if (n_new < 0) return kvq::fail(KVQ_EINVAL, "%s: n_new=%d", fn, n_new);
+  if (start_pos < 0 || (int64_t)start_pos + n_new > cache->capacity)
+    return kvq::fail(KVQ_ERANGE, "%s: positions [%d, %lld) outside capacity %d", fn, start_pos,
+                     (long long)start_pos + n_new, cache->capacity);
+  if (n_new == 0) return KVQ_OK;
+  if (!k || !v) return kvq::fail(KVQ_EINVAL, "%s: k or v is NULL", fn);
+  if (!aligned(k, 16) || !aligned(v, 16)) return kvq::fail(KVQ_EINVAL, "%s: k and v must be 16-byte aligned", fn);
+  if ((int64_t)cache->batch * cache->kv_heads * n_new > (1ll << 31) / 64)
+    return kvq::fail(KVQ_EINVAL, "%s: too many vectors in one call", fn);
+  kvq::AppendArgs a{k, v, dtype == KVQ_F16, cache->batch, cache->kv_heads, cache->head_dim, cache->capacity,
+                    start_pos, n_new, cache->k_format, cache->v_format,
+                    static_cast<uint8_t *>(cache->k_codes), static_cast<uint8_t *>(cache->v_codes),
+                    cache->k_norms, cache->v_norms, cache->signs, cache->k_centroids, cache->v_centroids};
+  bool ok = true;
+  hipError_t e = kvq::launch_append(a, stream, &ok);
+  if (!ok) return kvq::fail(KVQ_EUNSUPPORTED, "%s: format combination not built", fn);
+  return hip_status(e, fn);
+}
+
+kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q_dtype, int32_t q_heads,
+                                int32_t seq_len, int32_t num_splits, int32_t num_near_splits, float *part_o,
+                                float *part_ml, hipStream_t stream) {
+  const char *fn = "kvq_decode_attention";
+  kvq::clear_error();
+  kvq_status st = check_cache(cache, fn);
+  if (st != KVQ_OK) return st;
+  if (!q || !part_o || !part_ml) return kvq::fail(KVQ_EINVAL, "%s: NULL q or partial buffer", fn);
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_F16) return kvq::fail(KVQ_EINVAL, "%s: q_dtype %d", fn, q_dtype);
+  if (q_heads < 1 || q_heads % cache->kv_heads)
+    return kvq::fail(KVQ_EINVAL, "%s: q_heads=%d not a multiple of kv_heads=%d", fn, q_heads, cache->kv_heads);
+  if (seq_len < 0) return kvq::fail(KVQ_EINVAL, "%s: seq_len=%d", fn, seq_len);
+  if (seq_len > cache->capacity)
+    return kvq::fail(KVQ_ERANGE, "%s: seq_len=%d > capacity=%d", fn, seq_len, cache->capacity);
+  if (num_splits < 1 || num_splits > 65535 || num_near_splits < 0 || num_near_splits > 65535)
+    return kvq::fail(KVQ_EINVAL, "%s: splits far=%d near=%d", fn, num_splits, num_near_splits);
+  if (num_near_splits > 0 && cache->near_len == 0)
+    return kvq::fail(KVQ_EINVAL, "%s: near splits requested but the cache has no near tier", fn);
+  if (num_near_splits == 0 && cache->near_len > 0)
+    return kvq::fail(KVQ_EINVAL, "%s: the cache has a near tier; give it at least one split", fn);
+  if ((int64_t)cache->batch * cache->kv_heads > 65535)
+    return kvq::fail(KVQ_EINVAL, "%s: batch*kv_heads above 65535", fn);
+  kvq::AttendArgs a{q, q_dtype == KVQ_F16, cache->batch, cache->kv_heads, q_heads, cache->head_dim,
+                    cache->capacity, seq_len, num_splits, num_near_splits, cache->near_len, cache->k_format,
+                    cache->v_format, static_cast<const uint8_t *>(cache->k_codes),
+                    static_cast<const uint8_t *>(cache->v_codes), cache->k_norms, cache->v_norms, cache->signs,
+                    cache->k_centroids, cache->v_centroids, cache->near_k, cache->near_v, part_o, part_ml};
+  bool ok = true;
+  hipError_t e = kvq::launch_attend(a, stream, &ok);
+  if (!ok)
+    return kvq::fail(KVQ_EUNSUPPORTED, "%s: group %d with formats (%d,%d) at head_dim %d not built", fn,
+                     q_heads / cache->kv_heads, cache->k_format, cache->v_format, cache->head_dim);
+  return hip_status(e, fn);
+}
+
+kvq_status kvq_merge(const kvq_cache *cache, const float *part_o, const float *part_ml, int32_t q_heads,
+                     int32_t num_splits, int32_t num_near_splits, float *out, float *lse, hipStream_t stream) {
+  const char *fn = "kvq_merge";
+  kvq::clear_error();
+  if (!cache) return kvq::fail(KVQ_EINVAL, "%s: cache is NULL", fn);
+  if (!kvq::valid_head_dim(cache->head_dim))
+    return kvq::fail(KVQ_EUNSUPPORTED, "%s: head_dim=%d", fn, cache->head_dim);
+  if (!part_o || !part_ml || !out || !cache->signs) return kvq::fail(KVQ_EINVAL, "%s: NULL buffer", fn);
+  if (cache->batch < 1 || q_heads < 1 || num_splits < 0 || num_near_splits < 0 || num_splits + num_near_splits < 1)
+    return kvq::fail(KVQ_EINVAL, "%s: bad shape", fn);
+  if ((int64_t)cache->batch * q_heads > (1ll << 31) - 1) return kvq::fail(KVQ_EINVAL, "%s: grid too large", fn);
+  kvq::MergeArgs a{part_o, part_ml, cache->batch, q_heads, cache->head_dim, num_splits, num_near_splits,
+                   cache->signs, out, lse};
+  bool ok = true;
+  hipError_t e = kvq::launch_merge(a, stream, &ok);
+  if (!ok) return kvq::fail(KVQ_EUNSUPPORTED, "%s: head_dim not built", fn);
+  return hip_status(e, fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,419 @@
+// Fused split-K GQA decode attention on the compressed cache, gfx950.
+//
+// Grid: x = split (near-tier splits first, then far-tier splits), y = (b, kv head).
+// A 256-thread work-group serves the G query heads that share one KV head, so
+// every code row is read from HBM once for all G heads.
+//
+// Per work-group:
+//   1. the G queries are loaded into LDS; for far splits they are sign-flipped
+//      and Walsh-Hadamard transformed there (the query is rotated once, keys
+//      are never rotated back); each is pre-scaled by log2(e)/sqrt(d) (near)
+//      or log2(e)/d (far: rotation normalisation times the softmax scale);
+//   2. each token row is processed by D/DPL lanes, each lane owning DPL
+//      consecutive coordinates: the lane reads its slice of the packed key row
+//      (one vector load), looks each code up in an LDS centroid table and
+//      accumulates q~ . c[code] for the G heads; the slice sums are combined by
+//      xor-shuffles and multiplied by the fp16 norm;
+//   3. online softmax per lane slot in base 2 (one exp2 per score, the running
+//      state rescaled only when the maximum grows); values are accumulated in
+//      the rotated domain straight from their codes;
+//   4. the slot states are merged by xor-shuffles inside the wave and through
+//      LDS across the four waves; the split writes (m, l) and sum p v / l.
+// Near-tier splits run the same loop on fp16 rows in the original domain.
+// Sources: "The Engineering Behind AdapTQ", "Engineering the Hot Path" (rotate
+// q once, score from codes through a table, no dequantize pass); "FoveatedKV",
+// "Making it fast" (fused split-K dispatch over both tiers, q pre-scaled,
+// online softmax with one exp per score, fp8 decode through a 256-entry table).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct Params {
+  const void *q;
+  int q_f16;
+  int kv_heads, q_heads, capacity, seq_len, num_splits, num_near_splits, near_len;
+  const uint8_t *k_codes, *v_codes;
+  const uint16_t *k_norms, *v_norms;
+  const int8_t *signs;
+  const float *k_centroids, *v_centroids;
+  const uint16_t *near_k, *near_v;
+  float *part_o, *part_ml;
+};
+
+// Loads NB bytes (NB a multiple of 2) at p into 32-bit words, using the widest
+// access the slice alignment allows.
+template <int NB>
+__device__ inline void load_slice(const uint8_t *p, uint32_t (&w)[(NB + 3) / 4]) {
+  if constexpr (NB % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) {
+      const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (NB % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 8; ++i) {
+      const uint2 v = reinterpret_cast<const uint2 *>(p)[i];
+      w[2 * i] = v.x; w[2 * i + 1] = v.y;
+    }
+  } else if constexpr (NB % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 4; ++i) w[i] = reinterpret_cast<const uint32_t *>(p)[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < (NB + 3) / 4; ++i) w[i] = 0;
+#pragma unroll
+    for (int i = 0; i < NB / 2; ++i) {
+      const uint32_t h = reinterpret_cast<const uint16_t *>(p)[i];
+      w[i >> 1] |= h << (16 * (i & 1));
+    }
+  }
+}
+
+// Code e of an LSB-first bit stream held in 32-bit words.
+template <int B>
+__device__ inline uint32_t code_at(const uint32_t *w, int e) {
+  const int o = e * B, wi = o >> 5, sh = o & 31;
+  if (sh + B <= 32) return (w[wi] >> sh) & ((1u << B) - 1u);
+  return ((w[wi] >> sh) | (w[wi + 1] << (32 - sh))) & ((1u << B) - 1u);
+}
+
+__device__ inline float half_to_float(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// OCP E4M3FN decode (for the LDS table): bias 7, subnormals m * 2^-9.
+__device__ inline float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = (e == 0) ? (float)m * 0.001953125f
+                       : __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
+  if ((c & 0x7Fu) == 0x7Fu) mag = __builtin_nanf("");
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Running softmax state of one lane slot for G heads (base-2 logits).
+template <int G, int DPL>
+struct State {
+  float m[G], l[G], acc[G][DPL];
+  __device__ void init() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+    }
+  }
+  // Adds one token with scores s[h] (already -inf if the token is absent);
+  // returns the weights p[h] for the value accumulation.
+  __device__ void add_scores(const float (&s)[G], float (&p)[G]) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (s[h] > m[h]) {
+        const float alpha = exp2f(m[h] - s[h]);
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha;
+        m[h] = s[h];
+      }
+      p[h] = (s[h] == -INFINITY) ? 0.f : exp2f(s[h] - m[h]);
+      l[h] += p[h];
+    }
+  }
+  // Merge with the state held by lane (lane ^ mask).
+  __device__ void merge_xor(int mask) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(m[h], mask);
+      const float lo = __shfl_xor(l[h], mask);
+      const float M = fmaxf(m[h], mo);
+      const float a = (m[h] == -INFINITY) ? 0.f : exp2f(m[h] - M);
+      const float b = (mo == -INFINITY) ? 0.f : exp2f(mo - M);
+      l[h] = l[h] * a + lo * b;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const float ao = __shfl_xor(acc[h][e], mask);
+        acc[h][e] = acc[h][e] * a + ao * b;
+      }
+      m[h] = M;
+    }
+  }
+};
+
+// Far tier: packed Lloyd-Max (KB in 2..4) or fp8 (KB = 8) keys, Lloyd-Max values.
+template <int D, int KB, int VB, int G, int DPL>
+struct FarTier {
+  static constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
+  static constexpr int KNB = DPL * KB / 8, VNB = DPL * VB / 8;
+  const uint8_t *krow0, *vrow0;
+  const uint16_t *kn0, *vn0;
+  const float *lutk, *lutv;
+  uint32_t kw[(KNB + 3) / 4], vw[(VNB + 3) / 4];
+  float nk, nv;
+
+  __device__ void load(int t, int ds) {
+    load_slice<KNB>(krow0 + (size_t)t * KROW + ds * KNB, kw);
+    load_slice<VNB>(vrow0 + (size_t)t * VROW + ds * VNB, vw);
+    nk = (KB == 8) ? 1.f : half_to_float(kn0[t]);
+    nv = half_to_float(vn0[t]);
+  }
+  __device__ void score(const float (&qr)[G][DPL], float (&part)[G]) const {
+#pragma unroll
+    for (int h = 0; h < G; ++h) part[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const float c = lutk[code_at<KB>(kw, e)];
+#pragma unroll
+      for (int h = 0; h < G; ++h) part[h] = fmaf(qr[h][e], c, part[h]);
+    }
+  }
+  __device__ float key_scale() const { return nk; }
+  __device__ void accumulate(const float (&p)[G], State<G, DPL> &st) const {
+    float w[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) w[h] = p[h] * nv;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const float c = lutv[code_at<VB>(vw, e)];
+#pragma unroll
+      for (int h = 0; h < G; ++h) st.acc[h][e] = fmaf(w[h], c, st.acc[h][e]);
+    }
+  }
+};
+
+// Near tier: exact fp16 rows in the original domain.
+template <int D, int G, int DPL>
+struct NearTier {
+  static constexpr int NB = DPL * 2;
+  const uint8_t *krow0, *vrow0;
+  uint32_t kw[NB / 4], vw[NB / 4];
+
+  __device__ void load(int t, int ds) {
+    load_slice<NB>(krow0 + (size_t)t * D * 2 + ds * NB, kw);
+    load_slice<NB>(vrow0 + (size_t)t * D * 2 + ds * NB, vw);
+  }
+  __device__ static float elem(const uint32_t *w, int e) { return half_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu); }
+  __device__ void score(const float (&qr)[G][DPL], float (&part)[G]) const {
+#pragma unroll
+    for (int h = 0; h < G; ++h) part[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const float k = elem(kw, e);
+#pragma unroll
+      for (int h = 0; h < G; ++h) part[h] = fmaf(qr[h][e], k, part[h]);
+    }
+  }
+  __device__ float key_scale() const { return 1.f; }
+  __device__ void accumulate(const float (&p)[G], State<G, DPL> &st) const {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const float v = elem(vw, e);
+#pragma unroll
+      for (int h = 0; h < G; ++h) st.acc[h][e] = fmaf(p[h], v, st.acc[h][e]);
+    }
+  }
+};
+
+template <int G, int DPL, int LPT, typename Tier>
+__device__ void token_loop(Tier &tier, const float (&qr)[G][DPL], State<G, DPL> &st, int t0, int t1) {
+  constexpr int TPW = 64 / LPT;
+  constexpr int TPB = TPW * kWaves;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ds = lane % LPT, ts = lane / LPT;
+  for (int base = t0; base < t1; base += TPB) {
+    const int t = base + wave * TPW + ts;
+    const bool valid = t < t1;
+    tier.load(valid ? t : t0, ds);
+    float part[G];
+    tier.score(qr, part);
+#pragma unroll
+    for (int m = 1; m < LPT; m <<= 1) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) part[h] += __shfl_xor(part[h], m);
+    }
+    float s[G], p[G];
+    const float ks = tier.key_scale();
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
+    st.add_scores(s, p);
+    tier.accumulate(p, st);
+  }
+}
+
+template <int D, int KB, int VB, int G>
+__global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
+  constexpr int DPL = (G == 1) ? 32 : 16;
+  constexpr int LPT = D / DPL;
+  static_assert(LPT >= 1 && LPT <= 64, "lane mapping");
+
+  __shared__ float qs[G][D];
+  __shared__ float lutk[KB == 8 ? 256 : 16];
+  __shared__ float lutv[16];
+  __shared__ float red_ml[kWaves][G][2];
+  __shared__ float red_acc[kWaves][G][D];
+
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / P.kv_heads, hkv = bh - b * P.kv_heads;
+  const bool near = split < P.num_near_splits;
+  const int total_splits = P.num_near_splits + P.num_splits;
+
+  // ---- query heads hkv*G .. hkv*G+G-1 into LDS, rotated for far splits ----
+  for (int i = tid; i < G * D; i += kBlock) {
+    const int h = i / D, j = i - (i / D) * D;
+    const size_t qi = ((size_t)b * P.q_heads + hkv * G + h) * D + j;
+    float v = P.q_f16 ? half_to_float(static_cast<const uint16_t *>(P.q)[qi]) : static_cast<const float *>(P.q)[qi];
+    if (!near && P.signs[j] < 0) v = -v;
+    qs[h][j] = v;
+  }
+  if (!near) {
+    if (KB == 8) {
+      for (int i = tid; i < 256; i += kBlock) lutk[i] = e4m3_value(i);
+    } else if (tid < (1 << KB)) {
+      lutk[tid] = P.k_centroids[tid];
+    }
+    if (tid < (1 << VB)) lutv[tid] = P.v_centroids[tid];
+  }
+  __syncthreads();
+  if (!near) {
+    for (int len = 1; len < D; len <<= 1) {
+      for (int i = tid; i < G * D / 2; i += kBlock) {
+        const int h = i / (D / 2), k = i - h * (D / 2);
+        const int lo = (k / len) * 2 * len + (k % len);
+        const float a = qs[h][lo], c = qs[h][lo + len];
+        qs[h][lo] = a + c;
+        qs[h][lo + len] = a - c;
+      }
+      __syncthreads();
+    }
+  }
+
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ds = lane % LPT;
+  const float prescale = near ? kLog2e / sqrtf((float)D) : kLog2e / (float)D;
+  float qr[G][DPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) qr[h][e] = qs[h][ds * DPL + e] * prescale;
+  }
+
+  State<G, DPL> st;
+  st.init();
+  if (near) {
+    const int chunk = (P.near_len + P.num_near_splits - 1) / P.num_near_splits;
+    const int t0 = min(P.near_len, split * chunk), t1 = min(P.near_len, t0 + chunk);
+    NearTier<D, G, DPL> tier;
+    const size_t base = (size_t)bh * P.near_len * D * 2;
+    tier.krow0 = reinterpret_cast<const uint8_t *>(P.near_k) + base;
+    tier.vrow0 = reinterpret_cast<const uint8_t *>(P.near_v) + base;
+    token_loop<G, DPL, LPT>(tier, qr, st, t0, t1);
+  } else {
+    const int fs = split - P.num_near_splits;
+    const int chunk = (P.seq_len + P.num_splits - 1) / P.num_splits;
+    const int t0 = min(P.seq_len, fs * chunk), t1 = min(P.seq_len, t0 + chunk);
+    FarTier<D, KB, VB, G, DPL> tier;
+    tier.krow0 = P.k_codes + (size_t)bh * P.capacity * (D * KB / 8);
+    tier.vrow0 = P.v_codes + (size_t)bh * P.capacity * (D * VB / 8);
+    tier.kn0 = P.k_norms + (size_t)bh * P.capacity;
+    tier.vn0 = P.v_norms + (size_t)bh * P.capacity;
+    tier.lutk = lutk;
+    tier.lutv = lutv;
+    token_loop<G, DPL, LPT>(tier, qr, st, t0, t1);
+  }
+
+  // ---- merge the lane slots of this wave, then the four waves ----
+#pragma unroll
+  for (int m = LPT; m < 64; m <<= 1) st.merge_xor(m);
+  if (lane < LPT) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) red_acc[wave][h][ds * DPL + e] = st.acc[h][e];
+      if (lane == 0) {
+        red_ml[wave][h][0] = st.m[h];
+        red_ml[wave][h][1] = st.l[h];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kBlock) {
+    const int h = i / D, j = i - (i / D) * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][h][0]);
+    float l = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = red_ml[w][h][0];
+      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      l += red_ml[w][h][1] * f;
+      o += red_acc[w][h][j] * f;
+    }
+    const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * total_splits + split;
+    P.part_o[row * D + j] = (l > 0.f) ? o / l : 0.f;
+    if (j == 0) {
+      P.part_ml[row * 2 + 0] = (M == -INFINITY) ? -INFINITY : M * kLn2;
+      P.part_ml[row * 2 + 1] = l;
+    }
+  }
+}
+
+template <int D, int KB, int VB, int G>
+hipError_t go(const AttendArgs &a, hipStream_t stream) {
+  Params P{a.q, a.q_f16, a.kv_heads, a.q_heads, a.capacity, a.seq_len, a.num_splits, a.num_near_splits,
+           a.near_len, a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids,
+           a.near_k, a.near_v, a.part_o, a.part_ml};
+  dim3 grid(a.num_near_splits + a.num_splits, a.batch * a.kv_heads);
+  hipLaunchKernelGGL((attend_kernel<D, KB, VB, G>), grid, dim3(kBlock), 0, stream, P);
+  return hipGetLastError();
+}
+
+template <int D, int KB, int VB>
+hipError_t by_group(const AttendArgs &a, hipStream_t stream, bool *ok) {
+  const int G = a.q_heads / a.kv_heads;
+  if (G == 1) return go<D, KB, VB, 1>(a, stream);
+  if constexpr (KB != 3 && VB != 3) {
+    if (G == 2) return go<D, KB, VB, 2>(a, stream);
+    if (G == 4) return go<D, KB, VB, 4>(a, stream);
+  }
+  *ok = false;
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t by_format(const AttendArgs &a, hipStream_t stream, bool *ok) {
+  const int kf = a.k_format, vf = a.v_format;
+  if (kf == 2 && vf == 2) return by_group<D, 2, 2>(a, stream, ok);
+  if (kf == 3 && vf == 3) return by_group<D, 3, 3>(a, stream, ok);
+  if (kf == 4 && vf == 4) return by_group<D, 4, 4>(a, stream, ok);
+  if (kf == 8 && vf == 4) return by_group<D, 8, 4>(a, stream, ok);
+  *ok = false;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported) {
+  *supported = true;
+  switch (a.head_dim) {
+    case 64: return by_format<64>(a, stream, supported);
+    case 128: return by_format<128>(a, stream, supported);
+    case 256: return by_format<256>(a, stream, supported);
+  }
+  *supported = false;
+  return hipSuccess;
+}
+
+}  // namespace kvq

