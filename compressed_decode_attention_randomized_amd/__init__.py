@@ -162,6 +162,7 @@ class KVCache:
         if not kr or not vr:
             raise ValueError("unsupported head_dim/format")
         dev = torch.device(device)
+        capacity = (capacity + 15) // 16 * 16          # the ABI wants a multiple of 16
         k_codes = torch.zeros((batch, kv_heads, capacity, kr), dtype=torch.uint8, device=dev)
         v_codes = torch.zeros((batch, kv_heads, capacity, vr), dtype=torch.uint8, device=dev)
         k_norms = torch.zeros((batch, kv_heads, capacity), dtype=torch.float16, device=dev)

@@ -24,7 +24,9 @@ ARCH = "gfx950"
 
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-munsafe-fp-atomics", "-ffp-contract=fast"]
+                "-munsafe-fp-atomics", "-ffp-contract=fast",
+                # matrix-core accumulators stay in VGPRs (no AGPR round trips around VALU rescaling)
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__"]
 
 

@@ -27,8 +27,9 @@ kvq_status check_cache(const kvq_cache *c, const char *fn) {
     return fail(KVQ_EINVAL, "%s: Lloyd-Max keys need k_norms and k_centroids", fn);
   if (!aligned(c->k_codes, 16) || !aligned(c->v_codes, 16))
     return fail(KVQ_EINVAL, "%s: code buffers must be 16-byte aligned", fn);
-  if (!aligned(c->k_norms, 2) || !aligned(c->v_norms, 2) || !aligned(c->signs, 8))
-    return fail(KVQ_EINVAL, "%s: norms must be 2-byte and signs 8-byte aligned", fn);
+  if (!aligned(c->k_norms, 16) || !aligned(c->v_norms, 16) || !aligned(c->signs, 8))
+    return fail(KVQ_EINVAL, "%s: norms must be 16-byte and signs 8-byte aligned", fn);
+  if (c->capacity % 16) return fail(KVQ_EINVAL, "%s: capacity %d is not a multiple of 16", fn, c->capacity);
   if (c->near_len < 0 || (c->near_len > 0 && (!c->near_k || !c->near_v)))
     return fail(KVQ_EINVAL, "%s: near tier needs near_k and near_v", fn);
   if (c->near_len > 0 && (!aligned(c->near_k, 16) || !aligned(c->near_v, 16)))

@@ -79,7 +79,7 @@ typedef enum { KVQ_LM2 = 2, KVQ_LM3 = 3, KVQ_LM4 = 4, KVQ_FP8_E4M3 = 8 } kvq_for
  *            k_centroids is unused (may be NULL) for FP8 keys
  *   near_k, near_v  two-tier caches only: [batch][kv_heads][near_len][head_dim]
  *            fp16 bits in the original (unrotated) domain; NULL with near_len 0
- * Code buffers must be 16-byte aligned. */
+ * Code and norm buffers must be 16-byte aligned and capacity a multiple of 16. */
 typedef struct kvq_cache {
   int32_t batch;
   int32_t kv_heads;
@@ -135,7 +135,9 @@ kvq_status kvq_quantize_append(const kvq_cache *cache, const void *k, const void
  * the Hot Path"; "Making it fast").  For each batch entry b and query head h
  * (KV head h / (q_heads / kv_heads)):
  *   far splits:  tokens [0, seq_len) of the code buffers, cut into num_splits
- *                contiguous chunks of ceil(seq_len / num_splits) tokens;
+ *                contiguous chunks of C = ceil(seq_len / num_splits) tokens
+ *                rounded up to a multiple of 16 (split s covers
+ *                [s*C, min((s+1)*C, seq_len)); trailing splits may be empty);
  *                scores s_t = (R q) . khat_t / sqrt(d) with khat the rotated
  *                reconstruction; values accumulated in the rotated domain.
  *   near splits: tokens [0, near_len) of near_k/near_v cut the same way into

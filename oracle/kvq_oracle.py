@@ -497,13 +497,15 @@ def attention_original_domain(q, k_rot, v_rot, signs):
     return np.einsum("bht,bhtd->bhd", p, v)
 
 
-def split_bounds(T: int, S: int):
-    """Contiguous chunks of ceil(T/S) tokens; trailing chunks may be empty."""
+def split_bounds(T: int, S: int, align: int = 1):
+    """Contiguous chunks of ceil(T/S) tokens, that size rounded up to a multiple
+    of `align`; trailing chunks may be empty."""
     step = -(-T // S) if S else 0
+    step = -(-step // align) * align
     return [(min(T, i * step), min(T, (i + 1) * step)) for i in range(S)]
 
 
-def attention_partials(q_rot_scaled: np.ndarray, k: np.ndarray, v: np.ndarray, S: int):
+def attention_partials(q_rot_scaled: np.ndarray, k: np.ndarray, v: np.ndarray, S: int, align: int = 1):
     """Split-K partial softmax states for one (query head, KV stream).
 
     q_rot_scaled: [d] query already in the domain of k and divided by sqrt(d);
@@ -511,7 +513,7 @@ def attention_partials(q_rot_scaled: np.ndarray, k: np.ndarray, v: np.ndarray, S
     normalised output (sum p v / l); an empty chunk gives m=-inf, l=0, o=0."""
     T, d = k.shape
     ms, ls, os_ = [], [], []
-    for a, b in split_bounds(T, S):
+    for a, b in split_bounds(T, S, align):
         if a == b:
             ms.append(-math.inf); ls.append(0.0); os_.append(np.zeros(d))
             continue

@@ -97,8 +97,8 @@ def test_brute_force_tiny_every_code_pattern():
         assert np.allclose(o, ref, atol=1e-14)
 
 
-@pytest.mark.parametrize("S", [1, 2, 3, 7, 64, 100])
-def test_split_merge_invariance(S):
+@pytest.mark.parametrize("S,align", [(1, 1), (2, 1), (3, 1), (7, 1), (64, 1), (100, 1), (3, 16), (7, 16)])
+def test_split_merge_invariance(S, align):
     rng = np.random.default_rng(6)
     d, T = 64, 97
     k = rng.standard_normal((T, d)) * 3
@@ -106,11 +106,12 @@ def test_split_merge_invariance(S):
     q = rng.standard_normal(d) / math.sqrt(d)
     s = k @ q
     p = np.exp(s - s.max()); p /= p.sum()
-    m, l, o = O.attention_partials(q, k, v, S)
+    m, l, o = O.attention_partials(q, k, v, S, align)
     out, lse = O.merge_partials(m, l, o)
     assert np.allclose(out, p @ v, atol=1e-13)
     assert lse == pytest.approx(s.max() + math.log(np.exp(s - s.max()).sum()), abs=1e-12)
-    bounds = O.split_bounds(T, S)
+    bounds = O.split_bounds(T, S, align)
+    assert all((a % align == 0) for a, _ in bounds)
     assert bounds[0][0] == 0 and bounds[-1][1] == T
     assert all(b0 == a1 for (_, b0), (a1, _) in zip(bounds, bounds[1:]))
 

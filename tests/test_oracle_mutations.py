@@ -78,7 +78,7 @@ def test_merge_without_rescale_is_caught(monkeypatch):
         W = l.sum()
         return (l[:, None] * o).sum(axis=0) / W, float(np.max(m))
     monkeypatch.setattr(O, "merge_partials", bad)
-    _fails(TA.test_split_merge_invariance, 7)
+    _fails(TA.test_split_merge_invariance, 7, 1)
 
 
 def test_gqa_head_map_mod_instead_of_div_is_caught(monkeypatch):
