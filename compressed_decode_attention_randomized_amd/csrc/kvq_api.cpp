@@ -27,8 +27,8 @@ kvq_status check_cache(const kvq_cache *c, const char *fn) {
     return fail(KVQ_EINVAL, "%s: Lloyd-Max keys need k_norms and k_centroids", fn);
   if (!aligned(c->k_codes, 16) || !aligned(c->v_codes, 16))
     return fail(KVQ_EINVAL, "%s: code buffers must be 16-byte aligned", fn);
-  if (!aligned(c->k_norms, 16) || !aligned(c->v_norms, 16) || !aligned(c->signs, 8))
-    return fail(KVQ_EINVAL, "%s: norms must be 16-byte and signs 8-byte aligned", fn);
+  if (!aligned(c->k_norms, 16) || !aligned(c->v_norms, 16) || !aligned(c->signs, 16))
+    return fail(KVQ_EINVAL, "%s: norms and signs must be 16-byte aligned", fn);
   if (c->capacity % 16) return fail(KVQ_EINVAL, "%s: capacity %d is not a multiple of 16", fn, c->capacity);
   if (c->near_len < 0 || (c->near_len > 0 && (!c->near_k || !c->near_v)))
     return fail(KVQ_EINVAL, "%s: near tier needs near_k and near_v", fn);
@@ -81,6 +81,7 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q
   kvq_status st = check_cache(cache, fn);
   if (st != KVQ_OK) return st;
   if (!q || !part_o || !part_ml) return kvq::fail(KVQ_EINVAL, "%s: NULL q or partial buffer", fn);
+  if (!aligned(q, 16)) return kvq::fail(KVQ_EINVAL, "%s: q must be 16-byte aligned", fn);
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_F16) return kvq::fail(KVQ_EINVAL, "%s: q_dtype %d", fn, q_dtype);
   if (q_heads < 1 || q_heads % cache->kv_heads)
     return kvq::fail(KVQ_EINVAL, "%s: q_heads=%d not a multiple of kv_heads=%d", fn, q_heads, cache->kv_heads);

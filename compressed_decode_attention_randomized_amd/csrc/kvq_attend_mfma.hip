@@ -21,11 +21,12 @@
 // centroid's (hi, lo) pair, so one 32-bit lookup is one operand register.
 //
 // Work mapping: grid (split, b * Hkv); 4 waves per work-group, each wave
-// walking 16-token tiles of the split; one tile = 1 KB of key codes loaded as
-// one 16-byte slice per lane (d=128, 4-bit).  Lane (g, n) = (lane / 16,
-// lane % 16): its key slice is token n, coordinates [g*d/4, (g+1)*d/4); its
-// scores are tokens 4g..4g+3 for head n % 8; its value codes are tokens
-// 4g..4g+3, coordinates [n*d/16, (n+1)*d/16).
+// walking batches of two 16-token tiles of the split.  Lane (g, n) =
+// (lane / 16, lane % 16): its key slice is token n of the tile, coordinates
+// [g*d/4, (g+1)*d/4) (one 16-byte load at d=128, 4-bit); its scores are
+// tokens 4g..4g+3 for head n % 8; its value codes are tokens 4g..4g+3,
+// coordinates [n*d/16, (n+1)*d/16).  All loads are buffer loads with the
+// cache arrays as SGPR resources and 32-bit lane offsets.
 // Sources: "The Engineering Behind AdapTQ", "Engineering the Hot Path"
 // (rotate q once, score from codes through a table, no dequantize pass);
 // "FoveatedKV", "Making it fast" (split-K, q pre-scaled, online softmax with
@@ -42,14 +43,17 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
 constexpr int kTile = 16;
+constexpr int kBatch = 1;                      // 16-token tiles per wave iteration
 constexpr int kGMax = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kCodeScale = 256.f;   // centroid scale: keeps the low fp16 half a normal number
+constexpr float kCodeScale = 256.f;            // centroid scale: keeps the low fp16 half a normal number
+constexpr int kRawBufferFlags = 0x00020000;    // 32-bit data format, untyped raw access
 
 struct MParams {
   const void *q;
@@ -79,31 +83,32 @@ __device__ inline uint32_t split_entry(float x) {
 
 __device__ inline float half_value(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
 
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRawBufferFlags);
+}
+
+// NB bytes at byte offset off of a buffer into 32-bit words (NB in {2,4,8,16,32}).
 template <int NB>
-__device__ inline void load_bytes(const uint8_t *p, uint32_t (&w)[(NB + 3) / 4]) {
+__device__ inline void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[(NB + 3) / 4]) {
   if constexpr (NB % 16 == 0) {
 #pragma unroll
     for (int i = 0; i < NB / 16; ++i) {
-      const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+      const uint4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
       w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
     }
-  } else if constexpr (NB % 8 == 0) {
-#pragma unroll
-    for (int i = 0; i < NB / 8; ++i) {
-      const uint2 v = reinterpret_cast<const uint2 *>(p)[i];
-      w[2 * i] = v.x; w[2 * i + 1] = v.y;
-    }
-  } else if constexpr (NB % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < NB / 4; ++i) w[i] = reinterpret_cast<const uint32_t *>(p)[i];
+  } else if constexpr (NB == 8) {
+    const uint2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (NB == 4) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   } else {
     static_assert(NB == 2, "slice size");
-    w[0] = *reinterpret_cast<const uint16_t *>(p);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
   }
 }
 
 // (byte K of v) * 4 in one VALU op: SDWA selects the byte as the shifted
-// operand.  Used to turn a byte holding one code into an LDS table offset.
+// operand.  Turns a byte holding one code into an LDS table offset.
 template <int K>
 __device__ inline uint32_t byte_x4(uint32_t v) {
   uint32_t r;
@@ -139,28 +144,121 @@ __device__ inline float row_swap8(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
 }
 
-template <int KB, int NW, int E = 0>
-__device__ inline void key_scores_word(const CodePlanes<KB> &cp, const uint32_t (*bk)[4], const uint32_t *lutk,
-                                       float4_t &dk, int kb0) {
+// Max / sum over the four 16-lane rows that hold one column, with the gfx950
+// row swaps (VALU, no LDS): after v_permlane16_swap on two copies of x, each
+// lane holds its own value in one copy and its xor-16 partner's in the other;
+// v_permlane32_swap does the same for xor 32.
+__device__ inline void swap16(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ inline void swap32(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ inline float max_rows(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  x = fmaxf(a, b);
+  a = x;
+  b = x;
+  swap32(a, b);
+  return fmaxf(a, b);
+}
+__device__ inline float sum_rows(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  x = a + b;
+  a = x;
+  b = x;
+  swap32(a, b);
+  return a + b;
+}
+
+template <int D, int KB, int VB>
+struct Geometry {
+  static constexpr int NKB = D / 16;          // key MFMAs per tile (16 coordinates each)
+  static constexpr int KSL = D * KB / 32;     // key bytes per lane slice (d/4 coordinates)
+  static constexpr int VDL = D / 16;          // value coordinates per lane
+  static constexpr int VSL = VDL * VB / 8;    // value bytes per lane per token
+  static constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
+  static constexpr int KW = (KSL + 3) / 4, VW = (VSL + 3) / 4;
+};
+
+template <int D, int KB, int VB>
+struct Tile {
+  using Gm = Geometry<D, KB, VB>;
+  uint32_t kw[Gm::KW];
+  uint32_t vw[4][Gm::VW];
+  uint32_t kn[2], vn[2];                       // fp16 norms of tokens ts..ts+3
+};
+
+struct Sources {
+  __amdgpu_buffer_rsrc_t kc, vc, kn, vn;
+};
+
+template <int D, int KB, int VB>
+__device__ inline void load_tile(Tile<D, KB, VB> &t, const Sources &src, int tb, int g, int n) {
+  using Gm = Geometry<D, KB, VB>;
+  buf_load<Gm::KSL>(src.kc, (uint32_t)(tb + n) * Gm::KROW + g * Gm::KSL, t.kw);
+  const int ts = tb + 4 * g;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) buf_load<Gm::VSL>(src.vc, (uint32_t)(ts + i) * Gm::VROW + n * Gm::VSL, t.vw[i]);
+  buf_load<8>(src.kn, (uint32_t)ts * 2, t.kn);
+  buf_load<8>(src.vn, (uint32_t)ts * 2, t.vn);
+}
+
+template <int KB, int E>
+__device__ inline half8_t key_operand(const CodePlanes<KB> &c, const uint32_t *lutk) {
+  return as_half8(lut_read(lutk, c.template addr<E>()), lut_read(lutk, c.template addr<E + 1>()),
+                  lut_read(lutk, c.template addr<E + 2>()), lut_read(lutk, c.template addr<E + 3>()));
+}
+
+// Key products of one code word of both tiles, k-blocks interleaved so the two
+// accumulation chains overlap.
+template <int KB, int W, int E = 0>
+__device__ inline void key_word(const CodePlanes<KB> &c0, const CodePlanes<KB> &c1, const uint32_t (*bk)[4],
+                                const uint32_t *lutk, float4_t &d0, float4_t &d1) {
   constexpr int KCW = 32 / KB;
   if constexpr (E < KCW) {
-    const half8_t a = as_half8(lut_read(lutk, cp.template addr<E + 0>()), lut_read(lutk, cp.template addr<E + 1>()),
-                               lut_read(lutk, cp.template addr<E + 2>()), lut_read(lutk, cp.template addr<E + 3>()));
-    const int kb = kb0 + E / 4;
+    constexpr int kb = (W * KCW + E) / 4;
     const half8_t bq = as_half8(bk[kb][0], bk[kb][1], bk[kb][2], bk[kb][3]);
-    dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, dk, 0, 0, 0);
-    key_scores_word<KB, NW, E + 4>(cp, bk, lutk, dk, kb0);
+    const half8_t a0 = key_operand<KB, E>(c0, lutk);
+    const half8_t a1 = key_operand<KB, E>(c1, lutk);
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bq, d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bq, d1, 0, 0, 0);
+    key_word<KB, W, E + 4>(c0, c1, bk, lutk, d0, d1);
   }
 }
 
-// Key tile product: lane's NW code words (4 coordinates per MFMA k-block).
-template <int KB, int NW>
-__device__ inline void key_scores(const uint32_t *kw, const uint32_t (*bk)[4], const uint32_t *lutk, float4_t &dk) {
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    CodePlanes<KB> cp;
-    cp.set(kw[w]);
-    key_scores_word<KB, NW>(cp, bk, lutk, dk, w * (32 / KB) / 4);
+template <int KB, int W, int E = 0>
+__device__ inline void key_word1(const CodePlanes<KB> &c0, const uint32_t (*bk)[4], const uint32_t *lutk, float4_t &d0) {
+  constexpr int KCW = 32 / KB;
+  if constexpr (E < KCW) {
+    constexpr int kb = (W * KCW + E) / 4;
+    const half8_t bq = as_half8(bk[kb][0], bk[kb][1], bk[kb][2], bk[kb][3]);
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<KB, E>(c0, lutk), bq, d0, 0, 0, 0);
+    key_word1<KB, W, E + 4>(c0, bk, lutk, d0);
+  }
+}
+
+template <int KB, int KW, int W = 0>
+__device__ inline void key_scores1(const uint32_t (&kw0)[KW], const uint32_t (*bk)[4], const uint32_t *lutk, float4_t &d0) {
+  if constexpr (W < KW) {
+    CodePlanes<KB> c0;
+    c0.set(kw0[W]);
+    key_word1<KB, W>(c0, bk, lutk, d0);
+    key_scores1<KB, KW, W + 1>(kw0, bk, lutk, d0);
+  }
+}
+
+template <int KB, int KW, int W = 0>
+__device__ inline void key_scores(const uint32_t (&kw0)[KW], const uint32_t (&kw1)[KW], const uint32_t (*bk)[4],
+                                  const uint32_t *lutk, float4_t &d0, float4_t &d1) {
+  if constexpr (W < KW) {
+    CodePlanes<KB> c0, c1;
+    c0.set(kw0[W]);
+    c1.set(kw1[W]);
+    key_word<KB, W>(c0, c1, bk, lutk, d0, d1);
+    key_scores<KB, KW, W + 1>(kw0, kw1, bk, lutk, d0, d1);
   }
 }
 
@@ -178,7 +276,7 @@ __device__ inline void value_update_dt(const CodePlanes<VB> (&vp)[4][NW], const 
 
 // Value tile product: tokens ts..ts+3 (one code word set each), VDL coordinate tiles.
 template <int VB, int VDL, int NW>
-__device__ inline void value_update(const uint32_t (*vw)[NW], const uint32_t *lutv, const half8_t &aw,
+__device__ inline void value_update(const uint32_t (&vw)[4][NW], const uint32_t *lutv, const half8_t &aw,
                                     float4_t (&dv)[VDL]) {
   CodePlanes<VB> vp[4][NW];
 #pragma unroll
@@ -189,56 +287,83 @@ __device__ inline void value_update(const uint32_t (*vw)[NW], const uint32_t *lu
   value_update_dt<VB, VDL, NW>(vp, lutv, aw, dv);
 }
 
-// Reductions across the four 16-lane rows of the wave.
-__device__ inline float max_rows(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
-}
-__device__ inline float sum_rows(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
-}
+// One batch (two tiles) of the online softmax.  TAIL masks tokens at or past
+// t1; full batches skip every per-token test.
+template <bool TAIL, int D, int KB, int VB>
+__device__ inline void process_batch(const Tile<D, KB, VB> (&cur)[kBatch], const uint32_t (*bk)[4], const uint32_t *lutk,
+                                     const uint32_t *lutv, float sfac, int tb, int t1, int g, int n,
+                                     float4_t (&dv)[Geometry<D, KB, VB>::VDL], float &m_run, float &l_run) {
+  using Gm = Geometry<D, KB, VB>;
+  float4_t dk[kBatch];
+  if constexpr (kBatch == 2) {
+    dk[0] = dk[1] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    key_scores<KB, Gm::KW>(cur[0].kw, cur[1].kw, bk, lutk, dk[0], dk[1]);
+  } else {
+    dk[0] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    key_scores1<KB, Gm::KW>(cur[0].kw, bk, lutk, dk[0]);
+  }
 
-template <int D, int KB, int VB>
-struct Tile {
-  static constexpr int KSL = D * KB / 32, VDL = D / 16, VSL = VDL * VB / 8;
-  uint32_t kw[(KSL + 3) / 4];
-  uint32_t vw[4][(VSL + 3) / 4];
-  uint2 kn, vn;                                   // fp16 norms of tokens ts..ts+3
-};
-
-template <int D, int KB, int VB>
-__device__ inline void load_tile(Tile<D, KB, VB> &t, const uint8_t *krow, const uint8_t *vrow, const uint16_t *kn,
-                                 const uint16_t *vn, int tb, int g, int n) {
-  using T = Tile<D, KB, VB>;
-  constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
-  load_bytes<T::KSL>(krow + (size_t)(tb + n) * KROW, t.kw);
-  const int ts = tb + 4 * g;
+  float s[kBatch][4];
+  float mt = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_bytes<T::VSL>(vrow + (size_t)(ts + i) * VROW, t.vw[i]);
-  t.kn = *reinterpret_cast<const uint2 *>(kn + ts);
-  t.vn = *reinterpret_cast<const uint2 *>(vn + ts);
+  for (int u = 0; u < kBatch; ++u) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float nk = half_value((cur[u].kn[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+      float v = (dk[u][i] + row_swap8(dk[u][i])) * (nk * sfac);
+      if constexpr (TAIL) v = (tb + u * kTile + 4 * g + i < t1) ? v : -INFINITY;
+      s[u][i] = v;
+      mt = fmaxf(mt, v);
+    }
+  }
+  mt = max_rows(mt);
+
+  if (__builtin_amdgcn_ballot_w64(mt > m_run) != 0) {
+    const float mn = fmaxf(m_run, mt);
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+    l_run *= alpha;
+    m_run = mn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, (4 * g + i) & 7);
+#pragma unroll
+      for (int dt = 0; dt < Gm::VDL; ++dt) dv[dt][i] *= ai;
+    }
+  }
+
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    uint32_t av[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p = __builtin_amdgcn_exp2f(s[u][i] - m_run);
+      if constexpr (TAIL) p = (s[u][i] == -INFINITY) ? 0.f : p;
+      l_run += p;
+      const float nv = half_value((cur[u].vn[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+      float w = p * nv;
+      if constexpr (TAIL) w = (p > 0.f) ? w : 0.f;
+      const _Float16 hi = (_Float16)w;
+      const _Float16 part = (n < 8) ? hi : (_Float16)(w - (float)hi);
+      av[i] = pack2(part, part);
+    }
+    const half8_t aw = as_half8(av[0], av[1], av[2], av[3]);
+    value_update<VB, Gm::VDL, Gm::VW>(cur[u].vw, lutv, aw, dv);
+  }
 }
 
-constexpr int kBatch = 2;          // 16-token tiles per wave iteration
-
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(kBlock) void attend_mfma_kernel(MParams P) {
-  constexpr int NKB = D / 16;                 // key MFMAs per tile (16 coordinates each)
-  constexpr int KSL = D * KB / 32;            // key bytes per lane slice (d/4 coordinates)
-  constexpr int VDL = D / 16;                 // value coordinates per lane
-  constexpr int VSL = VDL * VB / 8;           // value bytes per lane per token
-  constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
-  constexpr int QP = D + 4;                   // padded query row (LDS banks)
+__global__ __launch_bounds__(kBlock, 4) void attend_mfma_kernel(MParams P) {
+  using Gm = Geometry<D, KB, VB>;
+  constexpr int NKB = Gm::NKB, VDL = Gm::VDL;
   constexpr int STEP = kWaves * kBatch * kTile;
   static_assert(KB == 2 || KB == 4, "key bits");
   static_assert(VB == 2 || VB == 4, "value bits");
 
   __shared__ uint32_t lutk[16], lutv[16];
-  __shared__ float qz[kGMax * QP];
-  __shared__ float qmax[kGMax];
   __shared__ float red_ml[kWaves][kGMax][2];
   __shared__ float red_acc[kWaves][16][D + 4];
+  __shared__ __attribute__((aligned(16))) uint32_t qent[kGMax][D + 4];
+  __shared__ float qfac[kGMax];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -249,75 +374,92 @@ __global__ __launch_bounds__(kBlock) void attend_mfma_kernel(MParams P) {
   // chunks of ceil(T/S) tokens rounded up to a multiple of the tile
   const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + kTile - 1) / kTile * kTile;
   const int t0 = min(P.seq_len, split * chunk), t1 = min(P.seq_len, t0 + chunk);
-  const uint8_t *krow = P.k_codes + (size_t)bh * P.capacity * KROW + g * KSL;
-  const uint8_t *vrow = P.v_codes + (size_t)bh * P.capacity * VROW + n * VSL;
-  const uint16_t *kn = P.k_norms + (size_t)bh * P.capacity;
-  const uint16_t *vn = P.v_norms + (size_t)bh * P.capacity;
+  const uint32_t cap = (uint32_t)P.capacity;
+  Sources src;
+  src.kc = make_rsrc(P.k_codes + (size_t)bh * cap * Gm::KROW, cap * Gm::KROW);
+  src.vc = make_rsrc(P.v_codes + (size_t)bh * cap * Gm::VROW, cap * Gm::VROW);
+  src.kn = make_rsrc(P.k_norms + (size_t)bh * cap, cap * 2);
+  src.vn = make_rsrc(P.v_norms + (size_t)bh * cap, cap * 2);
 
-  // first batch in flight before the prologue; a tile that starts past the
-  // split end reloads the batch's first tile (all its tokens are masked)
+  // first batch in flight before the prologue; tiles stay inside the cache
+  // (t0 and the capacity are multiples of 16) and tokens past t1 are masked
   Tile<D, KB, VB> cur[kBatch], nxt[kBatch];
   int tb = t0 + wave * kBatch * kTile;
   if (tb < t1) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) load_tile(cur[u], krow, vrow, kn, vn, (tb + u * kTile < t1) ? tb + u * kTile : tb, g, n);
+    for (int u = 0; u < kBatch; ++u) load_tile(cur[u], src, (tb + u * kTile < t1) ? tb + u * kTile : tb, g, n);
   }
 
-  // ---- centroid tables and the sign-flipped queries ----
+  // ---- rotated queries, shared by the work-group ----
+  // Wave w rotates heads w and w+4: lane l holds coordinates [l*E1, (l+1)*E1);
+  // sign flip, Walsh-Hadamard stages of stride < E1 inside the lane, strides
+  // E1..32*E1 across lanes (xor 1..32).  Each rotated coordinate z, scaled so
+  // that max |z| of its head lies in (64, 128], is stored as an fp16 (hi, lo)
+  // pair; the row stride D+4 keeps the later 16-byte reads conflict-free.
+  constexpr int E1 = D / 64;
+  for (int h = wave; h < G; h += kWaves) {
+    float z[E1];
+    const size_t qoff = ((size_t)b * P.q_heads + hkv * G + h) * D + lane * E1;
+    if (P.q_f16) {
+      const uint16_t *qs = static_cast<const uint16_t *>(P.q) + qoff;
+#pragma unroll
+      for (int e = 0; e < E1; ++e) z[e] = half_value(qs[e]);
+    } else {
+      const float *qs = static_cast<const float *>(P.q) + qoff;
+#pragma unroll
+      for (int e = 0; e < E1; ++e) z[e] = qs[e];
+    }
+#pragma unroll
+    for (int e = 0; e < E1; ++e) z[e] = (P.signs[lane * E1 + e] < 0) ? -z[e] : z[e];
+#pragma unroll
+    for (int st = 1; st < E1; st <<= 1) {
+#pragma unroll
+      for (int e = 0; e < E1; ++e) {
+        if (!(e & st)) {
+          const float a = z[e], c = z[e + st];
+          z[e] = a + c;
+          z[e + st] = a - c;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int e = 0; e < E1; ++e) {
+        const float o = __shfl_xor(z[e], m);
+        z[e] = upper ? (o - z[e]) : (z[e] + o);
+      }
+    }
+    float zmax = 0.f;
+#pragma unroll
+    for (int e = 0; e < E1; ++e) zmax = fmaxf(zmax, fabsf(z[e]));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, m));
+    const float qscale = (zmax > 0.f) ? exp2f(7.f - ceilf(log2f(zmax))) : 1.f;
+#pragma unroll
+    for (int e = 0; e < E1; ++e) qent[h][lane * E1 + e] = split_entry(z[e] * qscale);
+    if (lane == 0) qfac[h] = kLog2e / ((float)D * kCodeScale * qscale);
+  }
   if (tid < (1 << KB)) lutk[tid] = split_entry(P.k_centroids[tid] * kCodeScale);
   if (tid >= 64 && tid < 64 + (1 << VB)) lutv[tid - 64] = split_entry(P.v_centroids[tid - 64] * kCodeScale);
-  for (int i = tid; i < kGMax * D; i += kBlock) {
-    const int h = i / D, j = i - (i / D) * D;
-    float v = 0.f;
-    if (h < G) {
-      const size_t qi = ((size_t)b * P.q_heads + hkv * G + h) * D + j;
-      v = P.q_f16 ? half_value(static_cast<const uint16_t *>(P.q)[qi]) : static_cast<const float *>(P.q)[qi];
-      if (P.signs[j] < 0) v = -v;
-    }
-    qz[h * QP + j] = v;
-  }
-  __syncthreads();
-  // unnormalised Walsh-Hadamard transform of each query (Sylvester order)
-  for (int len = 1; len < D; len <<= 1) {
-    for (int i = tid; i < G * (D / 2); i += kBlock) {
-      const int h = i / (D / 2), k = i - h * (D / 2);
-      const int lo = (k / len) * 2 * len + (k % len);
-      const float a = qz[h * QP + lo], c = qz[h * QP + lo + len];
-      qz[h * QP + lo] = a + c;
-      qz[h * QP + lo + len] = a - c;
-    }
-    __syncthreads();
-  }
-  if (wave == 0) {
-    for (int h = 0; h < G; ++h) {
-      float m = 0.f;
-      for (int j = lane; j < D; j += 64) m = fmaxf(m, fabsf(qz[h * QP + j]));
-      m = max_rows(m);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-      if (lane == 0) qmax[h] = m;
-    }
-  }
   __syncthreads();
 
   // ---- key-side B operand: column n serves head n % 8 ----
+  // columns 0..7 take (z_hi, z_hi), columns 8..15 take (z_lo, 0); columns of
+  // heads >= G carry zeros and feed only value rows that are never read
   const int hq = n & 7;
   const bool col_live = hq < G;
-  float qscale = 1.f;
-  if (col_live && qmax[hq] > 0.f) qscale = exp2f(7.f - ceilf(log2f(qmax[hq])));   // max |z * qscale| in (64, 128]
+  const uint32_t sel = (n < 8) ? 0x01000100u : 0x0C0C0302u;   // v_perm byte selectors
   uint32_t bk[NKB][4];
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
+  for (int k4 = 0; k4 < NKB; ++k4) {
+    uint4_t e = {0u, 0u, 0u, 0u};
+    if (col_live) e = *reinterpret_cast<const uint4_t *>(&qent[hq][g * (D / 4) + 4 * k4]);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float z = col_live ? qz[hq * QP + g * (D / 4) + 4 * kb + p] * qscale : 0.f;
-      const _Float16 hi = (_Float16)z;
-      const _Float16 lo = (_Float16)(z - (float)hi);
-      bk[kb][p] = (n < 8) ? pack2(hi, hi) : pack2(lo, (_Float16)0.f);
-    }
+    for (int p = 0; p < 4; ++p) bk[k4][p] = __builtin_amdgcn_perm(e[p], e[p], sel);
   }
-  // score in base-2 units = norm * (column h + column h+8) * sfac
-  const float sfac = col_live ? kLog2e / ((float)D * kCodeScale * qscale) : 0.f;
+  const float sfac = col_live ? qfac[hq] : 0.f;
 
   float4_t dv[VDL];
 #pragma unroll
@@ -328,61 +470,12 @@ __global__ __launch_bounds__(kBlock) void attend_mfma_kernel(MParams P) {
     const int tn = tb + STEP;
     if (tn < t1) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) load_tile(nxt[u], krow, vrow, kn, vn, (tn + u * kTile < t1) ? tn + u * kTile : tn, g, n);
+      for (int u = 0; u < kBatch; ++u) load_tile(nxt[u], src, (tn + u * kTile < t1) ? tn + u * kTile : tn, g, n);
     }
-
-    // ---- scores of tokens ts..ts+3 of each tile for head hq ----
-    float4_t dk[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      dk[u] = (float4_t){0.f, 0.f, 0.f, 0.f};
-      key_scores<KB, KSL / 4>(cur[u].kw, bk, lutk, dk[u]);
-    }
-    float s[kBatch][4];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int ts = tb + u * kTile + 4 * g;
-      const uint32_t knw[2] = {cur[u].kn.x, cur[u].kn.y};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float nk = half_value((knw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-        const float v = (dk[u][i] + row_swap8(dk[u][i])) * (nk * sfac);
-        s[u][i] = (col_live && ts + i < t1) ? v : -INFINITY;
-        mt = fmaxf(mt, s[u][i]);
-      }
-    }
-    mt = max_rows(mt);
-
-    if (__builtin_amdgcn_ballot_w64(mt > m_run) != 0) {
-      const float mn = fmaxf(m_run, mt);
-      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
-      l_run *= alpha;
-      m_run = mn;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, (4 * g + i) & 7);
-#pragma unroll
-        for (int dt = 0; dt < VDL; ++dt) dv[dt][i] *= ai;
-      }
-    }
-
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const uint32_t vnw[2] = {cur[u].vn.x, cur[u].vn.y};
-      uint32_t av[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = (s[u][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[u][i] - m_run);
-        l_run += p;
-        const float nv = half_value((vnw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-        const float w = (p > 0.f) ? p * nv : 0.f;
-        const _Float16 hi = (_Float16)w;
-        const _Float16 part = (n < 8) ? hi : (_Float16)(w - (float)hi);
-        av[i] = pack2(part, part);
-      }
-      const half8_t aw = as_half8(av[0], av[1], av[2], av[3]);
-      value_update<VB, VDL, (VSL + 3) / 4>(cur[u].vw, lutv, aw, dv);
+    if (tb + kBatch * kTile <= t1) {
+      process_batch<false>(cur, bk, lutk, lutv, sfac, tb, t1, g, n, dv, m_run, l_run);
+    } else {
+      process_batch<true>(cur, bk, lutk, lutv, sfac, tb, t1, g, n, dv, m_run, l_run);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) cur[u] = nxt[u];
@@ -447,7 +540,9 @@ hipError_t by_format(const AttendArgs &a, hipStream_t stream, bool *ok) {
 bool mfma_attend_supported(const AttendArgs &a) {
   const int G = a.q_heads / a.kv_heads;
   const bool fmt = (a.k_format == 4 && a.v_format == 4) || (a.k_format == 2 && a.v_format == 2);
-  return fmt && a.num_near_splits == 0 && G >= 1 && G <= kGMax && (a.head_dim == 128 || a.head_dim == 256);
+  // buffer resources address one (b, kv head) slice with 32-bit offsets
+  const bool fits = (int64_t)a.capacity * a.head_dim / 2 < (1ll << 31);
+  return fmt && fits && a.num_near_splits == 0 && G >= 1 && G <= kGMax && (a.head_dim == 128 || a.head_dim == 256);
 }
 
 hipError_t launch_attend_mfma(const AttendArgs &a, hipStream_t stream, bool *supported) {

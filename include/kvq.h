@@ -79,7 +79,7 @@ typedef enum { KVQ_LM2 = 2, KVQ_LM3 = 3, KVQ_LM4 = 4, KVQ_FP8_E4M3 = 8 } kvq_for
  *            k_centroids is unused (may be NULL) for FP8 keys
  *   near_k, near_v  two-tier caches only: [batch][kv_heads][near_len][head_dim]
  *            fp16 bits in the original (unrotated) domain; NULL with near_len 0
- * Code and norm buffers must be 16-byte aligned and capacity a multiple of 16. */
+ * Code, norm and sign buffers must be 16-byte aligned and capacity a multiple of 16. */
 typedef struct kvq_cache {
   int32_t batch;
   int32_t kv_heads;
@@ -150,7 +150,7 @@ kvq_status kvq_quantize_append(const kvq_cache *cache, const void *k, const void
  *           sum_t exp(s_t - m) * vhat_t / l   (0 if empty); near splits first,
  *           original domain; far splits rotated domain.
  *   q       device [batch][q_heads][head_dim] in q_dtype (KVQ_F32/F16),
- *           original domain.
+ *           original domain, 16-byte aligned.
  * The softmax scale 1/sqrt(d) is applied inside.  num_near_splits must be 0
  * unless the cache has a near tier.  Errors: KVQ_EINVAL, KVQ_ERANGE
  * (seq_len > capacity), KVQ_EUNSUPPORTED (GQA group or format combination not
