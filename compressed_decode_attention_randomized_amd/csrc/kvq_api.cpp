@@ -82,6 +82,8 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q
   if (st != KVQ_OK) return st;
   if (!q || !part_o || !part_ml) return kvq::fail(KVQ_EINVAL, "%s: NULL q or partial buffer", fn);
   if (!aligned(q, 16)) return kvq::fail(KVQ_EINVAL, "%s: q must be 16-byte aligned", fn);
+  if (!aligned(part_o, 16) || !aligned(part_ml, 16))
+    return kvq::fail(KVQ_EINVAL, "%s: partial buffers must be 16-byte aligned", fn);
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_F16) return kvq::fail(KVQ_EINVAL, "%s: q_dtype %d", fn, q_dtype);
   if (q_heads < 1 || q_heads % cache->kv_heads)
     return kvq::fail(KVQ_EINVAL, "%s: q_heads=%d not a multiple of kv_heads=%d", fn, q_heads, cache->kv_heads);

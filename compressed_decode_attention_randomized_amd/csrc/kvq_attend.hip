@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
   State<G, DPL> st;
   st.init();
   if (near) {
-    const int chunk = ((P.near_len + P.num_near_splits - 1) / P.num_near_splits + 15) / 16 * 16;
+    const int chunk = ((P.near_len + P.num_near_splits - 1) / P.num_near_splits + 31) / 32 * 32;
     const int t0 = min(P.near_len, split * chunk), t1 = min(P.near_len, t0 + chunk);
     NearTier<D, G, DPL> tier;
     const size_t base = (size_t)bh * P.near_len * D * 2;
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     token_loop<G, DPL, LPT>(tier, qr, st, t0, t1);
   } else {
     const int fs = split - P.num_near_splits;
-    const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + 15) / 16 * 16;
+    const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + 31) / 32 * 32;
     const int t0 = min(P.seq_len, fs * chunk), t1 = min(P.seq_len, t0 + chunk);
     FarTier<D, KB, VB, G, DPL> tier;
     tier.krow0 = P.k_codes + (size_t)bh * P.capacity * (D * KB / 8);
@@ -406,6 +406,10 @@ hipError_t by_format(const AttendArgs &a, hipStream_t stream, bool *ok) {
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported) {
+  if (pair_attend_supported(a)) {
+    *supported = true;
+    return launch_attend_pair(a, stream);
+  }
   if (mfma_attend_supported(a)) return launch_attend_mfma(a, stream, supported);
   *supported = true;
   switch (a.head_dim) {

@@ -48,7 +48,6 @@ typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
 constexpr int kTile = 16;
-constexpr int kBatch = 1;                      // 16-token tiles per wave iteration
 constexpr int kGMax = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -195,15 +194,20 @@ struct Sources {
   __amdgpu_buffer_rsrc_t kc, vc, kn, vn;
 };
 
+// Loads of the tile at token tb.  With skip set every offset is moved past
+// the end of its buffer, where buffer loads return zeros without touching
+// memory; loads are thus issued unconditionally, which keeps the wait for a
+// tile at its first use instead of at a control-flow join.
 template <int D, int KB, int VB>
-__device__ inline void load_tile(Tile<D, KB, VB> &t, const Sources &src, int tb, int g, int n) {
+__device__ inline void load_tile(Tile<D, KB, VB> &t, const Sources &src, int tb, bool skip, int g, int n) {
   using Gm = Geometry<D, KB, VB>;
-  buf_load<Gm::KSL>(src.kc, (uint32_t)(tb + n) * Gm::KROW + g * Gm::KSL, t.kw);
+  const uint32_t far = skip ? 0x80000000u : 0u;
+  buf_load<Gm::KSL>(src.kc, far + (uint32_t)(tb + n) * Gm::KROW + g * Gm::KSL, t.kw);
   const int ts = tb + 4 * g;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) buf_load<Gm::VSL>(src.vc, (uint32_t)(ts + i) * Gm::VROW + n * Gm::VSL, t.vw[i]);
-  buf_load<8>(src.kn, (uint32_t)ts * 2, t.kn);
-  buf_load<8>(src.vn, (uint32_t)ts * 2, t.vn);
+  for (int i = 0; i < 4; ++i) buf_load<Gm::VSL>(src.vc, far + (uint32_t)(ts + i) * Gm::VROW + n * Gm::VSL, t.vw[i]);
+  buf_load<8>(src.kn, far + (uint32_t)ts * 2, t.kn);
+  buf_load<8>(src.vn, far + (uint32_t)ts * 2, t.vn);
 }
 
 template <int KB, int E>
@@ -212,53 +216,24 @@ __device__ inline half8_t key_operand(const CodePlanes<KB> &c, const uint32_t *l
                   lut_read(lutk, c.template addr<E + 2>()), lut_read(lutk, c.template addr<E + 3>()));
 }
 
-// Key products of one code word of both tiles, k-blocks interleaved so the two
-// accumulation chains overlap.
 template <int KB, int W, int E = 0>
-__device__ inline void key_word(const CodePlanes<KB> &c0, const CodePlanes<KB> &c1, const uint32_t (*bk)[4],
-                                const uint32_t *lutk, float4_t &d0, float4_t &d1) {
-  constexpr int KCW = 32 / KB;
-  if constexpr (E < KCW) {
-    constexpr int kb = (W * KCW + E) / 4;
-    const half8_t bq = as_half8(bk[kb][0], bk[kb][1], bk[kb][2], bk[kb][3]);
-    const half8_t a0 = key_operand<KB, E>(c0, lutk);
-    const half8_t a1 = key_operand<KB, E>(c1, lutk);
-    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bq, d0, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bq, d1, 0, 0, 0);
-    key_word<KB, W, E + 4>(c0, c1, bk, lutk, d0, d1);
-  }
-}
-
-template <int KB, int W, int E = 0>
-__device__ inline void key_word1(const CodePlanes<KB> &c0, const uint32_t (*bk)[4], const uint32_t *lutk, float4_t &d0) {
+__device__ inline void key_word(const CodePlanes<KB> &c0, const uint32_t (*bk)[4], const uint32_t *lutk, float4_t &d0) {
   constexpr int KCW = 32 / KB;
   if constexpr (E < KCW) {
     constexpr int kb = (W * KCW + E) / 4;
     const half8_t bq = as_half8(bk[kb][0], bk[kb][1], bk[kb][2], bk[kb][3]);
     d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<KB, E>(c0, lutk), bq, d0, 0, 0, 0);
-    key_word1<KB, W, E + 4>(c0, bk, lutk, d0);
+    key_word<KB, W, E + 4>(c0, bk, lutk, d0);
   }
 }
 
 template <int KB, int KW, int W = 0>
-__device__ inline void key_scores1(const uint32_t (&kw0)[KW], const uint32_t (*bk)[4], const uint32_t *lutk, float4_t &d0) {
+__device__ inline void key_scores(const uint32_t (&kw0)[KW], const uint32_t (*bk)[4], const uint32_t *lutk, float4_t &d0) {
   if constexpr (W < KW) {
     CodePlanes<KB> c0;
     c0.set(kw0[W]);
-    key_word1<KB, W>(c0, bk, lutk, d0);
-    key_scores1<KB, KW, W + 1>(kw0, bk, lutk, d0);
-  }
-}
-
-template <int KB, int KW, int W = 0>
-__device__ inline void key_scores(const uint32_t (&kw0)[KW], const uint32_t (&kw1)[KW], const uint32_t (*bk)[4],
-                                  const uint32_t *lutk, float4_t &d0, float4_t &d1) {
-  if constexpr (W < KW) {
-    CodePlanes<KB> c0, c1;
-    c0.set(kw0[W]);
-    c1.set(kw1[W]);
-    key_word<KB, W>(c0, c1, bk, lutk, d0, d1);
-    key_scores<KB, KW, W + 1>(kw0, kw1, bk, lutk, d0, d1);
+    key_word<KB, W>(c0, bk, lutk, d0);
+    key_scores<KB, KW, W + 1>(kw0, bk, lutk, d0);
   }
 }
 
@@ -287,34 +262,25 @@ __device__ inline void value_update(const uint32_t (&vw)[4][NW], const uint32_t 
   value_update_dt<VB, VDL, NW>(vp, lutv, aw, dv);
 }
 
-// One batch (two tiles) of the online softmax.  TAIL masks tokens at or past
-// t1; full batches skip every per-token test.
+// One 16-token tile of the online softmax.  TAIL masks tokens at or past t1;
+// full tiles skip every per-token test.
 template <bool TAIL, int D, int KB, int VB>
-__device__ inline void process_batch(const Tile<D, KB, VB> (&cur)[kBatch], const uint32_t (*bk)[4], const uint32_t *lutk,
-                                     const uint32_t *lutv, float sfac, int tb, int t1, int g, int n,
-                                     float4_t (&dv)[Geometry<D, KB, VB>::VDL], float &m_run, float &l_run) {
+__device__ inline void process_tile(const Tile<D, KB, VB> &t, const uint32_t (*bk)[4], const uint32_t *lutk,
+                                    const uint32_t *lutv, float sfac, int tb, int t1, int g, int n,
+                                    float4_t (&dv)[Geometry<D, KB, VB>::VDL], float &m_run, float &l_run) {
   using Gm = Geometry<D, KB, VB>;
-  float4_t dk[kBatch];
-  if constexpr (kBatch == 2) {
-    dk[0] = dk[1] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    key_scores<KB, Gm::KW>(cur[0].kw, cur[1].kw, bk, lutk, dk[0], dk[1]);
-  } else {
-    dk[0] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    key_scores1<KB, Gm::KW>(cur[0].kw, bk, lutk, dk[0]);
-  }
+  float4_t dk = {0.f, 0.f, 0.f, 0.f};
+  key_scores<KB, Gm::KW>(t.kw, bk, lutk, dk);
 
-  float s[kBatch][4];
+  float s[4];
   float mt = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float nk = half_value((cur[u].kn[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-      float v = (dk[u][i] + row_swap8(dk[u][i])) * (nk * sfac);
-      if constexpr (TAIL) v = (tb + u * kTile + 4 * g + i < t1) ? v : -INFINITY;
-      s[u][i] = v;
-      mt = fmaxf(mt, v);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const float nk = half_value((t.kn[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    float v = (dk[i] + row_swap8(dk[i])) * (nk * sfac);
+    if constexpr (TAIL) v = (tb + 4 * g + i < t1) ? v : -INFINITY;
+    s[i] = v;
+    mt = fmaxf(mt, v);
   }
   mt = max_rows(mt);
 
@@ -331,31 +297,27 @@ __device__ inline void process_batch(const Tile<D, KB, VB> (&cur)[kBatch], const
     }
   }
 
+  uint32_t av[4];
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    uint32_t av[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float p = __builtin_amdgcn_exp2f(s[u][i] - m_run);
-      if constexpr (TAIL) p = (s[u][i] == -INFINITY) ? 0.f : p;
-      l_run += p;
-      const float nv = half_value((cur[u].vn[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-      float w = p * nv;
-      if constexpr (TAIL) w = (p > 0.f) ? w : 0.f;
-      const _Float16 hi = (_Float16)w;
-      const _Float16 part = (n < 8) ? hi : (_Float16)(w - (float)hi);
-      av[i] = pack2(part, part);
-    }
-    const half8_t aw = as_half8(av[0], av[1], av[2], av[3]);
-    value_update<VB, Gm::VDL, Gm::VW>(cur[u].vw, lutv, aw, dv);
+  for (int i = 0; i < 4; ++i) {
+    float p = __builtin_amdgcn_exp2f(s[i] - m_run);
+    if constexpr (TAIL) p = (s[i] == -INFINITY) ? 0.f : p;
+    l_run += p;
+    const float nv = half_value((t.vn[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    float w = p * nv;
+    if constexpr (TAIL) w = (p > 0.f) ? w : 0.f;
+    const _Float16 hi = (_Float16)w;
+    const _Float16 part = (n < 8) ? hi : (_Float16)(w - (float)hi);
+    av[i] = pack2(part, part);
   }
+  value_update<VB, Gm::VDL, Gm::VW>(t.vw, lutv, as_half8(av[0], av[1], av[2], av[3]), dv);
 }
 
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(kBlock, 4) void attend_mfma_kernel(MParams P) {
+__global__ __launch_bounds__(kBlock, 3) void attend_mfma_kernel(MParams P) {
   using Gm = Geometry<D, KB, VB>;
   constexpr int NKB = Gm::NKB, VDL = Gm::VDL;
-  constexpr int STEP = kWaves * kBatch * kTile;
+  constexpr int STEP = kWaves * kTile;
   static_assert(KB == 2 || KB == 4, "key bits");
   static_assert(VB == 2 || VB == 4, "value bits");
 
@@ -365,14 +327,15 @@ __global__ __launch_bounds__(kBlock, 4) void attend_mfma_kernel(MParams P) {
   __shared__ __attribute__((aligned(16))) uint32_t qent[kGMax][D + 4];
   __shared__ float qfac[kGMax];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n = lane & 15;
   const int G = P.q_heads / P.kv_heads;
   const int split = blockIdx.x, bh = blockIdx.y;
   const int b = bh / P.kv_heads, hkv = bh - b * P.kv_heads;
 
-  // chunks of ceil(T/S) tokens rounded up to a multiple of the tile
-  const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + kTile - 1) / kTile * kTile;
+  // chunks of ceil(T/S) tokens rounded up to a multiple of 32 (two tiles)
+  const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + 2 * kTile - 1) / (2 * kTile) * (2 * kTile);
   const int t0 = min(P.seq_len, split * chunk), t1 = min(P.seq_len, t0 + chunk);
   const uint32_t cap = (uint32_t)P.capacity;
   Sources src;
@@ -381,14 +344,13 @@ __global__ __launch_bounds__(kBlock, 4) void attend_mfma_kernel(MParams P) {
   src.kn = make_rsrc(P.k_norms + (size_t)bh * cap, cap * 2);
   src.vn = make_rsrc(P.v_norms + (size_t)bh * cap, cap * 2);
 
-  // first batch in flight before the prologue; tiles stay inside the cache
-  // (t0 and the capacity are multiples of 16) and tokens past t1 are masked
-  Tile<D, KB, VB> cur[kBatch], nxt[kBatch];
-  int tb = t0 + wave * kBatch * kTile;
-  if (tb < t1) {
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) load_tile(cur[u], src, (tb + u * kTile < t1) ? tb + u * kTile : tb, g, n);
-  }
+  // Full tiles [t0, t1f) go through the main loop; a partial last tile (only
+  // the last split can have one) is handled after it.  Tiles stay inside the
+  // cache: t0 and the capacity are multiples of 16.
+  const int t1f = t0 + ((t1 - t0) & ~(kTile - 1));
+  Tile<D, KB, VB> ta, tc;
+  int tb = t0 + wave * kTile;
+  load_tile(ta, src, tb, tb >= t1f, g, n);        // in flight during the prologue
 
   // ---- rotated queries, shared by the work-group ----
   // Wave w rotates heads w and w+4: lane l holds coordinates [l*E1, (l+1)*E1);
@@ -466,19 +428,19 @@ __global__ __launch_bounds__(kBlock, 4) void attend_mfma_kernel(MParams P) {
   for (int dt = 0; dt < VDL; ++dt) dv[dt] = (float4_t){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (; tb < t1; tb += STEP) {
-    const int tn = tb + STEP;
-    if (tn < t1) {
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) load_tile(nxt[u], src, (tn + u * kTile < t1) ? tn + u * kTile : tn, g, n);
-    }
-    if (tb + kBatch * kTile <= t1) {
-      process_batch<false>(cur, bk, lutk, lutv, sfac, tb, t1, g, n, dv, m_run, l_run);
-    } else {
-      process_batch<true>(cur, bk, lutk, lutv, sfac, tb, t1, g, n, dv, m_run, l_run);
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) cur[u] = nxt[u];
+  // Two tiles used in turn (no register copies between iterations, so the
+  // wait for a tile's loads sits at its first use and the next tile's loads
+  // stay in flight meanwhile).
+  for (; tb < t1f; tb += 2 * STEP) {
+    load_tile(tc, src, tb + STEP, tb + STEP >= t1f, g, n);
+    process_tile<false>(ta, bk, lutk, lutv, sfac, tb, t1, g, n, dv, m_run, l_run);
+    if (tb + STEP >= t1f) break;
+    load_tile(ta, src, tb + 2 * STEP, tb + 2 * STEP >= t1f, g, n);
+    process_tile<false>(tc, bk, lutk, lutv, sfac, tb + STEP, t1, g, n, dv, m_run, l_run);
+  }
+  if (t1f < t1 && wave == ((t1f - t0) / kTile) % kWaves) {
+    load_tile(ta, src, t1f, false, g, n);
+    process_tile<true>(ta, bk, lutk, lutv, sfac, t1f, t1, g, n, dv, m_run, l_run);
   }
 
   // ---- wave epilogue: l per head over the 4 lane groups; value tile rows to LDS ----

@@ -1,0 +1,507 @@
+// Split-K GQA decode attention on 4-bit Lloyd-Max keys and values, head
+// dimension 128: matrix-core products fed from a byte-indexed pair table.
+//
+// Each packed byte holds two 4-bit codes.  The LDS table maps a byte to the
+// operand registers of both codes at once: entry(byte) = (e(c[lo]), e(c[hi])),
+// e(x) the fp16 (hi, lo) split of x = RN(x) + RN(x - RN(x)) in one 32-bit
+// word.  So one 64-bit LDS read serves two codes and needs one address op.
+// The table is replicated over 16 lane slots (address = byte*256 + slot*8,
+// slot = lane % 16) so that the 16 lanes an LDS cycle serves never meet in a
+// bank; a key table and a value table share each 256-byte row (value table at
+// +128).  The address is one v_perm: slot*8 from a per-lane register in byte
+// 0, the code byte in byte 1.
+//
+//   keys    token n of the tile in A row n; the byte pair (2kb, 2kb+1) of the
+//           lane's 16-byte slice gives coordinates 4kb..4kb+3 as k-slot pairs
+//           (c_hi, c_lo); B columns 0..7 hold (z_hi, z_hi) of head n, columns
+//           8..15 hold (z_lo, 0), so column h + column h+8 is the score of
+//           head h up to the fp32 accumulation.
+//   values  k-slot pairs are the 4 tokens of the lane group; a value byte
+//           built from the same coordinate of two tokens (low nibble token
+//           t, high nibble token t+1) reads both tokens' (c_hi, c_lo) at once;
+//           A rows 0..7 hold (w_hi, w_hi) and rows 8..15 (w_lo, w_lo) of the
+//           weight w = exp2(score - max) * norm.
+//
+// Work mapping: grid (split, b * Hkv), 6 waves per work-group walking the
+// split's 16-token tiles round robin, two tiles in flight per wave.  All HBM
+// reads are buffer loads with the cache arrays as SGPR resources.
+// Sources: "The Engineering Behind AdapTQ", "Engineering the Hot Path"
+// (rotate q once, score from codes through a table, no dequantize pass);
+// "FoveatedKV", "Making it fast" (split-K, pre-scaled q, online softmax with
+// one exp per score, split merge); "I Ported a Google Research Paper to Apple
+// Silicon", "The Bit-Packing Problem" (4-bit codes, low nibble first).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr int kWaves = 16;
+constexpr int kMinWaves = 4;                   // waves per SIMD the register budget is sized for
+constexpr int kBlock = kWaves * 64;
+constexpr int kTile = 16;
+constexpr int kPairTok = 2 * kTile;             // tokens per claimed tile pair (the split chunk granule)
+constexpr int kGMax = 8;
+constexpr int kRow = D / 2;                     // packed bytes per 4-bit vector
+constexpr int kVDL = D / 16;                    // value coordinates per lane
+constexpr int kRowPad = D + 4;                  // query table row stride (words)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kCodeScale = 256.f;             // centroid scale: keeps the low fp16 half a normal number
+constexpr int kRawBufferFlags = 0x00020000;     // 32-bit data format, untyped raw access
+constexpr uint32_t kNib = 0x0F0F0F0Fu;
+// s_waitcnt vmcnt(7) expcnt(7) lgkmcnt(15): the seven loads of one tile
+constexpr int kWaitOlderTile = 0x0F77;
+
+struct PParams {
+  const void *q;
+  int q_f16;
+  int kv_heads, q_heads, capacity, seq_len, num_splits;
+  const uint8_t *k_codes, *v_codes;
+  const uint16_t *k_norms, *v_norms;
+  const int8_t *signs;
+  const float *k_centroids, *v_centroids;
+  float *part_o, *part_ml;
+};
+
+__device__ inline uint32_t pack2(_Float16 a, _Float16 b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ inline half8_t as_half8(uint2_t a, uint2_t b) {
+  const uint4_t v = {a.x, a.y, b.x, b.y};
+  return __builtin_bit_cast(half8_t, v);
+}
+
+__device__ inline float half_value(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
+
+// (hi, lo) fp16 split of x in one word: hi = RN(x), lo = RN(x - hi).
+__device__ inline uint32_t split_entry(float x) {
+  const _Float16 hi = (_Float16)x;
+  return pack2(hi, (_Float16)(x - (float)hi));
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRawBufferFlags);
+}
+
+// v_perm selector putting byte B of the first operand into byte 1 and byte 0
+// of the second (the lane's slot offset) into byte 0; bytes 2, 3 become zero.
+template <int B>
+__device__ inline uint32_t pair_addr(uint32_t word, uint32_t slot8) {
+  return __builtin_amdgcn_perm(word, slot8, 0x0C0C0000u | ((4u + B) << 8));
+}
+
+template <int OFF>
+__device__ inline uint2_t table_read(const uint8_t *tab, uint32_t addr) {
+  return *reinterpret_cast<const uint2_t *>(tab + OFF + addr);
+}
+
+// xor-1 exchange (DPP quad permutation [1, 0, 3, 2]).
+__device__ inline float lane_swap1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+
+// Max / sum over the four 16-lane rows holding one column, with the gfx950
+// row swaps (two distinct registers per swap).
+__device__ inline void swap16(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ inline void swap32(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ inline float max_rows(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  x = fmaxf(a, b);
+  a = x;
+  b = x;
+  swap32(a, b);
+  return fmaxf(a, b);
+}
+__device__ inline float sum_rows(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  x = a + b;
+  a = x;
+  b = x;
+  swap32(a, b);
+  return a + b;
+}
+
+// Value of lane l ^ M (M = 1, 2, 4, 8, 16, 32) without LDS: DPP for the
+// exchanges inside a 16-lane row (row_ror:n hands lane i the value of lane
+// i - n mod 16), the gfx950 row swaps across rows.  After
+// v_permlane16_swap on two copies of x, lanes of even rows find their xor-16
+// partner in the second copy and lanes of odd rows in the first; likewise
+// for v_permlane32_swap and the two halves of the wave.
+template <int M>
+__device__ inline float xor_lane(float x, int lane) {
+  const int xi = __builtin_bit_cast(int, x);
+  if constexpr (M == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false));
+  if constexpr (M == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false));
+  if constexpr (M == 4) {
+    const int up = __builtin_amdgcn_mov_dpp(xi, 0x12C, 0xF, 0xF, false);    // row_ror:12: lane i + 4
+    const int dn = __builtin_amdgcn_mov_dpp(xi, 0x124, 0xF, 0xF, false);    // row_ror:4: lane i - 4
+    return __builtin_bit_cast(float, (lane & 4) ? dn : up);
+  }
+  if constexpr (M == 8) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0x128, 0xF, 0xF, false));
+  if constexpr (M == 16) {
+    float a = x, b = x;
+    swap16(a, b);
+    return (lane & 16) ? a : b;
+  }
+  if constexpr (M == 32) {
+    float a = x, b = x;
+    swap32(a, b);
+    return (lane & 32) ? a : b;
+  }
+}
+
+// Walsh-Hadamard butterfly across lanes at lane stride M: the lower lane of
+// each pair keeps x + partner, the upper one partner - x.
+template <int M>
+__device__ inline float butterfly(float x, int lane) {
+  const float o = xor_lane<M>(x, lane);
+  return (lane & M) ? (o - x) : (x + o);
+}
+
+struct Tile {
+  uint4_t kw;          // key bytes: token n, coordinates [32g, 32g+32)
+  uint32_t vw[4];      // value bytes: tokens 4g+i, coordinates [8n, 8n+8)
+  uint2_t kn, vn;      // fp16 norms of tokens 4g..4g+3
+};
+
+struct Sources {
+  __amdgpu_buffer_rsrc_t kc, vc, kn, vn;
+};
+
+// Loads of the tile at token tb.  With skip set every offset is moved past
+// the end of its buffer, where buffer loads return zeros without touching
+// memory, so loads need no branch and a tile's wait sits at its first use.
+__device__ inline void load_tile(Tile &t, const Sources &src, int tb, bool skip, int g, int n) {
+  const uint32_t far = skip ? 0x80000000u : 0u;
+  t.kw = __builtin_amdgcn_raw_buffer_load_b128(src.kc, far + (uint32_t)(tb + n) * kRow + g * 16, 0, 0);
+  const int ts = tb + 4 * g;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t.vw[i] = __builtin_amdgcn_raw_buffer_load_b32(src.vc, far + (uint32_t)(ts + i) * kRow + n * 4, 0, 0);
+  t.kn = __builtin_amdgcn_raw_buffer_load_b64(src.kn, far + (uint32_t)ts * 2, 0, 0);
+  t.vn = __builtin_amdgcn_raw_buffer_load_b64(src.vn, far + (uint32_t)ts * 2, 0, 0);
+}
+
+// Key block kb: coordinates 4kb..4kb+3 of the lane's slice = bytes 2kb, 2kb+1.
+template <int KB = 0>
+__device__ inline void key_scores(const uint4_t &kw, const uint4_t (&bk)[D / 16], const uint8_t *tab,
+                                  uint32_t slot8, float4_t &dk) {
+  if constexpr (KB < D / 16) {
+    const uint32_t w = kw[KB / 2];
+    const uint2_t e0 = table_read<0>(tab, pair_addr<2 * (KB % 2)>(w, slot8));
+    const uint2_t e1 = table_read<0>(tab, pair_addr<2 * (KB % 2) + 1>(w, slot8));
+    dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(e0, e1), __builtin_bit_cast(half8_t, bk[KB]), dk, 0, 0, 0);
+    key_scores<KB + 1>(kw, bk, tab, slot8, dk);
+  }
+}
+
+// Value coordinate tiles 2m (low nibbles) and 2m+1 (high nibbles) from byte m
+// of the token-pair bytes.
+template <int M = 0>
+__device__ inline void value_update(const uint32_t (&ev)[2], const uint32_t (&od)[2], const uint8_t *tab,
+                                    uint32_t slot8, const half8_t &aw, float4_t (&dv)[kVDL]) {
+  if constexpr (M < 4) {
+    const uint2_t a0 = table_read<128>(tab, pair_addr<M>(ev[0], slot8));
+    const uint2_t a1 = table_read<128>(tab, pair_addr<M>(ev[1], slot8));
+    dv[2 * M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(a0, a1), dv[2 * M], 0, 0, 0);
+    const uint2_t b0 = table_read<128>(tab, pair_addr<M>(od[0], slot8));
+    const uint2_t b1 = table_read<128>(tab, pair_addr<M>(od[1], slot8));
+    dv[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(b0, b1), dv[2 * M + 1], 0, 0, 0);
+    value_update<M + 1>(ev, od, tab, slot8, aw, dv);
+  }
+}
+
+// One 16-token tile of the online softmax.  TAIL masks tokens at or past t1.
+template <bool TAIL>
+__device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], const uint8_t *tab, uint32_t slot8,
+                                    float sfac, int tb, int t1, int g, int n, float4_t (&dv)[kVDL], float &m_run,
+                                    float &l_run) {
+  float4_t dk = {0.f, 0.f, 0.f, 0.f};
+  key_scores(t.kw, bk, tab, slot8, dk);
+
+  // lane (g, n): tokens 4g..4g+3, head n / 2 (both columns of a head end up
+  // with the full score)
+  float s[4];
+  float mt = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float nk = half_value((t.kn[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    float v = (dk[i] + lane_swap1(dk[i])) * (nk * sfac);
+    if constexpr (TAIL) v = (tb + 4 * g + i < t1) ? v : -INFINITY;
+    s[i] = v;
+    mt = fmaxf(mt, v);
+  }
+  mt = max_rows(mt);
+
+  if (__builtin_amdgcn_ballot_w64(mt > m_run) != 0) {
+    const float mn = fmaxf(m_run, mt);
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+    l_run *= alpha;
+    m_run = mn;
+    // accumulator rows 4g, 4g+1 belong to head 2g, rows 4g+2, 4g+3 to head 2g+1
+    const float a0 = __shfl(alpha, 4 * g), a1 = __shfl(alpha, 4 * g + 2);
+#pragma unroll
+    for (int dt = 0; dt < kVDL; ++dt) {
+      dv[dt][0] *= a0;
+      dv[dt][1] *= a0;
+      dv[dt][2] *= a1;
+      dv[dt][3] *= a1;
+    }
+  }
+
+  // value bytes of token pairs (4g, 4g+1) and (4g+2, 4g+3): even coordinates
+  // from the low nibbles, odd coordinates from the high nibbles
+  uint32_t ev[2], od[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    ev[p] = (t.vw[2 * p] & kNib) | ((t.vw[2 * p + 1] << 4) & ~kNib);
+    od[p] = ((t.vw[2 * p] >> 4) & kNib) | (t.vw[2 * p + 1] & ~kNib);
+  }
+
+  uint32_t av[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float p = __builtin_amdgcn_exp2f(s[i] - m_run);
+    if constexpr (TAIL) p = (s[i] == -INFINITY) ? 0.f : p;
+    l_run += p;
+    const float nv = half_value((t.vn[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    float w = p * nv;
+    if constexpr (TAIL) w = (p > 0.f) ? w : 0.f;
+    const _Float16 hi = (_Float16)w;
+    const _Float16 part = (n & 1) ? (_Float16)(w - (float)hi) : hi;
+    av[i] = pack2(part, part);
+  }
+  const uint4_t a4 = {av[0], av[1], av[2], av[3]};
+  value_update(ev, od, tab, slot8, __builtin_bit_cast(half8_t, a4), dv);
+}
+
+__global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams P) {
+  // pair tables during the loop, the waves' value rows afterwards
+  __shared__ __attribute__((aligned(16))) uint8_t tab[65536];
+  __shared__ __attribute__((aligned(16))) uint32_t qtab[2 * kGMax][kRowPad];
+  __shared__ float red_ml[kWaves][kGMax][2];
+  __shared__ float qfac[kGMax];
+  __shared__ uint32_t next_pair;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, n = lane & 15;
+  const int G = P.q_heads / P.kv_heads;
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / P.kv_heads, hkv = bh - b * P.kv_heads;
+
+  // chunks of ceil(T/S) tokens rounded up to a multiple of 32; whole tile
+  // pairs [t0, t1f) go through the main loop, the rest of the last split
+  // (under 32 tokens) after it
+  const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + kPairTok - 1) / kPairTok * kPairTok;
+  const int t0 = min(P.seq_len, split * chunk), t1 = min(P.seq_len, t0 + chunk);
+  const int npairs = (t1 - t0) / kPairTok;
+  const int t1f = t0 + npairs * kPairTok;
+  const uint32_t cap = (uint32_t)P.capacity;
+  Sources src;
+  src.kc = make_rsrc(P.k_codes + (size_t)bh * cap * kRow, cap * kRow);
+  src.vc = make_rsrc(P.v_codes + (size_t)bh * cap * kRow, cap * kRow);
+  src.kn = make_rsrc(P.k_norms + (size_t)bh * cap, cap * 2);
+  src.vn = make_rsrc(P.v_norms + (size_t)bh * cap, cap * 2);
+
+  // ---- small loads first (centroids, this wave's query head, signs), then
+  // the first tile pair in issue order, so that waiting for the small loads
+  // never waits for a tile and the tile order matches the main loop's ----
+  // Table chunks (16 bytes, two slots) are written by consecutive lanes:
+  // thread t writes chunks t + 1024k, k = 0..3, i.e. rows (code bytes)
+  // t/16 + 64k, key table if t % 16 < 8 else value table.  The low nibble of
+  // those rows is (t/16) % 16 for every k, the high nibble t/256 + 4k.
+  static_assert(kBlock == 1024, "pair-table fill assumes 1024 threads");
+  const float *ctab = ((tid & 15) < 8) ? P.k_centroids : P.v_centroids;
+  const float c_lo = ctab[(tid >> 4) & 15];
+  float c_hi[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c_hi[k] = ctab[(tid >> 8) + 4 * k];
+  const bool has_q = wave < G;
+  const size_t qoff = ((size_t)b * P.q_heads + hkv * G + (has_q ? wave : 0)) * D + lane * 2;
+  uint32_t qh = 0u;
+  float2 qf = {0.f, 0.f};
+  if (P.q_f16) qh = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(P.q) + qoff);
+  else qf = *reinterpret_cast<const float2 *>(static_cast<const float *>(P.q) + qoff);
+  const uint16_t sg = *reinterpret_cast<const uint16_t *>(P.signs + lane * 2);
+  __builtin_amdgcn_sched_barrier(0);
+  int pr = wave;                                     // first pair of this wave; later ones from the counter
+  Tile ta, tc;
+  load_tile(ta, src, t0 + pr * kPairTok, pr >= npairs, g, n);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(tc, src, t0 + pr * kPairTok + kTile, pr >= npairs, g, n);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- pair tables ----
+  {
+    const uint32_t lo = split_entry(c_lo * kCodeScale);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t hi = split_entry(c_hi[k] * kCodeScale);
+      const uint4_t e = {lo, hi, lo, hi};
+      *reinterpret_cast<uint4_t *>(tab + (tid + 1024 * k) * 16) = e;
+    }
+  }
+  if (tid == 0) next_pair = kWaves;
+
+  // ---- rotated query of head `wave` (waves G..7 write zero rows) ----
+  // Lane l holds coordinates 2l, 2l+1: sign flip, the stride-1 butterfly in
+  // the lane, strides 2..64 across lanes (xor 1..32).  The rotated vector is
+  // scaled so that its largest |z| lies in (64, 128] and stored in the two
+  // B-operand forms (z_hi, z_hi) (row 2h) and (z_lo, 0) (row 2h+1).
+  if (wave < kGMax) {
+    uint2_t f0 = {0u, 0u}, f1 = {0u, 0u};
+    float fac = 0.f;
+    if (has_q) {
+      float z0 = P.q_f16 ? half_value(qh & 0xFFFFu) : qf.x;
+      float z1 = P.q_f16 ? half_value(qh >> 16) : qf.y;
+      z0 = (sg & 0x80u) ? -z0 : z0;
+      z1 = (sg & 0x8000u) ? -z1 : z1;
+      float a = z0 + z1, c = z0 - z1;
+      a = butterfly<1>(a, lane);  c = butterfly<1>(c, lane);
+      a = butterfly<2>(a, lane);  c = butterfly<2>(c, lane);
+      a = butterfly<4>(a, lane);  c = butterfly<4>(c, lane);
+      a = butterfly<8>(a, lane);  c = butterfly<8>(c, lane);
+      a = butterfly<16>(a, lane); c = butterfly<16>(c, lane);
+      a = butterfly<32>(a, lane); c = butterfly<32>(c, lane);
+      float zmax = fmaxf(fabsf(a), fabsf(c));
+      zmax = fmaxf(zmax, xor_lane<1>(zmax, lane));
+      zmax = fmaxf(zmax, xor_lane<2>(zmax, lane));
+      zmax = fmaxf(zmax, xor_lane<4>(zmax, lane));
+      zmax = fmaxf(zmax, xor_lane<8>(zmax, lane));
+      zmax = max_rows(zmax);
+      const float qscale = (zmax > 0.f) ? exp2f(7.f - ceilf(log2f(zmax))) : 1.f;
+      const float za = a * qscale, zc = c * qscale;
+      const _Float16 ha = (_Float16)za, hc = (_Float16)zc;
+      const _Float16 la = (_Float16)(za - (float)ha), lc = (_Float16)(zc - (float)hc);
+      f0 = (uint2_t){pack2(ha, ha), pack2(hc, hc)};
+      f1 = (uint2_t){pack2(la, (_Float16)0.f), pack2(lc, (_Float16)0.f)};
+      fac = kLog2e / ((float)D * kCodeScale * qscale);
+    }
+    *reinterpret_cast<uint2_t *>(&qtab[2 * wave][lane * 2]) = f0;
+    *reinterpret_cast<uint2_t *>(&qtab[2 * wave + 1][lane * 2]) = f1;
+    if (lane == 0) qfac[wave] = fac;
+  }
+  __syncthreads();
+
+  // B operand of key block kb for column n: query table row n (head n / 2,
+  // form n % 2), coordinates 32g + 4kb .. +3
+  uint4_t bk[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) bk[kb] = *reinterpret_cast<const uint4_t *>(&qtab[n][g * 32 + 4 * kb]);
+  const float sfac = qfac[n >> 1];
+  const uint32_t slot8 = (uint32_t)n * 8;
+
+  float4_t dv[kVDL];
+#pragma unroll
+  for (int dt = 0; dt < kVDL; ++dt) dv[dt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // The two tiles of a pair use the two tile buffers; each buffer is refilled
+  // with the next claimed pair right after use.  The explicit vmcnt(7) waits
+  // for the older tile's seven loads only.  The loop has no exit inside its
+  // body; a pair index at or past npairs ends it (its loads return zeros).
+  while (pr < npairs) {
+    uint32_t nx = 0u;
+    if (lane == 0) nx = atomicAdd(&next_pair, 1u);
+    const int pn = __builtin_amdgcn_readfirstlane(nx);
+    const int tb = t0 + pr * kPairTok, tn = t0 + pn * kPairTok;
+    __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
+    process_tile<false>(ta, bk, tab, slot8, sfac, tb, t1, g, n, dv, m_run, l_run);
+    load_tile(ta, src, tn, pn >= npairs, g, n);
+    __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
+    process_tile<false>(tc, bk, tab, slot8, sfac, tb + kTile, t1, g, n, dv, m_run, l_run);
+    load_tile(tc, src, tn + kTile, pn >= npairs, g, n);
+    pr = pn;
+  }
+  // the last split's tokens [t1f, t1): up to two tiles, waves 0 and 1
+  if (wave < 2 && t1f + wave * kTile < t1) {
+    load_tile(ta, src, t1f + wave * kTile, false, g, n);
+    process_tile<true>(ta, bk, tab, slot8, sfac, t1f + wave * kTile, t1, g, n, dv, m_run, l_run);
+  }
+
+  // ---- wave epilogue: l per head over the 4 lane groups; per-head value rows to LDS ----
+  l_run = sum_rows(l_run);
+  __syncthreads();                                   // every wave is done with the tables
+  float *red_acc = reinterpret_cast<float *>(tab);   // [wave][head][D]
+  {
+    float4_t h0[2], h1[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      h0[q] = (float4_t){dv[4 * q][0] + dv[4 * q][1], dv[4 * q + 1][0] + dv[4 * q + 1][1],
+                         dv[4 * q + 2][0] + dv[4 * q + 2][1], dv[4 * q + 3][0] + dv[4 * q + 3][1]};
+      h1[q] = (float4_t){dv[4 * q][2] + dv[4 * q][3], dv[4 * q + 1][2] + dv[4 * q + 1][3],
+                         dv[4 * q + 2][2] + dv[4 * q + 2][3], dv[4 * q + 3][2] + dv[4 * q + 3][3]};
+    }
+    float *r0 = red_acc + ((size_t)wave * kGMax + 2 * g) * D + n * kVDL;
+    float *r1 = r0 + D;
+    *reinterpret_cast<float4_t *>(r0) = h0[0];
+    *reinterpret_cast<float4_t *>(r0 + 4) = h0[1];
+    *reinterpret_cast<float4_t *>(r1) = h1[0];
+    *reinterpret_cast<float4_t *>(r1 + 4) = h1[1];
+  }
+  if (lane < 2 * kGMax && !(lane & 1)) {
+    red_ml[wave][lane >> 1][0] = m_run;
+    red_ml[wave][lane >> 1][1] = l_run;
+  }
+  __syncthreads();
+
+  // ---- merge the waves ----
+  for (int i = tid; i < G * (D / 4); i += kBlock) {
+    const int h = i / (D / 4), j = (i - h * (D / 4)) * 4;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][h][0]);
+    float l = 0.f;
+    float4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = red_ml[w][h][0];
+      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      l += red_ml[w][h][1] * f;
+      o += *reinterpret_cast<const float4_t *>(red_acc + ((size_t)w * kGMax + h) * D + j) * f;
+    }
+    const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * P.num_splits + split;
+    const float inv = (l > 0.f) ? 1.f / (l * kCodeScale) : 0.f;
+    *reinterpret_cast<float4_t *>(P.part_o + row * D + j) = o * inv;
+    if (j == 0) {
+      P.part_ml[row * 2 + 0] = (M == -INFINITY) ? -INFINITY : M * kLn2;
+      P.part_ml[row * 2 + 1] = l;
+    }
+  }
+}
+
+}  // namespace
+
+bool pair_attend_supported(const AttendArgs &a) {
+  const int G = a.q_heads / a.kv_heads;
+  const bool fits = (int64_t)a.capacity * a.head_dim / 2 < (1ll << 31);
+  return a.head_dim == D && a.k_format == 4 && a.v_format == 4 && a.num_near_splits == 0 && G >= 1 &&
+         G <= kGMax && fits;
+}
+
+hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream) {
+  PParams P{a.q, a.q_f16, a.kv_heads, a.q_heads, a.capacity, a.seq_len, a.num_splits, a.k_codes, a.v_codes,
+            a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids, a.part_o, a.part_ml};
+  dim3 grid(a.num_splits, a.batch * a.kv_heads);
+  hipLaunchKernelGGL(attend_pair_kernel, grid, dim3(kBlock), 0, stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -44,6 +44,9 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supporte
 // Matrix-core variant (Lloyd-Max 2/4-bit keys and values, no near tier, G <= 8).
 bool mfma_attend_supported(const AttendArgs &a);
 hipError_t launch_attend_mfma(const AttendArgs &a, hipStream_t stream, bool *supported);
+// Pair-table variant (4-bit keys and values, head_dim 128, no near tier, G <= 8).
+bool pair_attend_supported(const AttendArgs &a);
+hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream);
 
 // Split-merge launch (validated arguments).
 struct MergeArgs {

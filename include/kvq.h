@@ -136,7 +136,7 @@ kvq_status kvq_quantize_append(const kvq_cache *cache, const void *k, const void
  * (KV head h / (q_heads / kv_heads)):
  *   far splits:  tokens [0, seq_len) of the code buffers, cut into num_splits
  *                contiguous chunks of C = ceil(seq_len / num_splits) tokens
- *                rounded up to a multiple of 16 (split s covers
+ *                rounded up to a multiple of 32 (split s covers
  *                [s*C, min((s+1)*C, seq_len)); trailing splits may be empty);
  *                scores s_t = (R q) . khat_t / sqrt(d) with khat the rotated
  *                reconstruction; values accumulated in the rotated domain.
@@ -151,6 +151,7 @@ kvq_status kvq_quantize_append(const kvq_cache *cache, const void *k, const void
  *           original domain; far splits rotated domain.
  *   q       device [batch][q_heads][head_dim] in q_dtype (KVQ_F32/F16),
  *           original domain, 16-byte aligned.
+ * part_o and part_ml must be 16-byte aligned.
  * The softmax scale 1/sqrt(d) is applied inside.  num_near_splits must be 0
  * unless the cache has a near tier.  Errors: KVQ_EINVAL, KVQ_ERANGE
  * (seq_len > capacity), KVQ_EUNSUPPORTED (GQA group or format combination not

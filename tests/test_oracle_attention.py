@@ -97,7 +97,7 @@ def test_brute_force_tiny_every_code_pattern():
         assert np.allclose(o, ref, atol=1e-14)
 
 
-@pytest.mark.parametrize("S,align", [(1, 1), (2, 1), (3, 1), (7, 1), (64, 1), (100, 1), (3, 16), (7, 16)])
+@pytest.mark.parametrize("S,align", [(1, 1), (2, 1), (3, 1), (7, 1), (64, 1), (100, 1), (3, 16), (7, 16), (3, 32), (7, 32)])
 def test_split_merge_invariance(S, align):
     rng = np.random.default_rng(6)
     d, T = 64, 97
@@ -111,7 +111,7 @@ def test_split_merge_invariance(S, align):
     assert np.allclose(out, p @ v, atol=1e-13)
     assert lse == pytest.approx(s.max() + math.log(np.exp(s - s.max()).sum()), abs=1e-12)
     bounds = O.split_bounds(T, S, align)
-    assert all((a % align == 0) for a, _ in bounds)
+    assert all((a % align == 0 or a == T) for a, _ in bounds)
     assert bounds[0][0] == 0 and bounds[-1][1] == T
     assert all(b0 == a1 for (_, b0), (a1, _) in zip(bounds, bounds[1:]))
 

@@ -143,8 +143,8 @@ def _check_partials(wl, inp, po, pml, k_rot, v_rot, kn, vn, S, SN):
             pieces = []
             if SN:
                 pieces.append(O.attention_partials(q64[b, h] / math.sqrt(d), kn[b, hk].astype(np.float64),
-                                                   vn[b, hk].astype(np.float64), SN, align=16))
-            pieces.append(O.attention_partials(qr[b, h] / math.sqrt(d), k_rot[b, hk], v_rot[b, hk], S, align=16))
+                                                   vn[b, hk].astype(np.float64), SN, align=32))
+            pieces.append(O.attention_partials(qr[b, h] / math.sqrt(d), k_rot[b, hk], v_rot[b, hk], S, align=32))
             m = np.concatenate([p[0] for p in pieces])
             l = np.concatenate([p[1] for p in pieces])
             o = np.concatenate([p[2] for p in pieces])
