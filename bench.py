@@ -302,7 +302,7 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "attend_kernel", "bytes_per_launch": att_bytes,
+                     "kernel": caches[0].attention_kernel(wl.q_heads, near_splits), "bytes_per_launch": att_bytes,
                      "avg_us": round(att_avg * 1e3, 3), "min_us": round(min(att_ms) * 1e3, 3)},
     }
     if not args.no_cpu_baseline:

@@ -21,8 +21,8 @@ KVQ_F32, KVQ_F16 = 0, 1
 KVQ_LM2, KVQ_LM3, KVQ_LM4, KVQ_FP8_E4M3 = 2, 3, 4, 8
 
 EXPORTED = ("kvq_row_bytes", "kvq_lloyd_max", "kvq_make_signs", "kvq_quantize_append",
-            "kvq_decode_attention", "kvq_merge", "kvq_partials_floats", "kvq_status_string",
-            "kvq_last_error")
+            "kvq_decode_attention", "kvq_decode_attention_kernel", "kvq_merge", "kvq_partials_floats",
+            "kvq_status_string", "kvq_last_error")
 
 
 class KVQError(RuntimeError):
@@ -64,6 +64,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvq_make_signs": (I32, [U64, I32, P]),
         "kvq_quantize_append": (I32, [CP, P, P, I32, I32, I32, P]),
         "kvq_decode_attention": (I32, [CP, P, I32, I32, I32, I32, I32, P, P, P]),
+        "kvq_decode_attention_kernel": (ctypes.c_char_p, [CP, I32, I32]),
         "kvq_merge": (I32, [CP, P, P, I32, I32, I32, P, P, P]),
         "kvq_partials_floats": (SZ, [I32, I32, I32, I32]),
         "kvq_status_string": (ctypes.c_char_p, [I32]),
@@ -236,6 +237,14 @@ class KVCache:
                                 num_near_splits, out.data_ptr(), 0 if lse is None else lse.data_ptr(),
                                 _stream_handle(part_o.device)), "kvq_merge")
         return out
+
+    def attention_kernel(self, q_heads: int, num_near_splits: int = 0) -> str:
+        """Name of the kernel kvq_decode_attention launches for this cache."""
+        cs = self.struct()
+        name = load().kvq_decode_attention_kernel(ctypes.byref(cs), q_heads, num_near_splits)
+        if not name:
+            raise KVQError(KVQ_EINVAL, "kvq_decode_attention_kernel", load().kvq_last_error().decode())
+        return name.decode()
 
     def decode(self, q, seq_len: int, num_splits: int, num_near_splits: int = 0, lse=None):
         po, pml = self.attend(q, seq_len, num_splits, num_near_splits)

@@ -111,6 +111,18 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q
   return hip_status(e, fn);
 }
 
+const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads, int32_t num_near_splits) {
+  kvq::clear_error();
+  if (check_cache(cache, "kvq_decode_attention_kernel") != KVQ_OK) return nullptr;
+  if (q_heads < 1 || q_heads % cache->kv_heads) return nullptr;
+  kvq::AttendArgs a{nullptr, 0, cache->batch, cache->kv_heads, q_heads, cache->head_dim, cache->capacity, 0, 1,
+                    num_near_splits, cache->near_len, cache->k_format, cache->v_format,
+                    static_cast<const uint8_t *>(cache->k_codes), static_cast<const uint8_t *>(cache->v_codes),
+                    cache->k_norms, cache->v_norms, cache->signs, cache->k_centroids, cache->v_centroids,
+                    cache->near_k, cache->near_v, nullptr, nullptr};
+  return kvq::attend_kernel_name(a);
+}
+
 kvq_status kvq_merge(const kvq_cache *cache, const float *part_o, const float *part_ml, int32_t q_heads,
                      int32_t num_splits, int32_t num_near_splits, float *out, float *lse, hipStream_t stream) {
   const char *fn = "kvq_merge";
@@ -119,6 +131,7 @@ kvq_status kvq_merge(const kvq_cache *cache, const float *part_o, const float *p
   if (!kvq::valid_head_dim(cache->head_dim))
     return kvq::fail(KVQ_EUNSUPPORTED, "%s: head_dim=%d", fn, cache->head_dim);
   if (!part_o || !part_ml || !out || !cache->signs) return kvq::fail(KVQ_EINVAL, "%s: NULL buffer", fn);
+  if (!aligned(part_o, 16)) return kvq::fail(KVQ_EINVAL, "%s: part_o must be 16-byte aligned", fn);
   if (cache->batch < 1 || q_heads < 1 || num_splits < 0 || num_near_splits < 0 || num_splits + num_near_splits < 1)
     return kvq::fail(KVQ_EINVAL, "%s: bad shape", fn);
   if ((int64_t)cache->batch * q_heads > (1ll << 31) - 1) return kvq::fail(KVQ_EINVAL, "%s: grid too large", fn);

@@ -405,6 +405,12 @@ hipError_t by_format(const AttendArgs &a, hipStream_t stream, bool *ok) {
 
 }  // namespace
 
+const char *attend_kernel_name(const AttendArgs &a) {
+  if (pair_attend_supported(a)) return "attend_pair_kernel";
+  if (mfma_attend_supported(a)) return "attend_mfma_kernel";
+  return "attend_kernel";
+}
+
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported) {
   if (pair_attend_supported(a)) {
     *supported = true;

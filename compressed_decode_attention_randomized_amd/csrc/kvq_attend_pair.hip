@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include "kvq_internal.h"
+#include "kvq_lane.h"
 
 namespace kvq {
 namespace {
@@ -109,70 +110,6 @@ __device__ inline uint2_t table_read(const uint8_t *tab, uint32_t addr) {
 // xor-1 exchange (DPP quad permutation [1, 0, 3, 2]).
 __device__ inline float lane_swap1(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-}
-
-// Max / sum over the four 16-lane rows holding one column, with the gfx950
-// row swaps (two distinct registers per swap).
-__device__ inline void swap16(float &a, float &b) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-__device__ inline void swap32(float &a, float &b) {
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-__device__ inline float max_rows(float x) {
-  float a = x, b = x;
-  swap16(a, b);
-  x = fmaxf(a, b);
-  a = x;
-  b = x;
-  swap32(a, b);
-  return fmaxf(a, b);
-}
-__device__ inline float sum_rows(float x) {
-  float a = x, b = x;
-  swap16(a, b);
-  x = a + b;
-  a = x;
-  b = x;
-  swap32(a, b);
-  return a + b;
-}
-
-// Value of lane l ^ M (M = 1, 2, 4, 8, 16, 32) without LDS: DPP for the
-// exchanges inside a 16-lane row (row_ror:n hands lane i the value of lane
-// i - n mod 16), the gfx950 row swaps across rows.  After
-// v_permlane16_swap on two copies of x, lanes of even rows find their xor-16
-// partner in the second copy and lanes of odd rows in the first; likewise
-// for v_permlane32_swap and the two halves of the wave.
-template <int M>
-__device__ inline float xor_lane(float x, int lane) {
-  const int xi = __builtin_bit_cast(int, x);
-  if constexpr (M == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false));
-  if constexpr (M == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false));
-  if constexpr (M == 4) {
-    const int up = __builtin_amdgcn_mov_dpp(xi, 0x12C, 0xF, 0xF, false);    // row_ror:12: lane i + 4
-    const int dn = __builtin_amdgcn_mov_dpp(xi, 0x124, 0xF, 0xF, false);    // row_ror:4: lane i - 4
-    return __builtin_bit_cast(float, (lane & 4) ? dn : up);
-  }
-  if constexpr (M == 8) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0x128, 0xF, 0xF, false));
-  if constexpr (M == 16) {
-    float a = x, b = x;
-    swap16(a, b);
-    return (lane & 16) ? a : b;
-  }
-  if constexpr (M == 32) {
-    float a = x, b = x;
-    swap32(a, b);
-    return (lane & 32) ? a : b;
-  }
-}
-
-// Walsh-Hadamard butterfly across lanes at lane stride M: the lower lane of
-// each pair keeps x + partner, the upper one partner - x.
-template <int M>
-__device__ inline float butterfly(float x, int lane) {
-  const float o = xor_lane<M>(x, lane);
-  return (lane & M) ? (o - x) : (x + o);
 }
 
 struct Tile {
@@ -374,18 +311,9 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
       z0 = (sg & 0x80u) ? -z0 : z0;
       z1 = (sg & 0x8000u) ? -z1 : z1;
       float a = z0 + z1, c = z0 - z1;
-      a = butterfly<1>(a, lane);  c = butterfly<1>(c, lane);
-      a = butterfly<2>(a, lane);  c = butterfly<2>(c, lane);
-      a = butterfly<4>(a, lane);  c = butterfly<4>(c, lane);
-      a = butterfly<8>(a, lane);  c = butterfly<8>(c, lane);
-      a = butterfly<16>(a, lane); c = butterfly<16>(c, lane);
-      a = butterfly<32>(a, lane); c = butterfly<32>(c, lane);
-      float zmax = fmaxf(fabsf(a), fabsf(c));
-      zmax = fmaxf(zmax, xor_lane<1>(zmax, lane));
-      zmax = fmaxf(zmax, xor_lane<2>(zmax, lane));
-      zmax = fmaxf(zmax, xor_lane<4>(zmax, lane));
-      zmax = fmaxf(zmax, xor_lane<8>(zmax, lane));
-      zmax = max_rows(zmax);
+      a = fwht_lanes(a, lane);
+      c = fwht_lanes(c, lane);
+      const float zmax = wave_max(fmaxf(fabsf(a), fabsf(c)), lane);
       const float qscale = (zmax > 0.f) ? exp2f(7.f - ceilf(log2f(zmax))) : 1.f;
       const float za = a * qscale, zc = c * qscale;
       const _Float16 ha = (_Float16)za, hc = (_Float16)zc;

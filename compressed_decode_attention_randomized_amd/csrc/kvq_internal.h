@@ -41,6 +41,8 @@ struct AttendArgs {
   float *part_o, *part_ml;
 };
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported);
+// Name of the kernel launch_attend picks for these arguments.
+const char *attend_kernel_name(const AttendArgs &a);
 // Matrix-core variant (Lloyd-Max 2/4-bit keys and values, no near tier, G <= 8).
 bool mfma_attend_supported(const AttendArgs &a);
 hipError_t launch_attend_mfma(const AttendArgs &a, hipStream_t stream, bool *supported);

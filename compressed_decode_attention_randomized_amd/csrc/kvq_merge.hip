@@ -1,11 +1,14 @@
 // Split merge and the single inverse rotation, gfx950.
 //
-// One work-group of D threads per (b, query head); thread j owns output
-// coordinate j.  All threads read the split states (m_s, l_s), form
+// One wave per (b, query head); lane l owns output coordinates
+// [l*E, (l+1)*E), E = D / 64.  The lanes read the split states (m_s, l_s)
+// 64 at a time and form, with wave reductions,
 //   M = max m_s, w_s = l_s exp(m_s - M), W = sum w_s,
-// and accumulate near-tier splits (original domain) and far-tier splits
-// (rotated domain) separately.  The far sum is mapped back once with
-// R^T y = s * (H y) / sqrt(D), the Walsh-Hadamard transform running in LDS.
+// then accumulate the near-tier splits (original domain) and the far-tier
+// splits (rotated domain) separately, eight splits' loads in flight at a
+// time.  The far sum is mapped back once with R^T y = s * (H y) / sqrt(D):
+// the Walsh-Hadamard stages inside a lane's E coordinates run in registers,
+// the six across lanes with DPP and row swaps.
 // Source: "FoveatedKV", "Making it fast" (split-K partial states merged after
 // the fused pass; near and far tiers share one softmax).
 #include <hip/hip_runtime.h>
@@ -13,72 +16,126 @@
 #include <stdint.h>
 
 #include "kvq_internal.h"
+#include "kvq_lane.h"
 
 namespace kvq {
 namespace {
 
+constexpr int kUnroll = 8;
+
+template <int E>
+__device__ inline void load_row(const float *p, float (&v)[E]) {
+  if constexpr (E == 1) {
+    v[0] = p[0];
+  } else if constexpr (E == 2) {
+    const float2 t = *reinterpret_cast<const float2 *>(p);
+    v[0] = t.x;
+    v[1] = t.y;
+  } else {
+    static_assert(E == 4, "coordinates per lane");
+    const float4 t = *reinterpret_cast<const float4 *>(p);
+    v[0] = t.x;
+    v[1] = t.y;
+    v[2] = t.z;
+    v[3] = t.w;
+  }
+}
+
 template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ part_o, const float *__restrict__ part_ml,
-                                                 int splits, int near_splits, const int8_t *__restrict__ signs,
-                                                 float *__restrict__ out, float *__restrict__ lse) {
-  __shared__ float y[D];
-  const int j = threadIdx.x;
+__global__ __launch_bounds__(64) void merge_kernel(const float *__restrict__ part_o, const float *__restrict__ part_ml,
+                                                  int splits, int near_splits, const int8_t *__restrict__ signs,
+                                                  float *__restrict__ out, float *__restrict__ lse) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x;
   const size_t row = blockIdx.x;
   const int S = splits + near_splits;
   const float *ml = part_ml + row * S * 2;
-  const float *po = part_o + row * S * D;
+  const float *po = part_o + row * S * D + lane * E;
 
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-  float W = 0.f, near_acc = 0.f, far_acc = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float m = ml[2 * s], l = ml[2 * s + 1];
-    const float w = (m == -INFINITY || l == 0.f) ? 0.f : l * expf(m - M);
-    W += w;
-    const float o = po[(size_t)s * D + j];
-    if (s < near_splits) near_acc = fmaf(w, o, near_acc); else far_acc = fmaf(w, o, far_acc);
-  }
-  y[j] = far_acc;
-  __syncthreads();
-  for (int len = 1; len < D; len <<= 1) {
-    const bool active = j < D / 2;
-    const int lo = active ? (j / len) * 2 * len + (j % len) : 0;
-    const float a = active ? y[lo] : 0.f, c = active ? y[lo + len] : 0.f;
-    __syncthreads();
-    if (active) {
-      y[lo] = a + c;
-      y[lo + len] = a - c;
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
+  M = wave_max(M, lane);
+
+  float W = 0.f;
+  float near_acc[E], far_acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) near_acc[e] = far_acc[e] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    float w = 0.f;
+    if (s0 + lane < S) {
+      const float m = ml[2 * (s0 + lane)], l = ml[2 * (s0 + lane) + 1];
+      w = (m == -INFINITY || l == 0.f) ? 0.f : l * expf(m - M);
     }
-    __syncthreads();
+    W += w;
+    const int cnt = min(64, S - s0);
+    for (int k0 = 0; k0 < cnt; k0 += kUnroll) {
+      float v[kUnroll][E];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (k0 + u < cnt) {
+          load_row<E>(po + (size_t)(s0 + k0 + u) * D, v[u]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) v[u][e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int k = min(k0 + u, cnt - 1);
+        const float wk = (k0 + u < cnt) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k)) : 0.f;
+        const bool near = s0 + k0 + u < near_splits;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (near) near_acc[e] = fmaf(wk, v[u][e], near_acc[e]);
+          else far_acc[e] = fmaf(wk, v[u][e], far_acc[e]);
+        }
+      }
+    }
   }
-  const float far = (signs[j] < 0 ? -y[j] : y[j]) * rsqrtf((float)D);
-  out[row * D + j] = (W > 0.f) ? (near_acc + far) / W : 0.f;
-  if (lse && j == 0) lse[row] = (W > 0.f) ? M + logf(W) : -INFINITY;
+  W = wave_sum(W, lane);
+
+  // inverse rotation of the far sum: stages of stride < E inside the lane,
+  // then the six cross-lane stages
+#pragma unroll
+  for (int st = 1; st < E; st <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (!(e & st)) {
+        const float a = far_acc[e], c = far_acc[e + st];
+        far_acc[e] = a + c;
+        far_acc[e + st] = a - c;
+      }
+    }
+  }
+  const float inv_w = (W > 0.f) ? 1.f / W : 0.f;
+  const float rs = rsqrtf((float)D);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float y = fwht_lanes(far_acc[e], lane) * rs;
+    const float far = (signs[lane * E + e] < 0) ? -y : y;
+    out[row * D + lane * E + e] = (near_acc[e] + far) * inv_w;
+  }
+  if (lse && lane == 0) lse[row] = (W > 0.f) ? M + logf(W) : -INFINITY;
+}
+
+template <int D>
+hipError_t go(const MergeArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL(merge_kernel<D>, dim3(a.batch * a.q_heads), dim3(64), 0, stream, a.part_o, a.part_ml,
+                     a.num_splits, a.num_near_splits, a.signs, a.out, a.lse);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream, bool *supported) {
   *supported = true;
-  const dim3 grid(a.batch * a.q_heads);
   switch (a.head_dim) {
-    case 64:
-      hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, a.part_o, a.part_ml, a.num_splits,
-                         a.num_near_splits, a.signs, a.out, a.lse);
-      break;
-    case 128:
-      hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, stream, a.part_o, a.part_ml, a.num_splits,
-                         a.num_near_splits, a.signs, a.out, a.lse);
-      break;
-    case 256:
-      hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, stream, a.part_o, a.part_ml, a.num_splits,
-                         a.num_near_splits, a.signs, a.out, a.lse);
-      break;
-    default:
-      *supported = false;
-      return hipSuccess;
+    case 64: return go<64>(a, stream);
+    case 128: return go<128>(a, stream);
+    case 256: return go<256>(a, stream);
   }
-  return hipGetLastError();
+  *supported = false;
+  return hipSuccess;
 }
 
 }  // namespace kvq

@@ -161,13 +161,19 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q
                                 int32_t num_near_splits, float *part_o, float *part_ml,
                                 hipStream_t stream);
 
+/* Name of the attention kernel kvq_decode_attention launches for this cache,
+ * query-head count and near-split count (for profiles and reports): a static
+ * string, or NULL if the cache description is invalid. */
+const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads, int32_t num_near_splits);
+
 /* Split merge and the single inverse rotation ("Making it fast": split-K
  * partial softmax states merged; rotated-domain values mapped back once):
  *   M = max_s m_s,  w_s = l_s exp(m_s - M),  W = sum_s w_s,
  *   out = ( sum_{near s} w_s o_s + R^T sum_{far s} w_s o_s ) / W
  *   out [batch][q_heads][head_dim] float32 (original domain);
  *   lse [batch][q_heads] float32 = M + log W, or NULL to skip.
- * Partials as written by kvq_decode_attention with the same split counts.
+ * Partials as written by kvq_decode_attention with the same split counts
+ * (part_o 16-byte aligned).
  * Errors: KVQ_EINVAL, KVQ_EHIP. */
 kvq_status kvq_merge(const kvq_cache *cache, const float *part_o, const float *part_ml,
                      int32_t q_heads, int32_t num_splits, int32_t num_near_splits,

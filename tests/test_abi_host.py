@@ -103,6 +103,27 @@ def test_attend_and_merge_validation():
     assert lib.kvq_merge(ctypes.byref(cs), 0, 0xB000, 4, 2, 0, 0xC000, 0, None) == kvq.KVQ_EINVAL
     assert lib.kvq_merge(ctypes.byref(cs), 0xA000, 0xB000, 4, 0, 0, 0xC000, 0, None) == kvq.KVQ_EINVAL
     assert lib.kvq_merge(None, 0xA000, 0xB000, 4, 2, 0, 0xC000, 0, None) == kvq.KVQ_EINVAL
+    assert lib.kvq_merge(ctypes.byref(cs), 0xA004, 0xB000, 4, 2, 0, 0xC000, 0, None) == kvq.KVQ_EINVAL
+    assert _attend(_fake_cache(), po=0xA004) == kvq.KVQ_EINVAL           # misaligned partials
+
+
+def test_attention_kernel_choice():
+    """The kernel kvq_decode_attention dispatches to (no launch involved)."""
+    lib = kvq.load()
+
+    def name(hq=4, SN=0, **over):
+        r = lib.kvq_decode_attention_kernel(ctypes.byref(_fake_cache(**over)), hq, SN)
+        return None if r is None else r.decode()
+
+    assert name() == "attend_pair_kernel"                                # 4-bit K and V, d=128, G=2
+    assert name(hq=2) == "attend_pair_kernel"                            # G=1
+    assert name(hq=32) == "attend_kernel"                                # G=16: above the matrix-core limit
+    assert name(head_dim=256) == "attend_mfma_kernel"
+    assert name(k_format=2, v_format=2) == "attend_mfma_kernel"
+    assert name(k_format=3, v_format=3) == "attend_kernel"
+    assert name(head_dim=64) == "attend_kernel"
+    assert name(k_format=8, k_norms=0, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_kernel"
+    assert name(hq=3) is None and name(head_dim=96) is None
 
 
 def test_status_strings():

@@ -90,7 +90,7 @@ WORKLOADS = {
                                  splits=8, outlier_channels=2, outlier_scale=20.0),
     "llama7b_layer": Workload("llama7b_layer", 2, batch=8, q_heads=32, kv_heads=8,
                               head_dim=128, seq_len=8192, k_bits=4, v_bits=4, dtype="f16",
-                              splits=16, outlier_channels=4, outlier_scale=20.0),
+                              splits=4, outlier_channels=4, outlier_scale=20.0),
     "long_context": Workload("long_context", 3, batch=1, q_heads=32, kv_heads=8,
                              head_dim=128, seq_len=32768, k_bits=4, v_bits=4, dtype="f16",
                              splits=64, lognormal_sigma=1.0),
