@@ -26,7 +26,9 @@ DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-munsafe-fp-atomics", "-ffp-contract=fast",
                 # matrix-core accumulators stay in VGPRs (no AGPR round trips around VALU rescaling)
-                "-mllvm", "-amdgpu-mfma-vgpr-form"]
+                "-mllvm", "-amdgpu-mfma-vgpr-form",
+                # one-lane LDS counter claims stay one atomic whose answer is read where the code reads it
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__"]
 
 

@@ -13,18 +13,23 @@
 //
 //   keys    token n of the tile in A row n; the byte pair (2kb, 2kb+1) of the
 //           lane's 16-byte slice gives coordinates 4kb..4kb+3 as k-slot pairs
-//           (c_hi, c_lo); B columns 0..7 hold (z_hi, z_hi) of head n, columns
-//           8..15 hold (z_lo, 0), so column h + column h+8 is the score of
-//           head h up to the fp32 accumulation.
+//           (c_hi, c_lo); B column 2h holds (z_hi, z_hi) of head h and column
+//           2h+1 holds (z_lo, 0), so columns 2h + 2h+1 give the score of head
+//           h up to the fp32 accumulation.
 //   values  k-slot pairs are the 4 tokens of the lane group; a value byte
 //           built from the same coordinate of two tokens (low nibble token
 //           t, high nibble token t+1) reads both tokens' (c_hi, c_lo) at once;
-//           A rows 0..7 hold (w_hi, w_hi) and rows 8..15 (w_lo, w_lo) of the
-//           weight w = exp2(score - max) * norm.
+//           A row 2h holds (w_hi, w_hi) and row 2h+1 (w_lo, w_lo) of head h's
+//           weight w = exp2(score - max) * norm, so the two halves of a head
+//           land in the same lane of the accumulator.
 //
-// Work mapping: grid (split, b * Hkv), 6 waves per work-group walking the
-// split's 16-token tiles round robin, two tiles in flight per wave.  All HBM
-// reads are buffer loads with the cache arrays as SGPR resources.
+// Work mapping: grid (split group, b * Hkv), one work-group of 16 waves per
+// compute unit sharing one table; with more splits than compute units a
+// work-group covers 2-8 consecutive splits of one (b, KV head), one wave
+// group each.  Waves take 16-token tiles from an LDS counter (so all waves
+// of a group finish within a tile of each other whatever their issue
+// priority), two tiles in flight per wave.  All HBM reads are buffer loads
+// with the cache arrays as SGPR resources.
 // Sources: "The Engineering Behind AdapTQ", "Engineering the Hot Path"
 // (rotate q once, score from codes through a table, no dequantize pass);
 // "FoveatedKV", "Making it fast" (split-K, pre-scaled q, online softmax with
@@ -50,7 +55,7 @@ constexpr int kWaves = 16;
 constexpr int kMinWaves = 4;                   // waves per SIMD the register budget is sized for
 constexpr int kBlock = kWaves * 64;
 constexpr int kTile = 16;
-constexpr int kPairTok = 2 * kTile;             // tokens per claimed tile pair (the split chunk granule)
+constexpr int kChunkTok = 32;                   // split chunks are multiples of this many tokens
 constexpr int kGMax = 8;
 constexpr int kRow = D / 2;                     // packed bytes per 4-bit vector
 constexpr int kVDL = D / 16;                    // value coordinates per lane
@@ -67,6 +72,7 @@ struct PParams {
   const void *q;
   int q_f16;
   int kv_heads, q_heads, capacity, seq_len, num_splits;
+  int group_log2;                  // log2 of the splits one work-group covers (its wave groups)
   const uint8_t *k_codes, *v_codes;
   const uint16_t *k_norms, *v_norms;
   const int8_t *signs;
@@ -164,6 +170,19 @@ __device__ inline void value_update(const uint32_t (&ev)[2], const uint32_t (&od
   }
 }
 
+// f16(half H of a packed pair) * f in one v_fma_mix (the product of an fp16
+// and an fp32 value, rounded once to fp32: equal to a conversion then a
+// multiply).
+template <int H>
+__device__ inline float half_mul(uint32_t packed, float f) {
+  float r;
+  if constexpr (H == 0)
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(packed), "v"(f));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(packed), "v"(f));
+  return r;
+}
+
 // One 16-token tile of the online softmax.  TAIL masks tokens at or past t1.
 template <bool TAIL>
 __device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], const uint8_t *tab, uint32_t slot8,
@@ -178,8 +197,8 @@ __device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], 
   float mt = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float nk = half_value((t.kn[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-    float v = (dk[i] + lane_swap1(dk[i])) * (nk * sfac);
+    const float nks = (i & 1) ? half_mul<1>(t.kn[i >> 1], sfac) : half_mul<0>(t.kn[i >> 1], sfac);
+    float v = (dk[i] + lane_swap1(dk[i])) * nks;
     if constexpr (TAIL) v = (tb + 4 * g + i < t1) ? v : -INFINITY;
     s[i] = v;
     mt = fmaxf(mt, v);
@@ -234,22 +253,30 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   __shared__ __attribute__((aligned(16))) uint32_t qtab[2 * kGMax][kRowPad];
   __shared__ float red_ml[kWaves][kGMax][2];
   __shared__ float qfac[kGMax];
-  __shared__ uint32_t next_pair;
+  __shared__ float cent[32];
+  __shared__ uint32_t sgnw[D / 4];
+  __shared__ uint32_t next_tile[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n = lane & 15;
   const int G = P.q_heads / P.kv_heads;
-  const int split = blockIdx.x, bh = blockIdx.y;
+  const int bh = blockIdx.y;
   const int b = bh / P.kv_heads, hkv = bh - b * P.kv_heads;
+  // the work-group covers 2^group_log2 consecutive splits of one (b, KV head),
+  // each with its own group of gw waves (all share the query and the tables)
+  const int gw = kWaves >> P.group_log2;
+  const int grp = wave / gw, gwave = wave - grp * gw;
+  const int split = (blockIdx.x << P.group_log2) + grp;
 
-  // chunks of ceil(T/S) tokens rounded up to a multiple of 32; whole tile
-  // pairs [t0, t1f) go through the main loop, the rest of the last split
-  // (under 32 tokens) after it
-  const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + kPairTok - 1) / kPairTok * kPairTok;
+  // chunks of ceil(T/S) tokens rounded up to a multiple of 32; full tiles
+  // [t0, t1f) go through the main loop, a partial last tile (only the last
+  // split can have one) after it; splits past S (a partly used last group)
+  // get no tokens and write nothing
+  const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + kChunkTok - 1) / kChunkTok * kChunkTok;
   const int t0 = min(P.seq_len, split * chunk), t1 = min(P.seq_len, t0 + chunk);
-  const int npairs = (t1 - t0) / kPairTok;
-  const int t1f = t0 + npairs * kPairTok;
+  const int ntiles = (t1 - t0) / kTile;
+  const int t1f = t0 + ntiles * kTile;
   const uint32_t cap = (uint32_t)P.capacity;
   Sources src;
   src.kc = make_rsrc(P.k_codes + (size_t)bh * cap * kRow, cap * kRow);
@@ -257,45 +284,53 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   src.kn = make_rsrc(P.k_norms + (size_t)bh * cap, cap * 2);
   src.vn = make_rsrc(P.v_norms + (size_t)bh * cap, cap * 2);
 
-  // ---- small loads first (centroids, this wave's query head, signs), then
-  // the first tile pair in issue order, so that waiting for the small loads
-  // never waits for a tile and the tile order matches the main loop's ----
+  // ---- set-up loads, then the first two tiles ----
+  // Every compute unit reads the same centroid and sign bytes, so one wave
+  // per work-group fetches them into LDS (one load instruction each) rather
+  // than every wave hitting the same cache lines; the query rows are read by
+  // the waves that rotate them.  The tile loads go out only after these have
+  // landed: issued together, the first tiles of the whole chip (two per
+  // wave, 4 KB each) queue ahead of the set-up loads in memory and hold the
+  // whole work-group at its first barrier.
+  static_assert(kBlock == 1024, "pair-table fill assumes 1024 threads");
+  if (wave == 0) {
+    if (lane < 32) cent[lane] = (lane < 16) ? P.k_centroids[lane] : P.v_centroids[lane - 16];
+    else sgnw[lane - 32] = *reinterpret_cast<const uint32_t *>(P.signs + 4 * (lane - 32));
+  }
+  const bool has_q = wave < G;
+  uint32_t qh = 0u;
+  float2 qf = {0.f, 0.f};
+  if (has_q) {
+    const size_t qoff = ((size_t)b * P.q_heads + hkv * G + wave) * D + lane * 2;
+    if (P.q_f16) qh = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(P.q) + qoff);
+    else qf = *reinterpret_cast<const float2 *>(static_cast<const float *>(P.q) + qoff);
+  }
+  if (tid < kWaves) next_tile[tid] = 2 * gw;
+  __syncthreads();
+
+  int ia = gwave, ic = gwave + gw;                   // first tiles of this wave; later ones from its group's counter
+  Tile ta, tc;
+  load_tile(ta, src, t0 + ia * kTile, ia >= ntiles, g, n);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(tc, src, t0 + ic * kTile, ic >= ntiles, g, n);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint16_t sg = (uint16_t)(sgnw[lane >> 1] >> (16 * (lane & 1)));   // signs of coordinates 2l, 2l+1
+
+  // ---- pair tables ----
   // Table chunks (16 bytes, two slots) are written by consecutive lanes:
   // thread t writes chunks t + 1024k, k = 0..3, i.e. rows (code bytes)
   // t/16 + 64k, key table if t % 16 < 8 else value table.  The low nibble of
   // those rows is (t/16) % 16 for every k, the high nibble t/256 + 4k.
-  static_assert(kBlock == 1024, "pair-table fill assumes 1024 threads");
-  const float *ctab = ((tid & 15) < 8) ? P.k_centroids : P.v_centroids;
-  const float c_lo = ctab[(tid >> 4) & 15];
-  float c_hi[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) c_hi[k] = ctab[(tid >> 8) + 4 * k];
-  const bool has_q = wave < G;
-  const size_t qoff = ((size_t)b * P.q_heads + hkv * G + (has_q ? wave : 0)) * D + lane * 2;
-  uint32_t qh = 0u;
-  float2 qf = {0.f, 0.f};
-  if (P.q_f16) qh = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(P.q) + qoff);
-  else qf = *reinterpret_cast<const float2 *>(static_cast<const float *>(P.q) + qoff);
-  const uint16_t sg = *reinterpret_cast<const uint16_t *>(P.signs + lane * 2);
-  __builtin_amdgcn_sched_barrier(0);
-  int pr = wave;                                     // first pair of this wave; later ones from the counter
-  Tile ta, tc;
-  load_tile(ta, src, t0 + pr * kPairTok, pr >= npairs, g, n);
-  __builtin_amdgcn_sched_barrier(0);
-  load_tile(tc, src, t0 + pr * kPairTok + kTile, pr >= npairs, g, n);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- pair tables ----
   {
-    const uint32_t lo = split_entry(c_lo * kCodeScale);
+    const int cbase = ((tid & 15) < 8) ? 0 : 16;
+    const uint32_t lo = split_entry(cent[cbase + ((tid >> 4) & 15)] * kCodeScale);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t hi = split_entry(c_hi[k] * kCodeScale);
+      const uint32_t hi = split_entry(cent[cbase + (tid >> 8) + 4 * k] * kCodeScale);
       const uint4_t e = {lo, hi, lo, hi};
       *reinterpret_cast<uint4_t *>(tab + (tid + 1024 * k) * 16) = e;
     }
   }
-  if (tid == 0) next_pair = kWaves;
 
   // ---- rotated query of head `wave` (waves G..7 write zero rows) ----
   // Lane l holds coordinates 2l, 2l+1: sign flip, the stride-1 butterfly in
@@ -341,33 +376,44 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   for (int dt = 0; dt < kVDL; ++dt) dv[dt] = (float4_t){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // The two tiles of a pair use the two tile buffers; each buffer is refilled
-  // with the next claimed pair right after use.  The explicit vmcnt(7) waits
-  // for the older tile's seven loads only.  The loop has no exit inside its
-  // body; a pair index at or past npairs ends it (its loads return zeros).
-  while (pr < npairs) {
+  // Tiles alternate between the two tile buffers; each buffer is refilled
+  // with a newly claimed tile right after use (ia < ic always holds, so once
+  // ic runs past the end the next ia does too).  Every iteration issues both
+  // buffers' loads, so the explicit vmcnt(7) (the older tile's seven loads)
+  // is the only wait for a tile's data; loads past the end return zeros.
+  // The counter's answer is first read after the tile, so the atomic's
+  // latency hides behind the tile's own LDS traffic.
+  while (ia < ntiles) {
     uint32_t nx = 0u;
-    if (lane == 0) nx = atomicAdd(&next_pair, 1u);
-    const int pn = __builtin_amdgcn_readfirstlane(nx);
-    const int tb = t0 + pr * kPairTok, tn = t0 + pn * kPairTok;
+    if (lane == 0) nx = atomicAdd(&next_tile[grp], 1u);
     __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-    process_tile<false>(ta, bk, tab, slot8, sfac, tb, t1, g, n, dv, m_run, l_run);
-    load_tile(ta, src, tn, pn >= npairs, g, n);
-    __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-    process_tile<false>(tc, bk, tab, slot8, sfac, tb + kTile, t1, g, n, dv, m_run, l_run);
-    load_tile(tc, src, tn + kTile, pn >= npairs, g, n);
-    pr = pn;
+    process_tile<false>(ta, bk, tab, slot8, sfac, t0 + ia * kTile, t1, g, n, dv, m_run, l_run);
+    asm volatile("" : "+v"(nx));                     // keeps the read of the answer here
+    const int na = __builtin_amdgcn_readfirstlane(nx);
+    load_tile(ta, src, t0 + na * kTile, na >= ntiles, g, n);
+    int nc = ntiles;
+    if (ic < ntiles) {
+      uint32_t ny = 0u;
+      if (lane == 0) ny = atomicAdd(&next_tile[grp], 1u);
+      __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
+      process_tile<false>(tc, bk, tab, slot8, sfac, t0 + ic * kTile, t1, g, n, dv, m_run, l_run);
+      asm volatile("" : "+v"(ny));
+      nc = __builtin_amdgcn_readfirstlane(ny);
+    }
+    load_tile(tc, src, t0 + nc * kTile, nc >= ntiles, g, n);
+    ia = na;
+    ic = nc;
   }
-  // the last split's tokens [t1f, t1): up to two tiles, waves 0 and 1
-  if (wave < 2 && t1f + wave * kTile < t1) {
-    load_tile(ta, src, t1f + wave * kTile, false, g, n);
-    process_tile<true>(ta, bk, tab, slot8, sfac, t1f + wave * kTile, t1, g, n, dv, m_run, l_run);
+  // the last split's partial tile [t1f, t1)
+  if (gwave == 0 && t1f < t1) {
+    load_tile(ta, src, t1f, false, g, n);
+    process_tile<true>(ta, bk, tab, slot8, sfac, t1f, t1, g, n, dv, m_run, l_run);
   }
 
   // ---- wave epilogue: l per head over the 4 lane groups; per-head value rows to LDS ----
   l_run = sum_rows(l_run);
   __syncthreads();                                   // every wave is done with the tables
-  float *red_acc = reinterpret_cast<float *>(tab);   // [wave][head][D]
+  float *red_acc = reinterpret_cast<float *>(tab);   // per wave: 8 heads x D floats
   {
     float4_t h0[2], h1[2];
 #pragma unroll
@@ -377,12 +423,13 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
       h1[q] = (float4_t){dv[4 * q][2] + dv[4 * q][3], dv[4 * q + 1][2] + dv[4 * q + 1][3],
                          dv[4 * q + 2][2] + dv[4 * q + 2][3], dv[4 * q + 3][2] + dv[4 * q + 3][3]};
     }
-    float *r0 = red_acc + ((size_t)wave * kGMax + 2 * g) * D + n * kVDL;
-    float *r1 = r0 + D;
-    *reinterpret_cast<float4_t *>(r0) = h0[0];
-    *reinterpret_cast<float4_t *>(r0 + 4) = h0[1];
-    *reinterpret_cast<float4_t *>(r1) = h1[0];
-    *reinterpret_cast<float4_t *>(r1 + 4) = h1[1];
+    // layout [wave][g][part][n][4]: part = 2 * (head - 2g) + half, so each
+    // 16-lane row of a write covers 256 contiguous bytes
+    float *r = red_acc + ((size_t)(wave * 4 + g) * 4 * 16 + n) * 4;
+    *reinterpret_cast<float4_t *>(r) = h0[0];
+    *reinterpret_cast<float4_t *>(r + 64) = h0[1];
+    *reinterpret_cast<float4_t *>(r + 128) = h1[0];
+    *reinterpret_cast<float4_t *>(r + 192) = h1[1];
   }
   if (lane < 2 * kGMax && !(lane & 1)) {
     red_ml[wave][lane >> 1][0] = m_run;
@@ -390,24 +437,31 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   }
   __syncthreads();
 
-  // ---- merge the waves ----
-  for (int i = tid; i < G * (D / 4); i += kBlock) {
-    const int h = i / (D / 4), j = (i - h * (D / 4)) * 4;
+  // ---- merge each group's waves: one thread per (group, head, coordinate);
+  // a wave's lanes share (group, head), so the state reads are broadcasts
+  // and the value reads are consecutive ----
+  const int ngroups = 1 << P.group_log2;
+  for (int i = tid; i < ngroups * G * D; i += kBlock) {
+    const int gi = i / (G * D);
+    const int r = i - gi * (G * D);
+    const int h = r / D, j = r - h * D;
+    const int sp = (blockIdx.x << P.group_log2) + gi;
+    if (sp >= P.num_splits) continue;
+    const int w0 = gi * gw;
     float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][h][0]);
-    float l = 0.f;
-    float4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = red_ml[w][h][0];
+#pragma unroll 4
+    for (int w = 0; w < gw; ++w) M = fmaxf(M, red_ml[w0 + w][h][0]);
+    float l = 0.f, o = 0.f;
+#pragma unroll 4
+    for (int w = 0; w < gw; ++w) {
+      const float mw = red_ml[w0 + w][h][0];
       const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-      l += red_ml[w][h][1] * f;
-      o += *reinterpret_cast<const float4_t *>(red_acc + ((size_t)w * kGMax + h) * D + j) * f;
+      l += red_ml[w0 + w][h][1] * f;
+      // head h = 2g + hp, coordinate j = 8n + c: part 2hp + c/4, float c % 4
+      o += red_acc[(((size_t)((w0 + w) * 4 + (h >> 1)) * 4 + 2 * (h & 1) + ((j >> 2) & 1)) * 16 + (j >> 3)) * 4 + (j & 3)] * f;
     }
-    const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * P.num_splits + split;
-    const float inv = (l > 0.f) ? 1.f / (l * kCodeScale) : 0.f;
-    *reinterpret_cast<float4_t *>(P.part_o + row * D + j) = o * inv;
+    const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * P.num_splits + sp;
+    P.part_o[row * D + j] = (l > 0.f) ? o / (l * kCodeScale) : 0.f;
     if (j == 0) {
       P.part_ml[row * 2 + 0] = (M == -INFINITY) ? -INFINITY : M * kLn2;
       P.part_ml[row * 2 + 1] = l;
@@ -425,9 +479,18 @@ bool pair_attend_supported(const AttendArgs &a) {
 }
 
 hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream) {
-  PParams P{a.q, a.q_f16, a.kv_heads, a.q_heads, a.capacity, a.seq_len, a.num_splits, a.k_codes, a.v_codes,
+  // One work-group fills a compute unit.  When the splits outnumber the
+  // compute units, a work-group takes 2, 4 or 8 consecutive splits of one
+  // (b, KV head) with a wave group each instead of running in several rounds.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int64_t pairs = (int64_t)a.batch * a.kv_heads;
+  int lg = 0;
+  while (lg < 3 && pairs * ((a.num_splits + (1 << lg) - 1) >> lg) > (int64_t)cus) ++lg;
+  PParams P{a.q, a.q_f16, a.kv_heads, a.q_heads, a.capacity, a.seq_len, a.num_splits, lg, a.k_codes, a.v_codes,
             a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids, a.part_o, a.part_ml};
-  dim3 grid(a.num_splits, a.batch * a.kv_heads);
+  dim3 grid((a.num_splits + (1 << lg) - 1) >> lg, a.batch * a.kv_heads);
   hipLaunchKernelGGL(attend_pair_kernel, grid, dim3(kBlock), 0, stream, P);
   return hipGetLastError();
 }
