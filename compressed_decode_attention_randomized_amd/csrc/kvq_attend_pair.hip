@@ -5,11 +5,11 @@
 // operand registers of both codes at once: entry(byte) = (e(c[lo]), e(c[hi])),
 // e(x) the fp16 (hi, lo) split of x = RN(x) + RN(x - RN(x)) in one 32-bit
 // word.  So one 64-bit LDS read serves two codes and needs one address op.
-// The table is replicated over 16 lane slots (address = byte*256 + slot*8,
-// slot = lane % 16) so that the 16 lanes an LDS cycle serves never meet in a
-// bank; a key table and a value table share each 256-byte row (value table at
-// +128).  The address is one v_perm: slot*8 from a per-lane register in byte
-// 0, the code byte in byte 1.
+// The table is replicated over 32 lane slots (address = byte*256 + slot*8,
+// slot = lane % 32) so that the 32 lanes an LDS cycle serves use all 64 banks
+// and never meet in one; the value table follows the key table at +64 KB.
+// The address is one v_perm: slot*8 (and the +64 KB) from a per-lane
+// register, the code byte in byte 1.
 //
 //   keys    token n of the tile in A row n; the byte pair (2kb, 2kb+1) of the
 //           lane's 16-byte slice gives coordinates 4kb..4kb+3 as k-slot pairs
@@ -101,11 +101,12 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRawBufferFlags);
 }
 
-// v_perm selector putting byte B of the first operand into byte 1 and byte 0
-// of the second (the lane's slot offset) into byte 0; bytes 2, 3 become zero.
+// Table address of code byte B of `word` in one v_perm: byte 0 and byte 2
+// come from the lane's slot register (slot * 8, plus 1 in byte 2 for the
+// value table), byte 1 is the code byte, byte 3 is zero.
 template <int B>
-__device__ inline uint32_t pair_addr(uint32_t word, uint32_t slot8) {
-  return __builtin_amdgcn_perm(word, slot8, 0x0C0C0000u | ((4u + B) << 8));
+__device__ inline uint32_t pair_addr(uint32_t word, uint32_t slotreg) {
+  return __builtin_amdgcn_perm(word, slotreg, 0x0C020000u | ((4u + B) << 8));
 }
 
 template <int OFF>
@@ -124,27 +125,36 @@ struct Tile {
   uint2_t kn, vn;      // fp16 norms of tokens 4g..4g+3
 };
 
+// Per (b, KV head) cache slices; a tile's loads use a per-lane constant
+// VGPR offset and the tile's token offset in an SGPR (no per-tile vector
+// address arithmetic).
 struct Sources {
-  __amdgpu_buffer_rsrc_t kc, vc, kn, vn;
+  const uint8_t *kc, *vc;
+  const uint16_t *kn, *vn;
+  uint32_t code_bytes, norm_bytes;
+  uint32_t ko, vo, no;                 // per-lane offsets: key slice, value word, norm pair
 };
 
-// Loads of the tile at token tb.  With skip set every offset is moved past
-// the end of its buffer, where buffer loads return zeros without touching
-// memory, so loads need no branch and a tile's wait sits at its first use.
-__device__ inline void load_tile(Tile &t, const Sources &src, int tb, bool skip, int g, int n) {
-  const uint32_t far = skip ? 0x80000000u : 0u;
-  t.kw = __builtin_amdgcn_raw_buffer_load_b128(src.kc, far + (uint32_t)(tb + n) * kRow + g * 16, 0, 0);
-  const int ts = tb + 4 * g;
+// Loads of the tile at token tb.  A skipped tile reads through descriptors
+// of size zero, where buffer loads return zeros without touching memory, so
+// loads need no branch and a tile's wait sits at its first use.
+__device__ inline void load_tile(Tile &t, const Sources &src, int tb, bool skip) {
+  const __amdgpu_buffer_rsrc_t kc = make_rsrc(src.kc, skip ? 0u : src.code_bytes);
+  const __amdgpu_buffer_rsrc_t vc = make_rsrc(src.vc, skip ? 0u : src.code_bytes);
+  const __amdgpu_buffer_rsrc_t kn = make_rsrc(src.kn, skip ? 0u : src.norm_bytes);
+  const __amdgpu_buffer_rsrc_t vn = make_rsrc(src.vn, skip ? 0u : src.norm_bytes);
+  const int cs = tb * kRow, ns = tb * 2;
+  t.kw = __builtin_amdgcn_raw_buffer_load_b128(kc, src.ko, cs, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) t.vw[i] = __builtin_amdgcn_raw_buffer_load_b32(src.vc, far + (uint32_t)(ts + i) * kRow + n * 4, 0, 0);
-  t.kn = __builtin_amdgcn_raw_buffer_load_b64(src.kn, far + (uint32_t)ts * 2, 0, 0);
-  t.vn = __builtin_amdgcn_raw_buffer_load_b64(src.vn, far + (uint32_t)ts * 2, 0, 0);
+  for (int i = 0; i < 4; ++i) t.vw[i] = __builtin_amdgcn_raw_buffer_load_b32(vc, src.vo + i * kRow, cs, 0);
+  t.kn = __builtin_amdgcn_raw_buffer_load_b64(kn, src.no, ns, 0);
+  t.vn = __builtin_amdgcn_raw_buffer_load_b64(vn, src.no, ns, 0);
 }
 
 // Key block kb: coordinates 4kb..4kb+3 of the lane's slice = bytes 2kb, 2kb+1.
 template <int KB = 0>
 __device__ inline void key_scores(const uint4_t &kw, const uint4_t (&bk)[D / 16], const uint8_t *tab,
-                                  uint32_t slot8, float4_t &dk) {
+                                  uint32_t slot8, float4_t &dk) {   // slot8: key slot register
   if constexpr (KB < D / 16) {
     const uint32_t w = kw[KB / 2];
     const uint2_t e0 = table_read<0>(tab, pair_addr<2 * (KB % 2)>(w, slot8));
@@ -160,13 +170,23 @@ template <int M = 0>
 __device__ inline void value_update(const uint32_t (&ev)[2], const uint32_t (&od)[2], const uint8_t *tab,
                                     uint32_t slot8, const half8_t &aw, float4_t (&dv)[kVDL]) {
   if constexpr (M < 4) {
-    const uint2_t a0 = table_read<128>(tab, pair_addr<M>(ev[0], slot8));
-    const uint2_t a1 = table_read<128>(tab, pair_addr<M>(ev[1], slot8));
+    const uint2_t a0 = table_read<0>(tab, pair_addr<M>(ev[0], slot8));
+    const uint2_t a1 = table_read<0>(tab, pair_addr<M>(ev[1], slot8));
     dv[2 * M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(a0, a1), dv[2 * M], 0, 0, 0);
-    const uint2_t b0 = table_read<128>(tab, pair_addr<M>(od[0], slot8));
-    const uint2_t b1 = table_read<128>(tab, pair_addr<M>(od[1], slot8));
+    const uint2_t b0 = table_read<0>(tab, pair_addr<M>(od[0], slot8));
+    const uint2_t b1 = table_read<0>(tab, pair_addr<M>(od[1], slot8));
     dv[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(b0, b1), dv[2 * M + 1], 0, 0, 0);
     value_update<M + 1>(ev, od, tab, slot8, aw, dv);
+  }
+}
+
+// o[i] = c[B + S*i], i = 0..3, for the key and value centroid tables.
+template <int B, int S>
+__device__ inline void pick4(const float (&ck)[16], const float (&cv)[16], float (&ok)[4], float (&ov)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ok[i] = ck[B + S * i];
+    ov[i] = cv[B + S * i];
   }
 }
 
@@ -185,11 +205,12 @@ __device__ inline float half_mul(uint32_t packed, float f) {
 
 // One 16-token tile of the online softmax.  TAIL masks tokens at or past t1.
 template <bool TAIL>
-__device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], const uint8_t *tab, uint32_t slot8,
+__device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], const uint8_t *tab, uint32_t kslot,
+                                    uint32_t vslot,
                                     float sfac, int tb, int t1, int g, int n, float4_t (&dv)[kVDL], float &m_run,
                                     float &l_run) {
   float4_t dk = {0.f, 0.f, 0.f, 0.f};
-  key_scores(t.kw, bk, tab, slot8, dk);
+  key_scores(t.kw, bk, tab, kslot, dk);
 
   // lane (g, n): tokens 4g..4g+3, head n / 2 (both columns of a head end up
   // with the full score)
@@ -203,9 +224,11 @@ __device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], 
     s[i] = v;
     mt = fmaxf(mt, v);
   }
-  mt = max_rows(mt);
 
+  // The column maximum over the four lane rows is needed only when some
+  // lane's scores exceed the running maximum (then the rescale below runs).
   if (__builtin_amdgcn_ballot_w64(mt > m_run) != 0) {
+    mt = max_rows(mt);
     const float mn = fmaxf(m_run, mt);
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
     l_run *= alpha;
@@ -244,17 +267,15 @@ __device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], 
     av[i] = pack2(part, part);
   }
   const uint4_t a4 = {av[0], av[1], av[2], av[3]};
-  value_update(ev, od, tab, slot8, __builtin_bit_cast(half8_t, a4), dv);
+  value_update(ev, od, tab, vslot, __builtin_bit_cast(half8_t, a4), dv);
 }
 
 __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams P) {
   // pair tables during the loop, the waves' value rows afterwards
-  __shared__ __attribute__((aligned(16))) uint8_t tab[65536];
+  __shared__ __attribute__((aligned(16))) uint8_t tab[2 * 65536];
   __shared__ __attribute__((aligned(16))) uint32_t qtab[2 * kGMax][kRowPad];
   __shared__ float red_ml[kWaves][kGMax][2];
   __shared__ float qfac[kGMax];
-  __shared__ float cent[32];
-  __shared__ uint32_t sgnw[D / 4];
   __shared__ uint32_t next_tile[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -279,54 +300,84 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   const int t1f = t0 + ntiles * kTile;
   const uint32_t cap = (uint32_t)P.capacity;
   Sources src;
-  src.kc = make_rsrc(P.k_codes + (size_t)bh * cap * kRow, cap * kRow);
-  src.vc = make_rsrc(P.v_codes + (size_t)bh * cap * kRow, cap * kRow);
-  src.kn = make_rsrc(P.k_norms + (size_t)bh * cap, cap * 2);
-  src.vn = make_rsrc(P.v_norms + (size_t)bh * cap, cap * 2);
+  src.kc = P.k_codes + (size_t)bh * cap * kRow;
+  src.vc = P.v_codes + (size_t)bh * cap * kRow;
+  src.kn = P.k_norms + (size_t)bh * cap;
+  src.vn = P.v_norms + (size_t)bh * cap;
+  src.code_bytes = cap * kRow;
+  src.norm_bytes = cap * 2;
+  src.ko = n * kRow + g * 16;
+  src.vo = 4 * g * kRow + n * 4;
+  src.no = 4 * g * 2;
 
   // ---- set-up loads, then the first two tiles ----
-  // Every compute unit reads the same centroid and sign bytes, so one wave
-  // per work-group fetches them into LDS (one load instruction each) rather
-  // than every wave hitting the same cache lines; the query rows are read by
-  // the waves that rotate them.  The tile loads go out only after these have
-  // landed: issued together, the first tiles of the whole chip (two per
-  // wave, 4 KB each) queue ahead of the set-up loads in memory and hold the
-  // whole work-group at its first barrier.
+  // The centroids are read with uniform addresses, i.e. scalar loads: every
+  // wave of the chip reads the same 128 bytes, and the scalar cache serves
+  // them without queueing behind the vector tile loads.  The query rows and
+  // signs are read by the waves that rotate them.  The first two tiles of
+  // every wave are requested right behind, so HBM streams during the set-up.
   static_assert(kBlock == 1024, "pair-table fill assumes 1024 threads");
-  if (wave == 0) {
-    if (lane < 32) cent[lane] = (lane < 16) ? P.k_centroids[lane] : P.v_centroids[lane - 16];
-    else sgnw[lane - 32] = *reinterpret_cast<const uint32_t *>(P.signs + 4 * (lane - 32));
+  float ck[16], cv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ck[i] = P.k_centroids[i];
+    cv[i] = P.v_centroids[i];
   }
   const bool has_q = wave < G;
   uint32_t qh = 0u;
   float2 qf = {0.f, 0.f};
+  uint16_t sg = 0;
   if (has_q) {
     const size_t qoff = ((size_t)b * P.q_heads + hkv * G + wave) * D + lane * 2;
     if (P.q_f16) qh = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(P.q) + qoff);
     else qf = *reinterpret_cast<const float2 *>(static_cast<const float *>(P.q) + qoff);
+    sg = *reinterpret_cast<const uint16_t *>(P.signs + lane * 2);     // signs of coordinates 2l, 2l+1
   }
   if (tid < kWaves) next_tile[tid] = 2 * gw;
-  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
 
   int ia = gwave, ic = gwave + gw;                   // first tiles of this wave; later ones from its group's counter
   Tile ta, tc;
-  load_tile(ta, src, t0 + ia * kTile, ia >= ntiles, g, n);
+  load_tile(ta, src, t0 + ia * kTile, ia >= ntiles);
   __builtin_amdgcn_sched_barrier(0);
-  load_tile(tc, src, t0 + ic * kTile, ic >= ntiles, g, n);
+  load_tile(tc, src, t0 + ic * kTile, ic >= ntiles);
   __builtin_amdgcn_sched_barrier(0);
-  const uint16_t sg = (uint16_t)(sgnw[lane >> 1] >> (16 * (lane & 1)));   // signs of coordinates 2l, 2l+1
 
-  // ---- pair tables ----
-  // Table chunks (16 bytes, two slots) are written by consecutive lanes:
-  // thread t writes chunks t + 1024k, k = 0..3, i.e. rows (code bytes)
-  // t/16 + 64k, key table if t % 16 < 8 else value table.  The low nibble of
-  // those rows is (t/16) % 16 for every k, the high nibble t/256 + 4k.
+  // ---- pair tables: key table in the first 64 KB, value table in the next ----
+  // Row (code byte) r of a table holds 32 slots of the 8-byte entry
+  // (e(c[r % 16]), e(c[r / 16])).  Chunks of 16 bytes (two slots) are written
+  // by consecutive lanes: thread t writes chunks t + 1024k, k = 0..7, i.e.
+  // table k / 4, row t/16 + 64 (k % 4): low nibble (t/16) % 16 for every k,
+  // high nibble t/256 + 4 (k % 4).
   {
-    const int cbase = ((tid & 15) < 8) ? 0 : 16;
-    const uint32_t lo = split_entry(cent[cbase + ((tid >> 4) & 15)] * kCodeScale);
+    // (t/16) % 16 = 4 (wave % 4) + lane / 16 and t/256 = wave / 4: uniform
+    // parts chosen by a scalar switch (constant indices keep the tables in
+    // scalar registers), then one of four values by lane row
+    const int r4 = lane >> 4;
+    float lk[4], lv[4], hk[4], hv[4];
+    switch (wave & 3) {
+      case 0: pick4<0, 1>(ck, cv, lk, lv); break;
+      case 1: pick4<4, 1>(ck, cv, lk, lv); break;
+      case 2: pick4<8, 1>(ck, cv, lk, lv); break;
+      default: pick4<12, 1>(ck, cv, lk, lv); break;
+    }
+    switch (wave >> 2) {
+      case 0: pick4<0, 4>(ck, cv, hk, hv); break;
+      case 1: pick4<1, 4>(ck, cv, hk, hv); break;
+      case 2: pick4<2, 4>(ck, cv, hk, hv); break;
+      default: pick4<3, 4>(ck, cv, hk, hv); break;
+    }
+    float lo_k = lk[0], lo_v = lv[0];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t hi = split_entry(cent[cbase + (tid >> 8) + 4 * k] * kCodeScale);
+    for (int u = 1; u < 4; ++u) {
+      lo_k = (r4 == u) ? lk[u] : lo_k;
+      lo_v = (r4 == u) ? lv[u] : lo_v;
+    }
+    const uint32_t lok = split_entry(lo_k * kCodeScale), lov = split_entry(lo_v * kCodeScale);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t lo = (k < 4) ? lok : lov;
+      const uint32_t hi = split_entry(((k < 4) ? hk[k & 3] : hv[k & 3]) * kCodeScale);
       const uint4_t e = {lo, hi, lo, hi};
       *reinterpret_cast<uint4_t *>(tab + (tid + 1024 * k) * 16) = e;
     }
@@ -369,7 +420,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
 #pragma unroll
   for (int kb = 0; kb < D / 16; ++kb) bk[kb] = *reinterpret_cast<const uint4_t *>(&qtab[n][g * 32 + 4 * kb]);
   const float sfac = qfac[n >> 1];
-  const uint32_t slot8 = (uint32_t)n * 8;
+  const uint32_t kslot = (uint32_t)(lane & 31) * 8, vslot = kslot | 0x10000u;
 
   float4_t dv[kVDL];
 #pragma unroll
@@ -387,27 +438,27 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
     uint32_t nx = 0u;
     if (lane == 0) nx = atomicAdd(&next_tile[grp], 1u);
     __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-    process_tile<false>(ta, bk, tab, slot8, sfac, t0 + ia * kTile, t1, g, n, dv, m_run, l_run);
+    process_tile<false>(ta, bk, tab, kslot, vslot, sfac, t0 + ia * kTile, t1, g, n, dv, m_run, l_run);
     asm volatile("" : "+v"(nx));                     // keeps the read of the answer here
     const int na = __builtin_amdgcn_readfirstlane(nx);
-    load_tile(ta, src, t0 + na * kTile, na >= ntiles, g, n);
+    load_tile(ta, src, t0 + na * kTile, na >= ntiles);
     int nc = ntiles;
     if (ic < ntiles) {
       uint32_t ny = 0u;
       if (lane == 0) ny = atomicAdd(&next_tile[grp], 1u);
       __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-      process_tile<false>(tc, bk, tab, slot8, sfac, t0 + ic * kTile, t1, g, n, dv, m_run, l_run);
+      process_tile<false>(tc, bk, tab, kslot, vslot, sfac, t0 + ic * kTile, t1, g, n, dv, m_run, l_run);
       asm volatile("" : "+v"(ny));
       nc = __builtin_amdgcn_readfirstlane(ny);
     }
-    load_tile(tc, src, t0 + nc * kTile, nc >= ntiles, g, n);
+    load_tile(tc, src, t0 + nc * kTile, nc >= ntiles);
     ia = na;
     ic = nc;
   }
   // the last split's partial tile [t1f, t1)
   if (gwave == 0 && t1f < t1) {
-    load_tile(ta, src, t1f, false, g, n);
-    process_tile<true>(ta, bk, tab, slot8, sfac, t1f, t1, g, n, dv, m_run, l_run);
+    load_tile(ta, src, t1f, false);
+    process_tile<true>(ta, bk, tab, kslot, vslot, sfac, t1f, t1, g, n, dv, m_run, l_run);
   }
 
   // ---- wave epilogue: l per head over the 4 lane groups; per-head value rows to LDS ----
