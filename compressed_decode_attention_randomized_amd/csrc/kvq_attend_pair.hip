@@ -62,9 +62,14 @@ constexpr int kVDL = D / 16;                    // value coordinates per lane
 constexpr int kRowPad = D + 4;                  // query table row stride (words)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kCodeScale = 256.f;             // centroid scale: keeps the low fp16 half a normal number
+constexpr float kCodeScale = 256.f;
+// The softmax reference (log2 units) is moved only when a score passes it,
+// and then to the column maximum plus this slack: weights stay <= 1, the
+// largest at least 2^-kSlack, and most tiles skip the accumulator rescale.
+constexpr float kSlack = 4.f;             // centroid scale: keeps the low fp16 half a normal number
 constexpr int kRawBufferFlags = 0x00020000;     // 32-bit data format, untyped raw access
 constexpr uint32_t kNib = 0x0F0F0F0Fu;
+constexpr int kStream = 2;                      // cache policy nt: the cache is read once per step
 // s_waitcnt vmcnt(7) expcnt(7) lgkmcnt(15): the seven loads of one tile
 constexpr int kWaitOlderTile = 0x0F77;
 
@@ -72,6 +77,8 @@ struct PParams {
   const void *q;
   int q_f16;
   int kv_heads, q_heads, capacity, seq_len, num_splits;
+  int group_size;                  // query heads per KV head
+  int chunk;                       // tokens per split (a multiple of 32)
   int group_log2;                  // log2 of the splits one work-group covers (its wave groups)
   const uint8_t *k_codes, *v_codes;
   const uint16_t *k_norms, *v_norms;
@@ -144,11 +151,11 @@ __device__ inline void load_tile(Tile &t, const Sources &src, int tb, bool skip)
   const __amdgpu_buffer_rsrc_t kn = make_rsrc(src.kn, skip ? 0u : src.norm_bytes);
   const __amdgpu_buffer_rsrc_t vn = make_rsrc(src.vn, skip ? 0u : src.norm_bytes);
   const int cs = tb * kRow, ns = tb * 2;
-  t.kw = __builtin_amdgcn_raw_buffer_load_b128(kc, src.ko, cs, 0);
+  t.kw = __builtin_amdgcn_raw_buffer_load_b128(kc, src.ko, cs, kStream);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) t.vw[i] = __builtin_amdgcn_raw_buffer_load_b32(vc, src.vo + i * kRow, cs, 0);
-  t.kn = __builtin_amdgcn_raw_buffer_load_b64(kn, src.no, ns, 0);
-  t.vn = __builtin_amdgcn_raw_buffer_load_b64(vn, src.no, ns, 0);
+  for (int i = 0; i < 4; ++i) t.vw[i] = __builtin_amdgcn_raw_buffer_load_b32(vc, src.vo + i * kRow, cs, kStream);
+  t.kn = __builtin_amdgcn_raw_buffer_load_b64(kn, src.no, ns, kStream);
+  t.vn = __builtin_amdgcn_raw_buffer_load_b64(vn, src.no, ns, kStream);
 }
 
 // Key block kb: coordinates 4kb..4kb+3 of the lane's slice = bytes 2kb, 2kb+1.
@@ -208,7 +215,7 @@ template <bool TAIL>
 __device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], const uint8_t *tab, uint32_t kslot,
                                     uint32_t vslot,
                                     float sfac, int tb, int t1, int g, int n, float4_t (&dv)[kVDL], float &m_run,
-                                    float &l_run) {
+                                    float &l_run, float &m_top) {
   float4_t dk = {0.f, 0.f, 0.f, 0.f};
   key_scores(t.kw, bk, tab, kslot, dk);
 
@@ -227,9 +234,10 @@ __device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], 
 
   // The column maximum over the four lane rows is needed only when some
   // lane's scores exceed the running maximum (then the rescale below runs).
+  m_top = fmaxf(m_top, mt);
   if (__builtin_amdgcn_ballot_w64(mt > m_run) != 0) {
     mt = max_rows(mt);
-    const float mn = fmaxf(m_run, mt);
+    const float mn = (mt > m_run) ? mt + kSlack : m_run;
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
     l_run *= alpha;
     m_run = mn;
@@ -270,31 +278,48 @@ __device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], 
   value_update(ev, od, tab, vslot, __builtin_bit_cast(half8_t, a4), dv);
 }
 
+// Weighted sum over the GW waves w0.. of a group of value row (head h,
+// coordinate j); the rows sit in LDS as [wave][g][part][n][4] with head
+// h = 2g + hp and coordinate j = 8n + c in part 2hp + c / 4, float c % 4.
+template <int GW>
+__device__ inline float merge_rows(const float *red_acc, const float (*wfac)[kGMax], int w0, int h, int j) {
+  const int in_wave = (((h >> 1) * 4 + 2 * (h & 1) + ((j >> 2) & 1)) * 16 + (j >> 3)) * 4 + (j & 3);
+  float o = 0.f;
+#pragma unroll
+  for (int w = 0; w < GW; ++w) o += red_acc[(w0 + w) * (4 * 4 * 16 * 4) + in_wave] * wfac[w0 + w][h];
+  return o;
+}
+
 __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams P) {
   // pair tables during the loop, the waves' value rows afterwards
   __shared__ __attribute__((aligned(16))) uint8_t tab[2 * 65536];
   __shared__ __attribute__((aligned(16))) uint32_t qtab[2 * kGMax][kRowPad];
-  __shared__ float red_ml[kWaves][kGMax][2];
+  __shared__ float red_ml[kWaves][kGMax][3];      // (reference, sum, largest score) per wave and head
+  __shared__ float wfac[kWaves][kGMax];
   __shared__ float qfac[kGMax];
   __shared__ uint32_t next_tile[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n = lane & 15;
-  const int G = P.q_heads / P.kv_heads;
-  const int bh = blockIdx.y;
-  const int b = bh / P.kv_heads, hkv = bh - b * P.kv_heads;
+  // Index arithmetic is kept free of divisions: at kernel start every wave
+  // of a SIMD runs it on the one scalar issue slot the SIMD gets per cycle
+  // group, ahead of its first loads.
+  const int G = P.group_size;
+  const int hkv = blockIdx.y, b = blockIdx.z;
+  const int bh = b * P.kv_heads + hkv;
   // the work-group covers 2^group_log2 consecutive splits of one (b, KV head),
   // each with its own group of gw waves (all share the query and the tables)
-  const int gw = kWaves >> P.group_log2;
-  const int grp = wave / gw, gwave = wave - grp * gw;
-  const int split = (blockIdx.x << P.group_log2) + grp;
+  const int lg = P.group_log2;
+  const int gw = kWaves >> lg;
+  const int grp = wave >> (4 - lg), gwave = wave & (gw - 1);
+  const int split = (blockIdx.x << lg) + grp;
 
-  // chunks of ceil(T/S) tokens rounded up to a multiple of 32; full tiles
-  // [t0, t1f) go through the main loop, a partial last tile (only the last
-  // split can have one) after it; splits past S (a partly used last group)
-  // get no tokens and write nothing
-  const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + kChunkTok - 1) / kChunkTok * kChunkTok;
+  // chunks of ceil(T/S) tokens rounded up to a multiple of 32 (from the
+  // host); full tiles [t0, t1f) go through the main loop, a partial last
+  // tile (only the last split can have one) after it; splits past S (a
+  // partly used last group) get no tokens and write nothing
+  const int chunk = P.chunk;
   const int t0 = min(P.seq_len, split * chunk), t1 = min(P.seq_len, t0 + chunk);
   const int ntiles = (t1 - t0) / kTile;
   const int t1f = t0 + ntiles * kTile;
@@ -310,37 +335,47 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   src.vo = 4 * g * kRow + n * 4;
   src.no = 4 * g * 2;
 
-  // ---- set-up loads, then the first two tiles ----
-  // The centroids are read with uniform addresses, i.e. scalar loads: every
-  // wave of the chip reads the same 128 bytes, and the scalar cache serves
-  // them without queueing behind the vector tile loads.  The query rows and
-  // signs are read by the waves that rotate them.  The first two tiles of
-  // every wave are requested right behind, so HBM streams during the set-up.
+  // ---- set-up loads and the first tile ----
+  // Scalar-memory results return out of order, so a wait for one scalar
+  // load is a wait for all of them, and every scalar value the set-up needs
+  // from the kernel arguments is read before the centroid loads go out.
+  // The centroids are read with uniform addresses, i.e. scalar loads the
+  // scalar cache serves to every wave of the chip; they go out first, ahead
+  // of the flood of tile requests, and are first waited for by the table
+  // fill.  The query rows and signs (read by the waves that rotate them,
+  // through zero-size descriptors elsewhere, so no branch) go out before the
+  // first tile so that the rotation's in-order wait for them does not wait
+  // for tile data.  The second tile follows the set-up.
   static_assert(kBlock == 1024, "pair-table fill assumes 1024 threads");
+  const bool has_q = wave < G;
+  const int q_f16 = P.q_f16;
+  const uint32_t q_es = q_f16 ? 2u : 4u;
+  const size_t q_row0 = ((size_t)b * P.q_heads + (size_t)hkv * G) * D;
+  const uintptr_t q_base = reinterpret_cast<uintptr_t>(P.q) + q_row0 * q_es;
+  const uintptr_t s_base = reinterpret_cast<uintptr_t>(P.signs);
+
   float ck[16], cv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     ck[i] = P.k_centroids[i];
     cv[i] = P.v_centroids[i];
   }
-  const bool has_q = wave < G;
-  uint32_t qh = 0u;
-  float2 qf = {0.f, 0.f};
-  uint16_t sg = 0;
-  if (has_q) {
-    const size_t qoff = ((size_t)b * P.q_heads + hkv * G + wave) * D + lane * 2;
-    if (P.q_f16) qh = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(P.q) + qoff);
-    else qf = *reinterpret_cast<const float2 *>(static_cast<const float *>(P.q) + qoff);
-    sg = *reinterpret_cast<const uint16_t *>(P.signs + lane * 2);     // signs of coordinates 2l, 2l+1
-  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(reinterpret_cast<const void *>(q_base), has_q ? (uint32_t)(G * D) * q_es : 0u);
+  const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(reinterpret_cast<const void *>(s_base), has_q ? (uint32_t)D : 0u);
+  const uint32_t q_off = (uint32_t)(wave * D + lane * 2) * q_es;
+  // coordinates 2l, 2l+1: both halves of q0 (fp16) or q0 and q1 (fp32);
+  // for fp16 queries q1 is unused (past the last row it reads as zero)
+  const uint32_t q0 = __builtin_amdgcn_raw_buffer_load_b32(qsrc, q_off, 0, 0);
+  const uint32_t q1 = __builtin_amdgcn_raw_buffer_load_b32(qsrc, q_off + 4u, 0, 0);
+  const uint32_t sg = __builtin_amdgcn_raw_buffer_load_b16(ssrc, lane * 2, 0, 0);   // signs of coordinates 2l, 2l+1
   if (tid < kWaves) next_tile[tid] = 2 * gw;
   __builtin_amdgcn_sched_barrier(0);
 
   int ia = gwave, ic = gwave + gw;                   // first tiles of this wave; later ones from its group's counter
   Tile ta, tc;
   load_tile(ta, src, t0 + ia * kTile, ia >= ntiles);
-  __builtin_amdgcn_sched_barrier(0);
-  load_tile(tc, src, t0 + ic * kTile, ic >= ntiles);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- pair tables: key table in the first 64 KB, value table in the next ----
@@ -392,8 +427,8 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
     uint2_t f0 = {0u, 0u}, f1 = {0u, 0u};
     float fac = 0.f;
     if (has_q) {
-      float z0 = P.q_f16 ? half_value(qh & 0xFFFFu) : qf.x;
-      float z1 = P.q_f16 ? half_value(qh >> 16) : qf.y;
+      float z0 = q_f16 ? half_value(q0 & 0xFFFFu) : __builtin_bit_cast(float, q0);
+      float z1 = q_f16 ? half_value(q0 >> 16) : __builtin_bit_cast(float, q1);
       z0 = (sg & 0x80u) ? -z0 : z0;
       z1 = (sg & 0x8000u) ? -z1 : z1;
       float a = z0 + z1, c = z0 - z1;
@@ -412,6 +447,9 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
     *reinterpret_cast<uint2_t *>(&qtab[2 * wave + 1][lane * 2]) = f1;
     if (lane == 0) qfac[wave] = fac;
   }
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(tc, src, t0 + ic * kTile, ic >= ntiles);
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
   // B operand of key block kb for column n: query table row n (head n / 2,
@@ -425,7 +463,8 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   float4_t dv[kVDL];
 #pragma unroll
   for (int dt = 0; dt < kVDL; ++dt) dv[dt] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;             // softmax reference and sum for this lane's column
+  float m_top = -INFINITY;                           // largest score of this lane's rows
 
   // Tiles alternate between the two tile buffers; each buffer is refilled
   // with a newly claimed tile right after use (ia < ic always holds, so once
@@ -438,7 +477,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
     uint32_t nx = 0u;
     if (lane == 0) nx = atomicAdd(&next_tile[grp], 1u);
     __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-    process_tile<false>(ta, bk, tab, kslot, vslot, sfac, t0 + ia * kTile, t1, g, n, dv, m_run, l_run);
+    process_tile<false>(ta, bk, tab, kslot, vslot, sfac, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
     asm volatile("" : "+v"(nx));                     // keeps the read of the answer here
     const int na = __builtin_amdgcn_readfirstlane(nx);
     load_tile(ta, src, t0 + na * kTile, na >= ntiles);
@@ -447,7 +486,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
       uint32_t ny = 0u;
       if (lane == 0) ny = atomicAdd(&next_tile[grp], 1u);
       __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-      process_tile<false>(tc, bk, tab, kslot, vslot, sfac, t0 + ic * kTile, t1, g, n, dv, m_run, l_run);
+      process_tile<false>(tc, bk, tab, kslot, vslot, sfac, t0 + ic * kTile, t1, g, n, dv, m_run, l_run, m_top);
       asm volatile("" : "+v"(ny));
       nc = __builtin_amdgcn_readfirstlane(ny);
     }
@@ -458,65 +497,90 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   // the last split's partial tile [t1f, t1)
   if (gwave == 0 && t1f < t1) {
     load_tile(ta, src, t1f, false);
-    process_tile<true>(ta, bk, tab, kslot, vslot, sfac, t1f, t1, g, n, dv, m_run, l_run);
+    process_tile<true>(ta, bk, tab, kslot, vslot, sfac, t1f, t1, g, n, dv, m_run, l_run, m_top);
   }
 
-  // ---- wave epilogue: l per head over the 4 lane groups; per-head value rows to LDS ----
+  // ---- wave epilogue: (m, l) per head to LDS; after the barrier (the
+  // tables are dead then) the value rows of the heads in use ----
   l_run = sum_rows(l_run);
+  m_top = max_rows(m_top);
+  if (lane < 2 * kGMax && !(lane & 1)) {            // lane 2h of the first row: head h
+    red_ml[wave][lane >> 1][0] = m_run;
+    red_ml[wave][lane >> 1][1] = l_run;
+    red_ml[wave][lane >> 1][2] = m_top;
+  }
   __syncthreads();                                   // every wave is done with the tables
   float *red_acc = reinterpret_cast<float *>(tab);   // per wave: 8 heads x D floats
   {
-    float4_t h0[2], h1[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      h0[q] = (float4_t){dv[4 * q][0] + dv[4 * q][1], dv[4 * q + 1][0] + dv[4 * q + 1][1],
-                         dv[4 * q + 2][0] + dv[4 * q + 2][1], dv[4 * q + 3][0] + dv[4 * q + 3][1]};
-      h1[q] = (float4_t){dv[4 * q][2] + dv[4 * q][3], dv[4 * q + 1][2] + dv[4 * q + 1][3],
-                         dv[4 * q + 2][2] + dv[4 * q + 2][3], dv[4 * q + 3][2] + dv[4 * q + 3][3]};
-    }
     // layout [wave][g][part][n][4]: part = 2 * (head - 2g) + half, so each
     // 16-lane row of a write covers 256 contiguous bytes
     float *r = red_acc + ((size_t)(wave * 4 + g) * 4 * 16 + n) * 4;
-    *reinterpret_cast<float4_t *>(r) = h0[0];
-    *reinterpret_cast<float4_t *>(r + 64) = h0[1];
-    *reinterpret_cast<float4_t *>(r + 128) = h1[0];
-    *reinterpret_cast<float4_t *>(r + 192) = h1[1];
+    if (2 * g < G) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        *reinterpret_cast<float4_t *>(r + 64 * q) =
+            (float4_t){dv[4 * q][0] + dv[4 * q][1], dv[4 * q + 1][0] + dv[4 * q + 1][1],
+                       dv[4 * q + 2][0] + dv[4 * q + 2][1], dv[4 * q + 3][0] + dv[4 * q + 3][1]};
+    }
+    if (2 * g + 1 < G) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        *reinterpret_cast<float4_t *>(r + 128 + 64 * q) =
+            (float4_t){dv[4 * q][2] + dv[4 * q][3], dv[4 * q + 1][2] + dv[4 * q + 1][3],
+                       dv[4 * q + 2][2] + dv[4 * q + 2][3], dv[4 * q + 3][2] + dv[4 * q + 3][3]};
+    }
   }
-  if (lane < 2 * kGMax && !(lane & 1)) {
-    red_ml[wave][lane >> 1][0] = m_run;
-    red_ml[wave][lane >> 1][1] = l_run;
+  // Weight of each wave's rows in its group's merge, one lane per (head h,
+  // wave w) in waves 0-1 (h = tid / 16, w = tid % 16): a group's waves are
+  // gw consecutive lanes of a 16-lane row, reduced with DPP exchanges.  The
+  // weight exp2(m_w - M) / (L * code scale) folds in the softmax
+  // denominator, so the per-coordinate pass below is a plain weighted sum.
+  if (tid < kWaves * kGMax) {
+    const int h = tid >> 4, w = tid & (kWaves - 1);
+    const float m = red_ml[w][h][0], l = red_ml[w][h][1], mt = red_ml[w][h][2];
+    float M = fmaxf(m, xor_lane<1>(m, lane));       // gw >= 2
+    if (gw > 2) M = fmaxf(M, xor_lane<2>(M, lane));
+    if (gw > 4) M = fmaxf(M, xor_lane<4>(M, lane));
+    if (gw > 8) M = fmaxf(M, xor_lane<8>(M, lane));
+    const float f = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    float L = l * f;
+    L += xor_lane<1>(L, lane);
+    if (gw > 2) L += xor_lane<2>(L, lane);
+    if (gw > 4) L += xor_lane<4>(L, lane);
+    if (gw > 8) L += xor_lane<8>(L, lane);
+    wfac[w][h] = (L > 0.f) ? f / (L * kCodeScale) : 0.f;
+    // the split's state is reported against its largest score
+    float Mt = fmaxf(mt, xor_lane<1>(mt, lane));
+    if (gw > 2) Mt = fmaxf(Mt, xor_lane<2>(Mt, lane));
+    if (gw > 4) Mt = fmaxf(Mt, xor_lane<4>(Mt, lane));
+    if (gw > 8) Mt = fmaxf(Mt, xor_lane<8>(Mt, lane));
+    const int sp = (blockIdx.x << lg) + (w >> (4 - lg));
+    if ((w & (gw - 1)) == 0 && h < G && sp < P.num_splits) {
+      const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * P.num_splits + sp;
+      const bool any = L > 0.f;
+      P.part_ml[row * 2 + 0] = any ? Mt * kLn2 : -INFINITY;
+      P.part_ml[row * 2 + 1] = any ? L * exp2f(M - Mt) : 0.f;
+    }
   }
   __syncthreads();
 
   // ---- merge each group's waves: one thread per (group, head, coordinate);
-  // a wave's lanes share (group, head), so the state reads are broadcasts
+  // a wave's lanes share (group, head), so the weight reads are broadcasts
   // and the value reads are consecutive ----
-  const int ngroups = 1 << P.group_log2;
-  for (int i = tid; i < ngroups * G * D; i += kBlock) {
-    const int gi = i / (G * D);
-    const int r = i - gi * (G * D);
-    const int h = r / D, j = r - h * D;
-    const int sp = (blockIdx.x << P.group_log2) + gi;
-    if (sp >= P.num_splits) continue;
-    const int w0 = gi * gw;
-    float M = -INFINITY;
-#pragma unroll 4
-    for (int w = 0; w < gw; ++w) M = fmaxf(M, red_ml[w0 + w][h][0]);
-    float l = 0.f, o = 0.f;
-#pragma unroll 4
-    for (int w = 0; w < gw; ++w) {
-      const float mw = red_ml[w0 + w][h][0];
-      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-      l += red_ml[w0 + w][h][1] * f;
-      // head h = 2g + hp, coordinate j = 8n + c: part 2hp + c/4, float c % 4
-      o += red_acc[(((size_t)((w0 + w) * 4 + (h >> 1)) * 4 + 2 * (h & 1) + ((j >> 2) & 1)) * 16 + (j >> 3)) * 4 + (j & 3)] * f;
+  static_assert(kGMax * D <= kBlock, "one thread per (head, coordinate)");
+  for (int gi = 0; gi < (1 << lg) && tid < G * D; ++gi) {
+    const int h = tid >> 7, j = tid & (D - 1);
+    const int sp = (blockIdx.x << lg) + gi;
+    if (sp >= P.num_splits) break;
+    float o;
+    switch (lg) {
+      case 0: o = merge_rows<16>(red_acc, wfac, 0, h, j); break;
+      case 1: o = merge_rows<8>(red_acc, wfac, gi * 8, h, j); break;
+      case 2: o = merge_rows<4>(red_acc, wfac, gi * 4, h, j); break;
+      default: o = merge_rows<2>(red_acc, wfac, gi * 2, h, j); break;
     }
     const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * P.num_splits + sp;
-    P.part_o[row * D + j] = (l > 0.f) ? o / (l * kCodeScale) : 0.f;
-    if (j == 0) {
-      P.part_ml[row * 2 + 0] = (M == -INFINITY) ? -INFINITY : M * kLn2;
-      P.part_ml[row * 2 + 1] = l;
-    }
+    P.part_o[row * D + j] = o;
   }
 }
 
@@ -539,9 +603,10 @@ hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream) {
   const int64_t pairs = (int64_t)a.batch * a.kv_heads;
   int lg = 0;
   while (lg < 3 && pairs * ((a.num_splits + (1 << lg) - 1) >> lg) > (int64_t)cus) ++lg;
-  PParams P{a.q, a.q_f16, a.kv_heads, a.q_heads, a.capacity, a.seq_len, a.num_splits, lg, a.k_codes, a.v_codes,
-            a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids, a.part_o, a.part_ml};
-  dim3 grid((a.num_splits + (1 << lg) - 1) >> lg, a.batch * a.kv_heads);
+  const int chunk = ((a.seq_len + a.num_splits - 1) / a.num_splits + kChunkTok - 1) / kChunkTok * kChunkTok;
+  PParams P{a.q, a.q_f16, a.kv_heads, a.q_heads, a.capacity, a.seq_len, a.num_splits, a.q_heads / a.kv_heads, chunk, lg,
+            a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids, a.part_o, a.part_ml};
+  dim3 grid((a.num_splits + (1 << lg) - 1) >> lg, a.kv_heads, a.batch);
   hipLaunchKernelGGL(attend_pair_kernel, grid, dim3(kBlock), 0, stream, P);
   return hipGetLastError();
 }
