@@ -106,16 +106,11 @@ __device__ inline void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t
   }
 }
 
-// (byte K of v) * 4 in one VALU op: SDWA selects the byte as the shifted
-// operand.  Turns a byte holding one code into an LDS table offset.
+// (byte K of v) * 4: turns a byte holding one code into an LDS table
+// offset (the compiler selects a byte-select shift where it can).
 template <int K>
 __device__ inline uint32_t byte_x4(uint32_t v) {
-  uint32_t r;
-  if constexpr (K == 0) asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(v));
-  if constexpr (K == 1) asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(v));
-  if constexpr (K == 2) asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(v));
-  if constexpr (K == 3) asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(v));
-  return r;
+  return ((v >> (8 * K)) & 0xFFu) << 2;
 }
 
 // The codes of one 32-bit word split into byte planes: plane k holds codes
@@ -147,11 +142,19 @@ __device__ inline float row_swap8(float x) {
 // row swaps (VALU, no LDS): after v_permlane16_swap on two copies of x, each
 // lane holds its own value in one copy and its xor-16 partner's in the other;
 // v_permlane32_swap does the same for xor 32.
+// (Compiler builtins, so that the compiler pads their hazards, matrix-core
+// operands included.)
 __device__ inline void swap16(float &a, float &b) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b), false, false);
+  const unsigned r0 = r[0], r1 = r[1];   // (copied out first: a bit cast of r[1] itself reads element 0)
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
 }
 __device__ inline void swap32(float &a, float &b) {
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b), false, false);
+  const unsigned r0 = r[0], r1 = r[1];   // (copied out first: a bit cast of r[1] itself reads element 0)
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
 }
 __device__ inline float max_rows(float x) {
   float a = x, b = x;

@@ -46,6 +46,7 @@ namespace kvq {
 namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
@@ -126,6 +127,16 @@ __device__ inline float lane_swap1(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
 }
 
+__device__ inline uint32_t swap1_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+}
+
+// x + (x of lane l ^ 1); written as a DPP update with a zero old value so
+// that the exchange folds into the add (one v_add_f32_dpp).
+__device__ inline float add_swap1(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+}
+
 struct Tile {
   uint4_t kw;          // key bytes: token n, coordinates [32g, 32g+32)
   uint32_t vw[4];      // value bytes: tokens 4g+i, coordinates [8n, 8n+8)
@@ -197,46 +208,57 @@ __device__ inline void pick4(const float (&ck)[16], const float (&cv)[16], float
   }
 }
 
-// f16(half H of a packed pair) * f in one v_fma_mix (the product of an fp16
-// and an fp32 value, rounded once to fp32: equal to a conversion then a
-// multiply).
+// f16(half H of a packed pair) * f: one v_fma_mix_f32 (the fma with a zero
+// addend of a converted fp16 and an fp32 value, rounded once to fp32:
+// equal to a conversion then a multiply).
 template <int H>
 __device__ inline float half_mul(uint32_t packed, float f) {
-  float r;
-  if constexpr (H == 0)
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(packed), "v"(f));
-  else
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(packed), "v"(f));
-  return r;
+  return __builtin_fmaf(half_value(packed >> (16 * H)), f, 0.f);
+}
+
+// hp = (RN(w0), RN(w1)) and lp = (RN(w0 - hi0), RN(w1 - hi1)) as fp16
+// pairs.  m1 holds -1 where the compiler cannot fold it, so the low parts
+// stay fused multiply-adds of an fp16 and two fp32 operands (v_fma_mix).
+__device__ inline void split_pair(float w0, float w1, float m1, uint32_t &hp, uint32_t &lp) {
+  const half2_t h = {(_Float16)w0, (_Float16)w1};
+  const half2_t l = {(_Float16)__builtin_fmaf((float)h.x, m1, w0), (_Float16)__builtin_fmaf((float)h.y, m1, w1)};
+  hp = __builtin_bit_cast(uint32_t, h);
+  lp = __builtin_bit_cast(uint32_t, l);
 }
 
 // One 16-token tile of the online softmax.  TAIL masks tokens at or past t1.
+//
+// Columns 2h and 2h+1 of the score tile hold the two parts of head h's
+// scores, so lanes 2h and 2h+1 of a lane row share the work of their four
+// tokens: lane 2h finishes tokens 4g, 4g+1 and lane 2h+1 tokens 4g+2, 4g+3
+// (one exponential per score), then they trade weight halves: A row 2h takes
+// the high fp16 parts of all four weights, row 2h+1 the low parts.  Both
+// lanes of a head keep the same softmax reference.
 template <bool TAIL>
 __device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], const uint8_t *tab, uint32_t kslot,
-                                    uint32_t vslot,
-                                    float sfac, int tb, int t1, int g, int n, float4_t (&dv)[kVDL], float &m_run,
-                                    float &l_run, float &m_top) {
+                                    uint32_t vslot, float sfac, float m1, int tb, int t1, int g, int n,
+                                    float4_t (&dv)[kVDL], float &m_run, float &l_run, float &m_top) {
   float4_t dk = {0.f, 0.f, 0.f, 0.f};
   key_scores(t.kw, bk, tab, kslot, dk);
 
-  // lane (g, n): tokens 4g..4g+3, head n / 2 (both columns of a head end up
-  // with the full score)
-  float s[4];
-  float mt = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float nks = (i & 1) ? half_mul<1>(t.kn[i >> 1], sfac) : half_mul<0>(t.kn[i >> 1], sfac);
-    float v = (dk[i] + lane_swap1(dk[i])) * nks;
-    if constexpr (TAIL) v = (tb + 4 * g + i < t1) ? v : -INFINITY;
-    s[i] = v;
-    mt = fmaxf(mt, v);
+  const bool odd = n & 1;
+  const uint32_t knp = odd ? t.kn.y : t.kn.x;        // fp16 norms of this lane's two tokens
+  const uint32_t vnp = odd ? t.vn.y : t.vn.x;
+  const float f0 = add_swap1(dk[0]), f1 = add_swap1(dk[1]), f2 = add_swap1(dk[2]), f3 = add_swap1(dk[3]);
+  float s[2] = {(odd ? f2 : f0) * half_mul<0>(knp, sfac), (odd ? f3 : f1) * half_mul<1>(knp, sfac)};
+  if constexpr (TAIL) {
+    const int tok = tb + 4 * g + 2 * (int)odd;
+    s[0] = (tok < t1) ? s[0] : -INFINITY;
+    s[1] = (tok + 1 < t1) ? s[1] : -INFINITY;
   }
+  float mt = fmaxf(s[0], s[1]);
 
   // The column maximum over the four lane rows is needed only when some
-  // lane's scores exceed the running maximum (then the rescale below runs).
-  m_top = fmaxf(m_top, mt);
+  // lane's scores pass the reference (then the rescale below runs).
+  m_top = (mt > m_top) ? mt : m_top;
   if (__builtin_amdgcn_ballot_w64(mt > m_run) != 0) {
     mt = max_rows(mt);
+    mt = fmaxf(mt, lane_swap1(mt));
     const float mn = (mt > m_run) ? mt + kSlack : m_run;
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
     l_run *= alpha;
@@ -261,20 +283,25 @@ __device__ inline void process_tile(const Tile &t, const uint4_t (&bk)[D / 16], 
     od[p] = ((t.vw[2 * p] >> 4) & kNib) | (t.vw[2 * p + 1] & ~kNib);
   }
 
-  uint32_t av[4];
+  // weights w = exp2(s - m) * norm of the lane's two tokens, split as
+  // w = hi + lo (fp16 each, about 22 bits together) into the packed pairs
+  // hp = (hi0, hi1) and lp = (lo0, lo1)
+  float w[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float p = __builtin_amdgcn_exp2f(s[i] - m_run);
-    if constexpr (TAIL) p = (s[i] == -INFINITY) ? 0.f : p;
+  for (int u = 0; u < 2; ++u) {
+    float p = __builtin_amdgcn_exp2f(s[u] - m_run);
+    if constexpr (TAIL) p = (s[u] == -INFINITY) ? 0.f : p;
     l_run += p;
-    const float nv = half_value((t.vn[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-    float w = p * nv;
-    if constexpr (TAIL) w = (p > 0.f) ? w : 0.f;
-    const _Float16 hi = (_Float16)w;
-    const _Float16 part = (n & 1) ? (_Float16)(w - (float)hi) : hi;
-    av[i] = pack2(part, part);
+    w[u] = u ? half_mul<1>(vnp, p) : half_mul<0>(vnp, p);
   }
-  const uint4_t a4 = {av[0], av[1], av[2], av[3]};
+  uint32_t hp, lp;
+  split_pair(w[0], w[1], m1, hp, lp);
+  // lane 2h gets the partner's high parts, lane 2h+1 the partner's low parts
+  const uint32_t got = swap1_u32(odd ? hp : lp);
+  const uint32_t first = odd ? got : hp, second = odd ? lp : got;      // tokens 4g, 4g+1 | 4g+2, 4g+3
+  const uint4_t a4 = {__builtin_amdgcn_perm(first, first, 0x01000100u), __builtin_amdgcn_perm(first, first, 0x03020302u),
+                      __builtin_amdgcn_perm(second, second, 0x01000100u),
+                      __builtin_amdgcn_perm(second, second, 0x03020302u)};
   value_update(ev, od, tab, vslot, __builtin_bit_cast(half8_t, a4), dv);
 }
 
@@ -459,6 +486,8 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   for (int kb = 0; kb < D / 16; ++kb) bk[kb] = *reinterpret_cast<const uint4_t *>(&qtab[n][g * 32 + 4 * kb]);
   const float sfac = qfac[n >> 1];
   const uint32_t kslot = (uint32_t)(lane & 31) * 8, vslot = kslot | 0x10000u;
+  float m1 = -1.f;
+  asm volatile("" : "+s"(m1));                       // no instruction: keeps -1 from being folded
 
   float4_t dv[kVDL];
 #pragma unroll
@@ -477,7 +506,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
     uint32_t nx = 0u;
     if (lane == 0) nx = atomicAdd(&next_tile[grp], 1u);
     __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-    process_tile<false>(ta, bk, tab, kslot, vslot, sfac, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
+    process_tile<false>(ta, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
     asm volatile("" : "+v"(nx));                     // keeps the read of the answer here
     const int na = __builtin_amdgcn_readfirstlane(nx);
     load_tile(ta, src, t0 + na * kTile, na >= ntiles);
@@ -486,7 +515,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
       uint32_t ny = 0u;
       if (lane == 0) ny = atomicAdd(&next_tile[grp], 1u);
       __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-      process_tile<false>(tc, bk, tab, kslot, vslot, sfac, t0 + ic * kTile, t1, g, n, dv, m_run, l_run, m_top);
+      process_tile<false>(tc, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run, l_run, m_top);
       asm volatile("" : "+v"(ny));
       nc = __builtin_amdgcn_readfirstlane(ny);
     }
@@ -497,13 +526,13 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   // the last split's partial tile [t1f, t1)
   if (gwave == 0 && t1f < t1) {
     load_tile(ta, src, t1f, false);
-    process_tile<true>(ta, bk, tab, kslot, vslot, sfac, t1f, t1, g, n, dv, m_run, l_run, m_top);
+    process_tile<true>(ta, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
   }
 
   // ---- wave epilogue: (m, l) per head to LDS; after the barrier (the
   // tables are dead then) the value rows of the heads in use ----
-  l_run = sum_rows(l_run);
-  m_top = max_rows(m_top);
+  l_run = sum_rows(add_swap1(l_run));                // both lanes of a head, all four lane rows
+  m_top = max_rows(fmaxf(m_top, lane_swap1(m_top)));
   if (lane < 2 * kGMax && !(lane & 1)) {            // lane 2h of the first row: head h
     red_ml[wave][lane >> 1][0] = m_run;
     red_ml[wave][lane >> 1][1] = l_run;

@@ -11,12 +11,19 @@ namespace kvq {
 // After v_permlane16_swap on two copies of a value, lanes of even rows find
 // the value of their xor-16 partner in the second copy and lanes of odd rows
 // in the first; v_permlane32_swap does the same for the two wave halves.
-// Two distinct registers per swap; the s_nop pairs cover the VALU hazards.
+// Compiler builtins, so that the compiler sees the instructions and pads
+// their hazards (with matrix-core operands too).
 __device__ inline void swap16(float &a, float &b) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b), false, false);
+  const unsigned r0 = r[0], r1 = r[1];   // (copied out first: a bit cast of r[1] itself reads element 0)
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
 }
 __device__ inline void swap32(float &a, float &b) {
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b), false, false);
+  const unsigned r0 = r[0], r1 = r[1];   // (copied out first: a bit cast of r[1] itself reads element 0)
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
 }
 
 // Max / sum over the four 16-lane rows (lanes l, l^16, l^32, l^48).
