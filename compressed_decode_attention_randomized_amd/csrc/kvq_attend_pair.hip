@@ -73,6 +73,8 @@ constexpr uint32_t kNib = 0x0F0F0F0Fu;
 constexpr int kStream = 2;                      // cache policy nt: the cache is read once per step
 // s_waitcnt vmcnt(7) expcnt(7) lgkmcnt(15): the seven loads of one tile
 constexpr int kWaitOlderTile = 0x0F77;
+constexpr int kSetupWaves = 8;                  // waves that build the tables and the rotated query
+constexpr int kSpinLimit = 1 << 20;             // bound of the set-up wait (s_sleep 1 each)
 
 struct PParams {
   const void *q;
@@ -198,11 +200,11 @@ __device__ inline void value_update(const uint32_t (&ev)[2], const uint32_t (&od
   }
 }
 
-// o[i] = c[B + S*i], i = 0..3, for the key and value centroid tables.
-template <int B, int S>
-__device__ inline void pick4(const float (&ck)[16], const float (&cv)[16], float (&ok)[4], float (&ov)[4]) {
+// o[i] = c[B + S*i] for the key and value centroid tables.
+template <int B, int S, int N>
+__device__ inline void pick(const float (&ck)[16], const float (&cv)[16], float (&ok)[N], float (&ov)[N]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < N; ++i) {
     ok[i] = ck[B + S * i];
     ov[i] = cv[B + S * i];
   }
@@ -325,6 +327,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   __shared__ float wfac[kWaves][kGMax];
   __shared__ float qfac[kGMax];
   __shared__ uint32_t next_tile[kWaves];
+  __shared__ uint32_t ready;                         // set-up waves done
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -362,95 +365,88 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   src.vo = 4 * g * kRow + n * 4;
   src.no = 4 * g * 2;
 
-  // ---- set-up loads and the first tile ----
-  // Scalar-memory results return out of order, so a wait for one scalar
-  // load is a wait for all of them, and every scalar value the set-up needs
-  // from the kernel arguments is read before the centroid loads go out.
-  // The centroids are read with uniform addresses, i.e. scalar loads the
-  // scalar cache serves to every wave of the chip; they go out first, ahead
-  // of the flood of tile requests, and are first waited for by the table
-  // fill.  The query rows and signs (read by the waves that rotate them,
-  // through zero-size descriptors elsewhere, so no branch) go out before the
-  // first tile so that the rotation's in-order wait for them does not wait
-  // for tile data.  The second tile follows the set-up.
-  static_assert(kBlock == 1024, "pair-table fill assumes 1024 threads");
-  const bool has_q = wave < G;
-  const int q_f16 = P.q_f16;
-  const uint32_t q_es = q_f16 ? 2u : 4u;
-  const size_t q_row0 = ((size_t)b * P.q_heads + (size_t)hkv * G) * D;
-  const uintptr_t q_base = reinterpret_cast<uintptr_t>(P.q) + q_row0 * q_es;
-  const uintptr_t s_base = reinterpret_cast<uintptr_t>(P.signs);
-
-  float ck[16], cv[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    ck[i] = P.k_centroids[i];
-    cv[i] = P.v_centroids[i];
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(reinterpret_cast<const void *>(q_base), has_q ? (uint32_t)(G * D) * q_es : 0u);
-  const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(reinterpret_cast<const void *>(s_base), has_q ? (uint32_t)D : 0u);
-  const uint32_t q_off = (uint32_t)(wave * D + lane * 2) * q_es;
-  // coordinates 2l, 2l+1: both halves of q0 (fp16) or q0 and q1 (fp32);
-  // for fp16 queries q1 is unused (past the last row it reads as zero)
-  const uint32_t q0 = __builtin_amdgcn_raw_buffer_load_b32(qsrc, q_off, 0, 0);
-  const uint32_t q1 = __builtin_amdgcn_raw_buffer_load_b32(qsrc, q_off + 4u, 0, 0);
-  const uint32_t sg = __builtin_amdgcn_raw_buffer_load_b16(ssrc, lane * 2, 0, 0);   // signs of coordinates 2l, 2l+1
+  // ---- set-up ----
+  // Waves 0-7 build the pair tables and the rotated query; waves 8-15 first
+  // request their first two tiles.  The set-up waves request theirs after
+  // the set-up: at kernel start every compute unit floods the memory system,
+  // a wave's tile requests can sit in the issue queue for microseconds, and
+  // a wave issues in order, so a set-up wave stuck behind its own tile
+  // requests would hold up the tables everybody needs.  Readiness is an LDS
+  // count the set-up waves bump, not a barrier, so no wave waits for another
+  // wave's requests to go out.
+  static_assert(kBlock == 1024 && kSetupWaves * 64 * 16 == 2 * 65536 / 16, "pair-table fill layout");
   if (tid < kWaves) next_tile[tid] = 2 * gw;
-  __builtin_amdgcn_sched_barrier(0);
+  if (tid == 0) ready = 0u;
+  __syncthreads();                                   // cheap here: no wave has memory requests yet
 
   int ia = gwave, ic = gwave + gw;                   // first tiles of this wave; later ones from its group's counter
   Tile ta, tc;
-  load_tile(ta, src, t0 + ia * kTile, ia >= ntiles);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- pair tables: key table in the first 64 KB, value table in the next ----
-  // Row (code byte) r of a table holds 32 slots of the 8-byte entry
-  // (e(c[r % 16]), e(c[r / 16])).  Chunks of 16 bytes (two slots) are written
-  // by consecutive lanes: thread t writes chunks t + 1024k, k = 0..7, i.e.
-  // table k / 4, row t/16 + 64 (k % 4): low nibble (t/16) % 16 for every k,
-  // high nibble t/256 + 4 (k % 4).
-  {
-    // (t/16) % 16 = 4 (wave % 4) + lane / 16 and t/256 = wave / 4: uniform
-    // parts chosen by a scalar switch (constant indices keep the tables in
-    // scalar registers), then one of four values by lane row
-    const int r4 = lane >> 4;
-    float lk[4], lv[4], hk[4], hv[4];
-    switch (wave & 3) {
-      case 0: pick4<0, 1>(ck, cv, lk, lv); break;
-      case 1: pick4<4, 1>(ck, cv, lk, lv); break;
-      case 2: pick4<8, 1>(ck, cv, lk, lv); break;
-      default: pick4<12, 1>(ck, cv, lk, lv); break;
-    }
-    switch (wave >> 2) {
-      case 0: pick4<0, 4>(ck, cv, hk, hv); break;
-      case 1: pick4<1, 4>(ck, cv, hk, hv); break;
-      case 2: pick4<2, 4>(ck, cv, hk, hv); break;
-      default: pick4<3, 4>(ck, cv, hk, hv); break;
-    }
-    float lo_k = lk[0], lo_v = lv[0];
+  if (wave < kSetupWaves) {
+    // Centroids through uniform addresses (scalar loads the scalar cache
+    // serves to every wave of the chip); query rows and signs for the waves
+    // that rotate them (zero-size descriptors elsewhere).
+    float ck[16], cv[16];
 #pragma unroll
-    for (int u = 1; u < 4; ++u) {
-      lo_k = (r4 == u) ? lk[u] : lo_k;
-      lo_v = (r4 == u) ? lv[u] : lo_v;
+    for (int i = 0; i < 16; ++i) {
+      ck[i] = P.k_centroids[i];
+      cv[i] = P.v_centroids[i];
     }
-    const uint32_t lok = split_entry(lo_k * kCodeScale), lov = split_entry(lo_v * kCodeScale);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t lo = (k < 4) ? lok : lov;
-      const uint32_t hi = split_entry(((k < 4) ? hk[k & 3] : hv[k & 3]) * kCodeScale);
-      const uint4_t e = {lo, hi, lo, hi};
-      *reinterpret_cast<uint4_t *>(tab + (tid + 1024 * k) * 16) = e;
-    }
-  }
+    const bool has_q = wave < G;
+    const int q_f16 = P.q_f16;
+    const uint32_t q_es = q_f16 ? 2u : 4u;
+    const size_t q_row0 = ((size_t)b * P.q_heads + (size_t)hkv * G) * D;
+    const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(static_cast<const uint8_t *>(P.q) + q_row0 * q_es,
+                                                  has_q ? (uint32_t)(G * D) * q_es : 0u);
+    const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(P.signs, has_q ? (uint32_t)D : 0u);
+    const uint32_t q_off = (uint32_t)(wave * D + lane * 2) * q_es;
+    // coordinates 2l, 2l+1: both halves of q0 (fp16) or q0 and q1 (fp32);
+    // for fp16 queries q1 is unused (past the last row it reads as zero)
+    const uint32_t q0 = __builtin_amdgcn_raw_buffer_load_b32(qsrc, q_off, 0, 0);
+    const uint32_t q1 = __builtin_amdgcn_raw_buffer_load_b32(qsrc, q_off + 4u, 0, 0);
+    const uint32_t sg = __builtin_amdgcn_raw_buffer_load_b16(ssrc, lane * 2, 0, 0);   // signs of coordinates 2l, 2l+1
 
-  // ---- rotated query of head `wave` (waves G..7 write zero rows) ----
-  // Lane l holds coordinates 2l, 2l+1: sign flip, the stride-1 butterfly in
-  // the lane, strides 2..64 across lanes (xor 1..32).  The rotated vector is
-  // scaled so that its largest |z| lies in (64, 128] and stored in the two
-  // B-operand forms (z_hi, z_hi) (row 2h) and (z_lo, 0) (row 2h+1).
-  if (wave < kGMax) {
+    // ---- pair tables: key table in the first 64 KB, value table in the next ----
+    // Row (code byte) r of a table holds 32 slots of the 8-byte entry
+    // (e(c[r % 16]), e(c[r / 16])).  Chunks of 16 bytes (two slots) are
+    // written by consecutive lanes: thread t < 512 writes chunks t + 512k,
+    // k = 0..15, i.e. table k / 8, row t/16 + 32 (k % 8): low nibble
+    // (t/16) % 16 = 4 (wave % 4) + lane / 16 for every k, high nibble
+    // wave / 4 + 2 (k % 8).
+    {
+      // uniform parts chosen by a scalar switch (constant indices keep the
+      // centroids in scalar registers), then one of four values by lane row
+      const int r4 = lane >> 4;
+      float lk[4], lv[4], hk[8], hv[8];
+      switch (wave & 3) {
+        case 0: pick<0, 1>(ck, cv, lk, lv); break;
+        case 1: pick<4, 1>(ck, cv, lk, lv); break;
+        case 2: pick<8, 1>(ck, cv, lk, lv); break;
+        default: pick<12, 1>(ck, cv, lk, lv); break;
+      }
+      if (wave >> 2) pick<1, 2>(ck, cv, hk, hv);
+      else pick<0, 2>(ck, cv, hk, hv);
+      float lo_k = lk[0], lo_v = lv[0];
+#pragma unroll
+      for (int u = 1; u < 4; ++u) {
+        lo_k = (r4 == u) ? lk[u] : lo_k;
+        lo_v = (r4 == u) ? lv[u] : lo_v;
+      }
+      const uint32_t lok = split_entry(lo_k * kCodeScale), lov = split_entry(lo_v * kCodeScale);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t lo = (k < 8) ? lok : lov;
+        const uint32_t hi = split_entry(((k < 8) ? hk[k & 7] : hv[k & 7]) * kCodeScale);
+        const uint4_t e = {lo, hi, lo, hi};
+        *reinterpret_cast<uint4_t *>(tab + (tid + 512 * k) * 16) = e;
+      }
+    }
+
+    // ---- rotated query of head `wave` (waves G..7 write zero rows) ----
+    // Lane l holds coordinates 2l, 2l+1: sign flip, the stride-1 butterfly in
+    // the lane, strides 2..64 across lanes (xor 1..32).  The rotated vector
+    // is scaled so that its largest |z| lies in (64, 128] and stored in the
+    // two B-operand forms (z_hi, z_hi) (row 2h) and (z_lo, 0) (row 2h+1).
+    static_assert(kSetupWaves == kGMax, "one set-up wave per query row pair");
     uint2_t f0 = {0u, 0u}, f1 = {0u, 0u};
     float fac = 0.f;
     if (has_q) {
@@ -473,11 +469,25 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
     *reinterpret_cast<uint2_t *>(&qtab[2 * wave][lane * 2]) = f0;
     *reinterpret_cast<uint2_t *>(&qtab[2 * wave + 1][lane * 2]) = f1;
     if (lane == 0) qfac[wave] = fac;
+    // this wave's table, query and factor writes complete before its count
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) __hip_atomic_fetch_add(&ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(ta, src, t0 + ia * kTile, ia >= ntiles);
   __builtin_amdgcn_sched_barrier(0);
   load_tile(tc, src, t0 + ic * kTile, ic >= ntiles);
   __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
+
+  // Wait for the eight set-up counts.  The spin is bounded: every set-up
+  // wave reaches its count without waiting on anything but its own loads,
+  // so the limit (tens of milliseconds) only guards against a hang.
+  for (int spin = 0; spin < kSpinLimit; ++spin) {
+    const uint32_t r = __hip_atomic_load(&ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (__builtin_amdgcn_readfirstlane(r) >= (uint32_t)kSetupWaves) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
   // B operand of key block kb for column n: query table row n (head n / 2,
   // form n % 2), coordinates 32g + 4kb .. +3
