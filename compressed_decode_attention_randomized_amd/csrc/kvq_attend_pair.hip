@@ -324,10 +324,11 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   __shared__ __attribute__((aligned(16))) uint8_t tab[2 * 65536];
   __shared__ __attribute__((aligned(16))) uint32_t qtab[2 * kGMax][kRowPad];
   __shared__ float red_ml[kWaves][kGMax][3];      // (reference, sum, largest score) per wave and head
-  __shared__ float wfac[kWaves][kGMax];
   __shared__ float qfac[kGMax];
+  __shared__ float wfac[kWaves][kGMax];
   __shared__ uint32_t next_tile[kWaves];
   __shared__ uint32_t ready;                         // set-up waves done
+  __shared__ uint32_t v_table[1];                    // offset of the value table: 0 when shared with the keys
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -405,6 +406,12 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
     const uint32_t q1 = __builtin_amdgcn_raw_buffer_load_b32(qsrc, q_off + 4u, 0, 0);
     const uint32_t sg = __builtin_amdgcn_raw_buffer_load_b16(ssrc, lane * 2, 0, 0);   // signs of coordinates 2l, 2l+1
 
+    // Keys and values with one codebook (the usual case: one format for
+    // both) share the key table.
+    bool same = true;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) same = same && (ck[i] == cv[i]);
+
     // ---- pair tables: key table in the first 64 KB, value table in the next ----
     // Row (code byte) r of a table holds 32 slots of the 8-byte entry
     // (e(c[r % 16]), e(c[r / 16])).  Chunks of 16 bytes (two slots) are
@@ -433,12 +440,20 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
       }
       const uint32_t lok = split_entry(lo_k * kCodeScale), lov = split_entry(lo_v * kCodeScale);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t lo = (k < 8) ? lok : lov;
-        const uint32_t hi = split_entry(((k < 8) ? hk[k & 7] : hv[k & 7]) * kCodeScale);
-        const uint4_t e = {lo, hi, lo, hi};
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t hi = split_entry(hk[k] * kCodeScale);
+        const uint4_t e = {lok, hi, lok, hi};
         *reinterpret_cast<uint4_t *>(tab + (tid + 512 * k) * 16) = e;
       }
+      if (!same) {
+#pragma unroll
+        for (int k = 8; k < 16; ++k) {
+          const uint32_t hi = split_entry(hv[k & 7] * kCodeScale);
+          const uint4_t e = {lov, hi, lov, hi};
+          *reinterpret_cast<uint4_t *>(tab + (tid + 512 * k) * 16) = e;
+        }
+      }
+      if (tid == 0) v_table[0] = same ? 0u : 0x10000u;
     }
 
     // ---- rotated query of head `wave` (waves G..7 write zero rows) ----
@@ -495,7 +510,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
 #pragma unroll
   for (int kb = 0; kb < D / 16; ++kb) bk[kb] = *reinterpret_cast<const uint4_t *>(&qtab[n][g * 32 + 4 * kb]);
   const float sfac = qfac[n >> 1];
-  const uint32_t kslot = (uint32_t)(lane & 31) * 8, vslot = kslot | 0x10000u;
+  const uint32_t kslot = (uint32_t)(lane & 31) * 8, vslot = kslot | v_table[0];
   float m1 = -1.f;
   asm volatile("" : "+s"(m1));                       // no instruction: keeps -1 from being folded
 

@@ -204,6 +204,34 @@ def test_mha_and_gqa2(dev):
         run_case(dev, wl)
 
 
+def test_distinct_value_codebook(dev):
+    """Keys and values decoded through different codebooks (the value table
+    replaced after the append by 1.2 times the Lloyd-Max centroids): the
+    attention kernels must not assume one table for both."""
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, seq_len=300, splits=3)
+    inp = W.generate(wl)
+    d, T = wl.head_dim, wl.seq_len
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, d, T, _fmt(wl.k_bits), _fmt(wl.v_bits),
+                                 seed=W.SIGN_SEED, device=dev)
+    cache.append(_t(inp.k, dev), _t(inp.v, dev), start_pos=0)
+    c, _ = O.codebook(wl.v_bits, d)
+    cv = (1.2 * c.astype(np.float64)).astype(np.float32)
+    cache.v_centroids.copy_(torch.from_numpy(cv).to(dev))
+    assert cache.attention_kernel(wl.q_heads) == "attend_pair_kernel"
+    q = _t(inp.q, dev)
+    part_o, part_ml = cache.attend(q, T, wl.splits, 0)
+    out = cache.merge(part_o, part_ml, wl.splits, 0)
+    torch.cuda.synchronize()
+    kp = cache.k_codes[:, :, :T].cpu().numpy()
+    vp = cache.v_codes[:, :, :T].cpu().numpy()
+    kn16 = cache.k_norms[:, :, :T].cpu().numpy()
+    vn16 = cache.v_norms[:, :, :T].cpu().numpy()
+    k_rot = _dequant_gpu_cache(kp, kn16, wl.k_bits, d)
+    v_rot = O.fp16_bits_to_f64(vn16.view(np.uint16))[..., None] * cv.astype(np.float64)[O.unpack(vp, wl.v_bits, d)]
+    ref = O.attention(inp.q.astype(np.float64), k_rot, v_rot, _signs(d))
+    _rows_close("distinct value codebook", out.cpu().numpy(), ref)
+
+
 def test_head_dim_64(dev):
     wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, head_dim=64, seq_len=200, splits=3)
     run_case(dev, wl)
