@@ -1,0 +1,68 @@
+"""A decode step (append one token, split attention, merge) captured in a HIP
+graph replays to the eager result, replay after replay, with eager work and
+synchronisation in between (the timed loop of bench.py runs this way)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import compressed_decode_attention_randomized_amd as kvq  # noqa: E402
+import workloads as W  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kvq.load()
+    return torch.device("cuda")
+
+
+@pytest.mark.parametrize("name", ["llama7b_layer", "two_tier"])
+def test_decode_step_graph_replays_match_eager(dev, name):
+    wl = W.WORKLOADS[name].scaled(batch=1, seq_len=700, splits=8)
+    inp = W.generate(wl)
+    if wl.near_fraction:
+        kn, vn = inp.tier("near")
+        kf, vf = inp.tier("far")
+        near_splits = 1
+        near_k = torch.from_numpy(np.ascontiguousarray(kn)).to(dev)
+        near_v = torch.from_numpy(np.ascontiguousarray(vn)).to(dev)
+    else:
+        kf, vf, near_splits, near_k, near_v = inp.k, inp.v, 0, None, None
+    T = kf.shape[2]
+    fmt = {2: kvq.KVQ_LM2, 3: kvq.KVQ_LM3, 4: kvq.KVQ_LM4, 8: kvq.KVQ_FP8_E4M3}
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, T, fmt[wl.k_bits], fmt[wl.v_bits],
+                                 seed=W.SIGN_SEED, device=dev, near_k=near_k, near_v=near_v)
+    cache.append(torch.from_numpy(np.ascontiguousarray(kf)).to(dev),
+                 torch.from_numpy(np.ascontiguousarray(vf)).to(dev), 0)
+    knew, vnew = (torch.from_numpy(a).to(dev) for a in W.new_token(wl))
+    q = torch.from_numpy(inp.q).to(dev)
+    po, pml = cache.partial_buffers(wl.q_heads, wl.splits, near_splits)
+    out = torch.empty((wl.batch, wl.q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+
+    def step():
+        cache.append(knew, vnew, T - 1)
+        cache.attend(q, T, wl.splits, near_splits, po, pml)
+        cache.merge(po, pml, wl.splits, near_splits, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    assert torch.isfinite(ref).all()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    po2, pml2 = cache.partial_buffers(wl.q_heads, wl.splits, near_splits)
+    for _ in range(4):
+        out.fill_(float("nan"))
+        po.fill_(float("nan"))
+        cache.attend(q, T, wl.splits, near_splits, po2, pml2)      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
