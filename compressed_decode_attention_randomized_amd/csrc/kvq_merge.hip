@@ -1,14 +1,5 @@
-// Split merge and the single inverse rotation, gfx950.
-//
-// One wave per (b, query head); lane l owns output coordinates
-// [l*E, (l+1)*E), E = D / 64.  The lanes read the split states (m_s, l_s)
-// 64 at a time and form, with wave reductions,
-//   M = max m_s, w_s = l_s exp(m_s - M), W = sum w_s,
-// then accumulate the near-tier splits (original domain) and the far-tier
-// splits (rotated domain) separately, eight splits' loads in flight at a
-// time.  The far sum is mapped back once with R^T y = s * (H y) / sqrt(D):
-// the Walsh-Hadamard stages inside a lane's E coordinates run in registers,
-// the six across lanes with DPP and row swaps.
+// Split-merge kernel: one wave per (b, query head) row; the merge itself is
+// merge_row (shared with the attention kernels that merge in place).
 // Source: "FoveatedKV", "Making it fast" (split-K partial states merged after
 // the fused pass; near and far tiers share one softmax).
 #include <hip/hip_runtime.h>
@@ -16,106 +7,19 @@
 #include <stdint.h>
 
 #include "kvq_internal.h"
-#include "kvq_lane.h"
+#include "kvq_merge.h"
 
 namespace kvq {
 namespace {
-
-constexpr int kUnroll = 8;
-
-template <int E>
-__device__ inline void load_row(const float *p, float (&v)[E]) {
-  if constexpr (E == 1) {
-    v[0] = p[0];
-  } else if constexpr (E == 2) {
-    const float2 t = *reinterpret_cast<const float2 *>(p);
-    v[0] = t.x;
-    v[1] = t.y;
-  } else {
-    static_assert(E == 4, "coordinates per lane");
-    const float4 t = *reinterpret_cast<const float4 *>(p);
-    v[0] = t.x;
-    v[1] = t.y;
-    v[2] = t.z;
-    v[3] = t.w;
-  }
-}
 
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(const float *__restrict__ part_o, const float *__restrict__ part_ml,
                                                   int splits, int near_splits, const int8_t *__restrict__ signs,
                                                   float *__restrict__ out, float *__restrict__ lse) {
-  constexpr int E = D / 64;
-  const int lane = threadIdx.x;
   const size_t row = blockIdx.x;
   const int S = splits + near_splits;
-  const float *ml = part_ml + row * S * 2;
-  const float *po = part_o + row * S * D + lane * E;
-
-  float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
-  M = wave_max(M, lane);
-
-  float W = 0.f;
-  float near_acc[E], far_acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) near_acc[e] = far_acc[e] = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    float w = 0.f;
-    if (s0 + lane < S) {
-      const float m = ml[2 * (s0 + lane)], l = ml[2 * (s0 + lane) + 1];
-      w = (m == -INFINITY || l == 0.f) ? 0.f : l * expf(m - M);
-    }
-    W += w;
-    const int cnt = min(64, S - s0);
-    for (int k0 = 0; k0 < cnt; k0 += kUnroll) {
-      float v[kUnroll][E];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (k0 + u < cnt) {
-          load_row<E>(po + (size_t)(s0 + k0 + u) * D, v[u]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < E; ++e) v[u][e] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int k = min(k0 + u, cnt - 1);
-        const float wk = (k0 + u < cnt) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k)) : 0.f;
-        const bool near = s0 + k0 + u < near_splits;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          if (near) near_acc[e] = fmaf(wk, v[u][e], near_acc[e]);
-          else far_acc[e] = fmaf(wk, v[u][e], far_acc[e]);
-        }
-      }
-    }
-  }
-  W = wave_sum(W, lane);
-
-  // inverse rotation of the far sum: stages of stride < E inside the lane,
-  // then the six cross-lane stages
-#pragma unroll
-  for (int st = 1; st < E; st <<= 1) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (!(e & st)) {
-        const float a = far_acc[e], c = far_acc[e + st];
-        far_acc[e] = a + c;
-        far_acc[e + st] = a - c;
-      }
-    }
-  }
-  const float inv_w = (W > 0.f) ? 1.f / W : 0.f;
-  const float rs = rsqrtf((float)D);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const float y = fwht_lanes(far_acc[e], lane) * rs;
-    const float far = (signs[lane * E + e] < 0) ? -y : y;
-    out[row * D + lane * E + e] = (near_acc[e] + far) * inv_w;
-  }
-  if (lse && lane == 0) lse[row] = (W > 0.f) ? M + logf(W) : -INFINITY;
+  merge_row<D>(part_o + row * S * D, part_ml + row * S * 2, splits, near_splits, signs, out + row * D,
+               lse ? lse + row : nullptr, threadIdx.x);
 }
 
 template <int D>
