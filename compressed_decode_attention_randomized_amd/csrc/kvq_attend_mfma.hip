@@ -317,7 +317,8 @@ __device__ inline void process_tile(const Tile<D, KB, VB> &t, const uint32_t (*b
 }
 
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(kBlock, 3) void attend_mfma_kernel(MParams P) {
+// d = 256 keeps two work-groups per SIMD row (at most 256 registers per lane)
+__global__ __launch_bounds__(kBlock, D == 256 ? 2 : 3) void attend_mfma_kernel(MParams P) {
   using Gm = Geometry<D, KB, VB>;
   constexpr int NKB = Gm::NKB, VDL = Gm::VDL;
   constexpr int STEP = kWaves * kTile;
