@@ -103,15 +103,22 @@ def read_traffic(workload: str, kernel_sha: str):
         return None
 
 
-def kernel_source_sha() -> str:
-    """Hash of every attention-kernel source (all three kernels and their
-    shared header), so a traffic figure taken on other code is not reused."""
-    import glob
+KERNEL_SOURCES = {
+    "attend_pair_kernel": ("kvq_attend_pair.hip",),
+    "attend_mfma_kernel": ("kvq_attend_mfma.hip",),
+    "attend_kernel": ("kvq_attend.hip",),
+}
+
+
+def kernel_source_sha(kernel: str = "attend_pair_kernel") -> str:
+    """Hash of the sources a traffic figure depends on: the kernel's own file
+    and the headers every attention kernel includes, so a figure taken on
+    other code is not reused."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "compressed_decode_attention_randomized_amd", "csrc")
-    for p in sorted(glob.glob(os.path.join(csrc, "kvq_attend*.hip")) + [os.path.join(csrc, "kvq_lane.h")]):
-        h.update(open(p, "rb").read())
+    for name in KERNEL_SOURCES.get(kernel, ()) + ("kvq_lane.h", "kvq_internal.h"):
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
 
@@ -301,7 +308,8 @@ def main(argv=None) -> int:
     att_bytes = by["cache"] + by["q"] + by["out"]
     step_bytes = att_bytes + by["append_token"]
     achieved = att_bytes / (att_avg / 1e3) / 1e9
-    traffic = read_traffic(wl.name, kernel_source_sha())
+    kernel = caches[0].attention_kernel(wl.q_heads, near_splits)
+    traffic = read_traffic(wl.name, kernel_source_sha(kernel))
     result = {
         "metric": METRIC,
         "value": round(step_bytes / (ms_step / 1e3) / 1e9, 2),
@@ -325,7 +333,7 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": caches[0].attention_kernel(wl.q_heads, near_splits), "bytes_per_launch": att_bytes,
+                     "kernel": kernel, "bytes_per_launch": att_bytes,
                      "avg_us": round(att_avg * 1e3, 3),
                      "event_pair_avg_us": round(float(np.mean(att_ms)) * 1e3, 3),
                      "event_pair_min_us": round(min(att_ms) * 1e3, 3)},
