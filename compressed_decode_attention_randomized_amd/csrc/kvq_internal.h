@@ -25,6 +25,9 @@ struct AppendArgs {
   const float *k_centroids, *v_centroids;
 };
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream, bool *supported);
+// Bulk-throughput variant (Lloyd-Max keys and values, head_dim 64/128/256).
+bool fast_append_supported(const AppendArgs &a);
+hipError_t launch_append_fast(const AppendArgs &a, hipStream_t stream);
 
 // Decode-attention launch (validated arguments).
 struct AttendArgs {
