@@ -173,11 +173,12 @@ __device__ inline uint32_t table_code(const TableEntry *table, float t, float ma
   return te.code_lo + (t >= te.boundary ? 1u : 0u);
 }
 
-// One vector in float64, exactly as the reference kernel computes it (the
-// butterflies are exact for fp16 input): its codes go to cb in coordinate
-// order; returns the fp16 norm bits.
+// One vector in float64, as the reference kernel computes it (the
+// butterflies are exact for fp16 input; each code counts the float64
+// midpoints at or below u = z / sqrt(D ||x||^2)): its codes go to cb in
+// coordinate order; returns the fp16 norm bits.
 template <int D, int BITS, typename T>
-__device__ uint16_t encode_exact(const T *src, const uint32_t (&smask)[kCpl], double *vb, const TableEntry *table,
+__device__ uint16_t encode_exact(const T *src, const uint32_t (&smask)[kCpl], double *vb, const float *centroids,
                                  int lv) {
   constexpr int LPV = D / kCpl;
   constexpr int GROUPS = kCpl / LPV;
@@ -206,12 +207,18 @@ __device__ uint16_t encode_exact(const T *src, const uint32_t (&smask)[kCpl], do
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   uint8_t *cb = reinterpret_cast<uint8_t *>(vb);
   if (ss > 0.0) {
-    const double r = 1.0 / sqrt(ss);
-    bool unused = false;
+    double mid[L - 1];
+#pragma unroll
+    for (int i = 0; i < L - 1; ++i) mid[i] = 0.5 * ((double)centroids[i] + (double)centroids[i + 1]);
+    const double r = 1.0 / sqrt((double)D * ss);
 #pragma unroll
     for (int i = 0; i < kCpl; ++i) {
+      const double u = z[i] * r;
+      uint32_t code = 0;
+#pragma unroll
+      for (int m = 0; m < L - 1; ++m) code += (u >= mid[m]) ? 1u : 0u;
       const int g = i / LPV, k = i % LPV;
-      cb[GROUPS * lv + g + kCpl * k] = (uint8_t)table_code(table, (float)(z[i] * r), 0.f, &unused);
+      cb[GROUPS * lv + g + kCpl * k] = (uint8_t)code;
     }
   } else {
 #pragma unroll
@@ -333,7 +340,7 @@ __device__ void encode_fast(const Stream &st, const int8_t *__restrict__ signs, 
     uint32_t nv = near ? 1u : 0u;
 #pragma unroll
     for (int m = 1; m < LPV; m <<= 1) nv |= __shfl_xor(nv, m);
-    if (nv) norm16 = encode_exact<D, BITS, T>(src, smask, vb, table, lv);
+    if (nv) norm16 = encode_exact<D, BITS, T>(src, smask, vb, st.centroids, lv);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
     // ---- pack this lane's 16 codes (coordinates 16 lv .. 16 lv + 15), LSB

@@ -250,6 +250,32 @@ def test_zero_and_special_vectors(dev):
     run_case(dev, wl, inp=inp)
 
 
+@pytest.mark.parametrize("d,bits", [(128, 4), (256, 2), (64, 3), (256, 4)])
+def test_append_near_decision_midpoints(dev, d, bits):
+    """Vectors whose rotated coordinates sit at a decision midpoint plus an
+    offset of 1e-7 .. 1e-3 on the N(0,1) scale (either side), fp32 input: the
+    bulk append decides most codes in fp32 and must send the ones it cannot
+    settle to its exact path; codes and norms match the oracle outside the
+    1e-6 band."""
+    rng = np.random.default_rng(77 + d + bits)
+    B, H, T = 1, 2, 256
+    _, mids = O.codebook(bits, d)
+    s = _signs(d)
+    n = B * H * T
+    pick = mids[rng.integers(0, len(mids), (n, d))] * math.sqrt(d)
+    off = rng.choice([-1.0, 1.0], (n, d)) * 10.0 ** rng.uniform(-7, -3, (n, d))
+    y = (pick + off) / math.sqrt(d) * rng.uniform(0.5, 4.0, (n, 1))     # rotated-domain vectors, various norms
+    x = (s * (y @ O.hadamard(d)) / math.sqrt(d)).astype(np.float32).reshape(B, H, T, d)
+    fmt = _fmt(bits)
+    cache = kvq.KVCache.allocate(B, H, d, T, fmt, fmt, seed=W.SIGN_SEED, device=dev)
+    cache.append(_t(x, dev), _t(x[:, :, ::-1].copy(), dev), 0)
+    torch.cuda.synchronize()
+    check_codes(f"d{d} b{bits} K", cache.k_codes[:, :, :T].cpu().numpy(), cache.k_norms[:, :, :T].cpu().numpy(),
+                x, bits, d)
+    check_codes(f"d{d} b{bits} V", cache.v_codes[:, :, :T].cpu().numpy(), cache.v_norms[:, :, :T].cpu().numpy(),
+                x[:, :, ::-1].copy(), bits, d)
+
+
 def test_incremental_append_equals_bulk(dev):
     wl = W.WORKLOADS["llama7b_layer"].scaled(batch=2, q_heads=8, kv_heads=2, seq_len=200)
     inp = W.generate(wl)
