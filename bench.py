@@ -104,7 +104,8 @@ def read_traffic(workload: str, kernel_sha: str):
 
 
 KERNEL_SOURCES = {
-    "attend_pair_kernel": ("kvq_attend_pair.hip",),
+    "attend_pair_kernel": ("kvq_attend_pair.hip", "kvq_pair.h"),
+    "attend_wide_kernel": ("kvq_attend_wide.hip", "kvq_pair.h"),
     "attend_mfma_kernel": ("kvq_attend_mfma.hip",),
     "attend_kernel": ("kvq_attend.hip",),
 }

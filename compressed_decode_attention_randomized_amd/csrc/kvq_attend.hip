@@ -407,6 +407,7 @@ hipError_t by_format(const AttendArgs &a, hipStream_t stream, bool *ok) {
 
 const char *attend_kernel_name(const AttendArgs &a) {
   if (pair_attend_supported(a)) return "attend_pair_kernel";
+  if (wide_attend_supported(a)) return "attend_wide_kernel";
   if (mfma_attend_supported(a)) return "attend_mfma_kernel";
   return "attend_kernel";
 }
@@ -415,6 +416,10 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supporte
   if (pair_attend_supported(a)) {
     *supported = true;
     return launch_attend_pair(a, stream);
+  }
+  if (wide_attend_supported(a)) {
+    *supported = true;
+    return launch_attend_wide(a, stream);
   }
   if (mfma_attend_supported(a)) return launch_attend_mfma(a, stream, supported);
   *supported = true;

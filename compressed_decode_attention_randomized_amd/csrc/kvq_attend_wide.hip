@@ -1,0 +1,391 @@
+// Split-K GQA decode attention on 4-bit Lloyd-Max keys and values, head
+// dimension 256: the pair-table matrix-core tile of the head-dimension-128
+// kernel (shared tile code), with twice the registers per tile.
+//
+// Work mapping: a work-group of 8 waves (two per SIMD: the query operand and
+// the value accumulator take 128 registers at this head size) fills a
+// compute unit and shares one pair table.  Its wave groups serve 2^lg
+// consecutive units of the flattened (b * Hkv + KV head, split) space, so
+// with few query heads per KV head a work-group covers splits of several
+// (b, KV head) pairs and the grid needs no second round of work-groups; a
+// group of several waves takes 16-token tiles from an LDS counter, two tiles
+// in flight per wave.  The group's rotated queries sit in LDS, one row pair
+// per head (hi and lo fp16 forms), at most 8 rows per work-group.
+// Sources: "The Engineering Behind AdapTQ", "Engineering the Hot Path"
+// (rotate q once, score from codes through a table, no dequantize pass);
+// "FoveatedKV", "Making it fast" (split-K, pre-scaled q, online softmax with
+// one exp per score, split merge); "I Ported a Google Research Paper to Apple
+// Silicon", "The Bit-Packing Problem" (4-bit codes, low nibble first).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+#include "kvq_lane.h"
+#include "kvq_pair.h"
+
+namespace kvq {
+namespace {
+
+using namespace pair;
+
+constexpr int D = 256;
+constexpr int kWaves = 8;
+constexpr int kMinWaves = 2;                   // waves per SIMD the register budget is sized for
+constexpr int kBlock = kWaves * 64;
+constexpr int kRow = D / 2;                     // packed bytes per 4-bit vector
+constexpr int kVDL = D / 16;                    // value coordinates per lane
+constexpr int kRowPad = D + 4;                  // query table row stride (words)
+constexpr int kZeroRow = 2 * kGMax;             // all-zero query row for the unused B columns
+// s_waitcnt vmcnt(8) expcnt(7) lgkmcnt(15): the eight loads of one tile
+constexpr int kWaitOlderTile = 0x0F70 | kTileLoads<D>;
+static_assert(kTileLoads<D> == 8, "tile loads");
+constexpr int kSetupWaves = 4;                  // waves that build the tables and the rotated queries
+
+struct WParams {
+  const void *q;
+  int q_f16;
+  int kv_heads, capacity, seq_len, num_splits;
+  int group_size;                  // query heads per KV head
+  int chunk;                       // tokens per split (a multiple of 32)
+  int group_log2;                  // log2 of the units one work-group covers (its wave groups)
+  int units;                       // (b, KV head) pairs times splits
+  const uint8_t *k_codes, *v_codes;
+  const uint16_t *k_norms, *v_norms;
+  const int8_t *signs;
+  const float *k_centroids, *v_centroids;
+  float *part_o, *part_ml;
+};
+
+__global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams P) {
+  // pair tables during the loop, the waves' value rows afterwards
+  __shared__ __attribute__((aligned(16))) uint8_t tab[2 * 65536];
+  __shared__ __attribute__((aligned(16))) uint32_t qtab[2 * kGMax + 1][kRowPad];
+  __shared__ float red_ml[kWaves][kGMax][3];      // (reference, sum, largest score) per wave and head
+  __shared__ float qfac[kGMax];
+  __shared__ float wfac[kWaves][kGMax];
+  __shared__ uint32_t next_tile[kWaves];
+  __shared__ uint32_t ready;                         // set-up waves done
+  __shared__ uint32_t v_table[1];                    // offset of the value table: 0 when shared with the keys
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, n = lane & 15;
+  const int G = P.group_size, S = P.num_splits;
+  const int lg = P.group_log2;                       // group_size << group_log2 <= 8 (host)
+  const int gw = kWaves >> lg;
+  const int grp = wave >> (3 - lg), gwave = wave & (gw - 1);
+  // this wave group's unit: pair index b * Hkv + KV head, and split; its
+  // query heads are rows pr * G + h of q, since Hq = Hkv * G
+  const int unit = (blockIdx.x << lg) + grp;
+  const bool active = unit < P.units;
+  const int pr = active ? unit / S : 0;
+  const int split = active ? unit - pr * S : 0;
+
+  // chunks of ceil(T/S) tokens rounded up to a multiple of 32 (from the
+  // host); full tiles [t0, t1f) go through the main loop, a partial last
+  // tile (only the last split can have one) after it
+  const int chunk = P.chunk;
+  const int t0 = active ? min(P.seq_len, split * chunk) : 0;
+  const int t1 = active ? min(P.seq_len, t0 + chunk) : 0;
+  const int ntiles = (t1 - t0) / kTile;
+  const int t1f = t0 + ntiles * kTile;
+  const uint32_t cap = (uint32_t)P.capacity;
+  Sources src;
+  src.kc = P.k_codes + (size_t)pr * cap * kRow;
+  src.vc = P.v_codes + (size_t)pr * cap * kRow;
+  src.kn = P.k_norms + (size_t)pr * cap;
+  src.vn = P.v_norms + (size_t)pr * cap;
+  src.code_bytes = cap * kRow;
+  src.norm_bytes = cap * 2;
+  set_offsets<D>(src, g, n);
+
+  // ---- set-up ----
+  // Waves 0-3 build the pair tables and the rotated queries; waves 4-7 first
+  // request their first two tiles (so the set-up waves' own requests do not
+  // sit ahead of the table work in their issue queues).  Readiness is an LDS
+  // count the set-up waves bump, not a barrier.
+  static_assert(kSetupWaves * 64 * 16 * 16 == 65536, "pair-table fill layout");
+  if (tid < kWaves) next_tile[tid] = 2 * gw;
+  if (tid == 0) ready = 0u;
+  __syncthreads();                                   // cheap here: no wave has memory requests yet
+
+  int ia = gwave, ic = gwave + gw;                   // first tiles of this wave; later ones from its group's counter
+  Tile<D> ta, tc;
+  if (wave < kSetupWaves) {
+    float ck[16], cv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ck[i] = P.k_centroids[i];
+      cv[i] = P.v_centroids[i];
+    }
+    bool same = true;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) same = same && (ck[i] == cv[i]);
+
+    // ---- pair tables: key table in the first 64 KB, value table in the next ----
+    // Row (code byte) r of a table holds 32 slots of the 8-byte entry
+    // (e(c[r % 16]), e(c[r / 16])).  Thread t < 256 writes the 16-byte
+    // chunks (two slots) t + 256k, k = 0..15: row t/16 + 16k, so low nibble
+    // t/16 = 4 wave + lane/16 for every k and high nibble k.
+    {
+      const int r4 = lane >> 4;
+      float lk[4], lv[4];
+      switch (wave) {
+        case 0: pick<0, 1>(ck, cv, lk, lv); break;
+        case 1: pick<4, 1>(ck, cv, lk, lv); break;
+        case 2: pick<8, 1>(ck, cv, lk, lv); break;
+        default: pick<12, 1>(ck, cv, lk, lv); break;
+      }
+      float lo_k = lk[0], lo_v = lv[0];
+#pragma unroll
+      for (int u = 1; u < 4; ++u) {
+        lo_k = (r4 == u) ? lk[u] : lo_k;
+        lo_v = (r4 == u) ? lv[u] : lo_v;
+      }
+      const uint32_t lok = split_entry(lo_k * kCodeScale), lov = split_entry(lo_v * kCodeScale);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t hi = split_entry(ck[k] * kCodeScale);
+        const uint4_t e = {lok, hi, lok, hi};
+        *reinterpret_cast<uint4_t *>(tab + (tid + 256 * k) * 16) = e;
+      }
+      if (!same) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const uint32_t hi = split_entry(cv[k] * kCodeScale);
+          const uint4_t e = {lov, hi, lov, hi};
+          *reinterpret_cast<uint4_t *>(tab + 65536 + (tid + 256 * k) * 16) = e;
+        }
+      }
+      if (tid == 0) v_table[0] = same ? 0u : 0x10000u;
+    }
+    if (tid < D) qtab[kZeroRow][tid] = 0u;
+
+    // ---- rotated queries: rows r = wave and wave + 4 (head r % G of the
+    // unit r / G of this work-group) ----
+    // Lane l holds coordinates 4l..4l+3: sign flip, the stride-1 and
+    // stride-2 butterflies in the lane, strides 4..128 across lanes (xor
+    // 1..32).  The rotated vector is scaled so that its largest |z| lies in
+    // (64, 128] and stored in the two B-operand forms (z_hi, z_hi) (row 2r)
+    // and (z_lo, 0) (row 2r+1).
+    const int q_f16 = P.q_f16;
+    const uint32_t q_es = q_f16 ? 2u : 4u;
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = wave + kSetupWaves * rr;
+      if (r >= (G << lg)) break;
+      const int gr = r / G, h = r - gr * G;
+      const int u = (blockIdx.x << lg) + gr;
+      const bool has_q = u < P.units;
+      const size_t q_row = (size_t)(has_q ? u / S : 0) * G + h;
+      const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(static_cast<const uint8_t *>(P.q) + q_row * D * q_es,
+                                                    has_q ? (uint32_t)D * q_es : 0u);
+      const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(P.signs, has_q ? (uint32_t)D : 0u);
+      // both forms are read; the one of the other element size goes unused
+      // (for fp16 rows its upper lanes lie past the row and read as zero)
+      const uint2_t qh = __builtin_amdgcn_raw_buffer_load_b64(qsrc, lane * 8, 0, 0);
+      const uint4_t qf = __builtin_amdgcn_raw_buffer_load_b128(qsrc, lane * 16, 0, 0);
+      const uint32_t sg = __builtin_amdgcn_raw_buffer_load_b32(ssrc, lane * 4, 0, 0);   // signs of 4l..4l+3
+      float z[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t hw = (e < 2) ? qh.x : qh.y;
+        const float v = q_f16 ? half_value((hw >> (16 * (e & 1))) & 0xFFFFu) : __builtin_bit_cast(float, qf[e]);
+        z[e] = ((sg >> (8 * e + 7)) & 1u) ? -v : v;
+      }
+      const float a0 = z[0] + z[1], a1 = z[0] - z[1], a2 = z[2] + z[3], a3 = z[2] - z[3];
+      float y[4] = {a0 + a2, a1 + a3, a0 - a2, a1 - a3};
+      float am = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[e] = fwht_lanes(y[e], lane);
+        am = fmaxf(am, fabsf(y[e]));
+      }
+      const float zmax = wave_max(am, lane);
+      const float qscale = (zmax > 0.f) ? exp2f(7.f - ceilf(log2f(zmax))) : 1.f;
+      uint4_t f0, f1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float zs = y[e] * qscale;
+        const _Float16 hs = (_Float16)zs;
+        f0[e] = pack2(hs, hs);
+        f1[e] = pack2((_Float16)(zs - (float)hs), (_Float16)0.f);
+      }
+      *reinterpret_cast<uint4_t *>(&qtab[2 * r][lane * 4]) = f0;
+      *reinterpret_cast<uint4_t *>(&qtab[2 * r + 1][lane * 4]) = f1;
+      if (lane == 0) qfac[r] = has_q ? kLog2e / ((float)D * kCodeScale * qscale) : 0.f;
+    }
+    // this wave's table, query and factor writes complete before its count
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) __hip_atomic_fetch_add(&ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile<D>(ta, src, t0 + ia * kTile, ia >= ntiles);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile<D>(tc, src, t0 + ic * kTile, ic >= ntiles);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Wait for the set-up counts (bounded: every set-up wave reaches its count
+  // without waiting on anything but its own loads).
+  for (int spin = 0; spin < kSpinLimit; ++spin) {
+    const uint32_t r = __hip_atomic_load(&ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (__builtin_amdgcn_readfirstlane(r) >= (uint32_t)kSetupWaves) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+  // B operand of key block kb for column n: the group's query row 2h + form
+  // for n = 2h + form < 2G (the zero row otherwise), coordinates
+  // 64g + 4kb .. +3
+  const bool col = n < 2 * G;
+  const int qrow = col ? grp * 2 * G + n : kZeroRow;
+  uint4_t bk[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) bk[kb] = *reinterpret_cast<const uint4_t *>(&qtab[qrow][g * 64 + 4 * kb]);
+  const float sfac = col ? qfac[grp * G + (n >> 1)] : 0.f;
+  const uint32_t kslot = (uint32_t)(lane & 31) * 8, vslot = kslot | v_table[0];
+  float m1 = -1.f;
+  asm volatile("" : "+s"(m1));                       // no instruction: keeps -1 from being folded
+
+  float4_t dv[kVDL];
+#pragma unroll
+  for (int dt = 0; dt < kVDL; ++dt) dv[dt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;             // softmax reference and sum for this lane's column
+  float m_top = -INFINITY;                           // largest score of this lane's rows
+
+  // Tiles alternate between the two tile buffers, each refilled with a newly
+  // claimed tile right after use; the explicit vmcnt (the older tile's
+  // loads) is the only wait for a tile's data; loads past the end return
+  // zeros.
+  while (ia < ntiles) {
+    uint32_t nx = 0u;
+    if (lane == 0) nx = atomicAdd(&next_tile[grp], 1u);
+    __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
+    process_tile<D, false>(ta, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
+    asm volatile("" : "+v"(nx));                     // keeps the read of the answer here
+    const int na = __builtin_amdgcn_readfirstlane(nx);
+    load_tile<D>(ta, src, t0 + na * kTile, na >= ntiles);
+    int nc = ntiles;
+    if (ic < ntiles) {
+      uint32_t ny = 0u;
+      if (lane == 0) ny = atomicAdd(&next_tile[grp], 1u);
+      __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
+      process_tile<D, false>(tc, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run, l_run, m_top);
+      asm volatile("" : "+v"(ny));
+      nc = __builtin_amdgcn_readfirstlane(ny);
+    }
+    load_tile<D>(tc, src, t0 + nc * kTile, nc >= ntiles);
+    ia = na;
+    ic = nc;
+  }
+  // the last split's partial tile [t1f, t1)
+  if (gwave == 0 && t1f < t1) {
+    load_tile<D>(ta, src, t1f, false);
+    process_tile<D, true>(ta, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
+  }
+
+  // ---- wave epilogue: (m, l) per head to LDS; after the barrier (the
+  // tables are dead then) the value rows of the heads in use ----
+  l_run = sum_rows(add_swap1(l_run));                // both lanes of a head, all four lane rows
+  m_top = max_rows(fmaxf(m_top, lane_swap1(m_top)));
+  if (lane < 2 * kGMax && !(lane & 1)) {            // lane 2h of the first row: head h
+    red_ml[wave][lane >> 1][0] = m_run;
+    red_ml[wave][lane >> 1][1] = l_run;
+    red_ml[wave][lane >> 1][2] = m_top;
+  }
+  __syncthreads();                                   // every wave is done with the tables
+  float *red_acc = reinterpret_cast<float *>(tab);   // [wave][head][D]
+  // accumulator rows 4g, 4g+1 (head 2g) and 4g+2, 4g+3 (head 2g+1);
+  // coordinate 16n + dt in dv[dt]
+#pragma unroll
+  for (int hp = 0; hp < 2; ++hp) {
+    if (2 * g + hp < G) {
+      float *r = red_acc + (size_t)(wave * kGMax + 2 * g + hp) * D + 16 * n;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4_t *>(r + 4 * q) =
+            (float4_t){dv[4 * q][2 * hp] + dv[4 * q][2 * hp + 1], dv[4 * q + 1][2 * hp] + dv[4 * q + 1][2 * hp + 1],
+                       dv[4 * q + 2][2 * hp] + dv[4 * q + 2][2 * hp + 1], dv[4 * q + 3][2 * hp] + dv[4 * q + 3][2 * hp + 1]};
+    }
+  }
+  // Weight of each wave's rows in its group's merge, one lane of wave 0 per
+  // (head h, wave w) (h = tid / 8, w = tid % 8): a group's waves are gw
+  // consecutive lanes, reduced with DPP exchanges.  The weight
+  // exp2(m_w - M) / (L * code scale) folds in the softmax denominator.
+  if (tid < kWaves * kGMax) {
+    const int h = tid >> 3, w = tid & (kWaves - 1);
+    const float m = red_ml[w][h][0], l = red_ml[w][h][1], mt = red_ml[w][h][2];
+    float M = m;
+    if (gw > 1) M = fmaxf(M, xor_lane<1>(M, lane));
+    if (gw > 2) M = fmaxf(M, xor_lane<2>(M, lane));
+    if (gw > 4) M = fmaxf(M, xor_lane<4>(M, lane));
+    const float f = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    float L = l * f;
+    if (gw > 1) L += xor_lane<1>(L, lane);
+    if (gw > 2) L += xor_lane<2>(L, lane);
+    if (gw > 4) L += xor_lane<4>(L, lane);
+    wfac[w][h] = (L > 0.f) ? f / (L * kCodeScale) : 0.f;
+    // the split's state is reported against its largest score
+    float Mt = mt;
+    if (gw > 1) Mt = fmaxf(Mt, xor_lane<1>(Mt, lane));
+    if (gw > 2) Mt = fmaxf(Mt, xor_lane<2>(Mt, lane));
+    if (gw > 4) Mt = fmaxf(Mt, xor_lane<4>(Mt, lane));
+    const int u = (blockIdx.x << lg) + (w >> (3 - lg));
+    if ((w & (gw - 1)) == 0 && h < G && u < P.units) {
+      const int upr = u / S, usp = u - upr * S;
+      const size_t row = ((size_t)upr * G + h) * S + usp;
+      const bool any = L > 0.f;
+      P.part_ml[row * 2 + 0] = any ? Mt * kLn2 : -INFINITY;
+      P.part_ml[row * 2 + 1] = any ? L * exp2f(M - Mt) : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- merge each group's waves: one thread per (head, coordinate) ----
+  for (int gi = 0; gi < (1 << lg); ++gi) {
+    const int u = (blockIdx.x << lg) + gi;
+    if (u >= P.units) break;
+    const int upr = u / S, usp = u - upr * S;
+    for (int i = tid; i < G * D; i += kBlock) {
+      const int h = i / D, j = i & (D - 1);
+      float o = 0.f;
+      for (int w = gi * gw; w < (gi + 1) * gw; ++w) o += red_acc[(size_t)(w * kGMax + h) * D + j] * wfac[w][h];
+      P.part_o[(((size_t)upr * G + h) * S + usp) * D + j] = o;
+    }
+  }
+}
+
+// log2 of the units per work-group: as few as keep the grid within one
+// work-group per compute unit, with at most 8 query rows per work-group.
+int wide_group_log2(int64_t units, int G, int cus) {
+  int lg = 0;
+  while (lg < 3 && (G << (lg + 1)) <= kGMax && ((units + (1 << lg) - 1) >> lg) > (int64_t)cus) ++lg;
+  return lg;
+}
+
+}  // namespace
+
+bool wide_attend_supported(const AttendArgs &a) {
+  const int G = a.q_heads / a.kv_heads;
+  const bool fits = (int64_t)a.capacity * a.head_dim / 2 < (1ll << 31) &&
+                    (int64_t)a.batch * a.kv_heads * a.num_splits < (1ll << 30);
+  return a.head_dim == D && a.k_format == 4 && a.v_format == 4 && a.num_near_splits == 0 && G >= 1 &&
+         G <= kGMax && fits;
+}
+
+hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int G = a.q_heads / a.kv_heads;
+  const int64_t units = (int64_t)a.batch * a.kv_heads * a.num_splits;
+  const int lg = wide_group_log2(units, G, cus);
+  const int chunk = ((a.seq_len + a.num_splits - 1) / a.num_splits + kChunkTok - 1) / kChunkTok * kChunkTok;
+  WParams P{a.q, a.q_f16, a.kv_heads, a.capacity, a.seq_len, a.num_splits, G, chunk, lg, (int)units,
+            a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids, a.part_o, a.part_ml};
+  dim3 grid((unsigned)((units + (1 << lg) - 1) >> lg));
+  hipLaunchKernelGGL(attend_wide_kernel, grid, dim3(kBlock), 0, stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -52,6 +52,9 @@ hipError_t launch_attend_mfma(const AttendArgs &a, hipStream_t stream, bool *sup
 // Pair-table variant (4-bit keys and values, head_dim 128, no near tier, G <= 8).
 bool pair_attend_supported(const AttendArgs &a);
 hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream);
+// Pair-table variant for head_dim 256 (4-bit keys and values, no near tier, G <= 8).
+bool wide_attend_supported(const AttendArgs &a);
+hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream);
 
 // Split-merge launch (validated arguments).
 struct MergeArgs {

@@ -204,11 +204,12 @@ def test_mha_and_gqa2(dev):
         run_case(dev, wl)
 
 
-def test_distinct_value_codebook(dev):
+@pytest.mark.parametrize("d,kernel", [(128, "attend_pair_kernel"), (256, "attend_wide_kernel")])
+def test_distinct_value_codebook(dev, d, kernel):
     """Keys and values decoded through different codebooks (the value table
     replaced after the append by 1.2 times the Lloyd-Max centroids): the
     attention kernels must not assume one table for both."""
-    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, seq_len=300, splits=3)
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, head_dim=d, seq_len=300, splits=3)
     inp = W.generate(wl)
     d, T = wl.head_dim, wl.seq_len
     cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, d, T, _fmt(wl.k_bits), _fmt(wl.v_bits),
@@ -217,7 +218,7 @@ def test_distinct_value_codebook(dev):
     c, _ = O.codebook(wl.v_bits, d)
     cv = (1.2 * c.astype(np.float64)).astype(np.float32)
     cache.v_centroids.copy_(torch.from_numpy(cv).to(dev))
-    assert cache.attention_kernel(wl.q_heads) == "attend_pair_kernel"
+    assert cache.attention_kernel(wl.q_heads) == kernel
     q = _t(inp.q, dev)
     part_o, part_ml = cache.attend(q, T, wl.splits, 0)
     out = cache.merge(part_o, part_ml, wl.splits, 0)
@@ -230,6 +231,18 @@ def test_distinct_value_codebook(dev):
     v_rot = O.fp16_bits_to_f64(vn16.view(np.uint16))[..., None] * cv.astype(np.float64)[O.unpack(vp, wl.v_bits, d)]
     ref = O.attention(inp.q.astype(np.float64), k_rot, v_rot, _signs(d))
     _rows_close("distinct value codebook", out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("hq", [8, 16, 24, 64])
+def test_head_dim_256_unit_groups(dev, hq):
+    """Head dimension 256, 4-bit, G = 1, 2, 3, 8 query heads per KV head, with
+    512 (b * Hkv, split) units: more than the compute units, so a work-group
+    serves several units (for G <= 4), with ragged and empty splits (200
+    tokens in chunks of 32 over 8 splits) and every head checked."""
+    wl = W.WORKLOADS["bitwidth_sweep"].scaled(batch=8, q_heads=hq, kv_heads=8, seq_len=200, splits=8)
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, wl.seq_len, seed=W.SIGN_SEED, device=dev)
+    assert cache.attention_kernel(wl.q_heads) == "attend_wide_kernel"
+    run_case(dev, wl)
 
 
 def test_head_dim_64(dev):
