@@ -1,6 +1,7 @@
-// Split-K GQA decode attention on 4-bit Lloyd-Max keys and values, head
-// dimension 256: the pair-table matrix-core tile of the head-dimension-128
-// kernel (shared tile code), with twice the registers per tile.
+// Split-K GQA decode attention on 4-bit or 2-bit Lloyd-Max keys and values,
+// head dimension 256: the pair-table matrix-core tile of the head-dimension-
+// 128 kernel (shared tile code; quad-table entries for 2-bit codes), with
+// twice the registers per tile.
 //
 // Work mapping: a work-group of 8 waves (two per SIMD: the query operand and
 // the value accumulator take 128 registers at this head size) fills a
@@ -33,13 +34,9 @@ constexpr int D = 256;
 constexpr int kWaves = 8;
 constexpr int kMinWaves = 2;                   // waves per SIMD the register budget is sized for
 constexpr int kBlock = kWaves * 64;
-constexpr int kRow = D / 2;                     // packed bytes per 4-bit vector
 constexpr int kVDL = D / 16;                    // value coordinates per lane
 constexpr int kRowPad = D + 4;                  // query table row stride (words)
 constexpr int kZeroRow = 2 * kGMax;             // all-zero query row for the unused B columns
-// s_waitcnt vmcnt(8) expcnt(7) lgkmcnt(15): the eight loads of one tile
-constexpr int kWaitOlderTile = 0x0F70 | kTileLoads<D>;
-static_assert(kTileLoads<D> == 8, "tile loads");
 constexpr int kSetupWaves = 4;                  // waves that build the tables and the rotated queries
 
 struct WParams {
@@ -57,7 +54,97 @@ struct WParams {
   float *part_o, *part_ml;
 };
 
+// Pair tables (4-bit) or quad tables (2-bit) of the key codebook in the
+// first 64 KB of `tab` and, when the value codebook differs, of the value
+// codebook in the next 64 KB; run by the four set-up waves.  Thread t < 256
+// writes the 16-byte chunks t + 256k, k = 0..15: row (code byte)
+// t/16 + 16k, so the low four bits of the row, t/16 = 4 wave + lane/16, are
+// the same for every k and the high four bits are k.
+//   4-bit: a row holds 32 slots of (e(c[r % 16]), e(c[r / 16])), a chunk two
+//          slots;
+//   2-bit: a row holds 16 slots of (e(c[r & 3]), e(c[(r >> 2) & 3]),
+//          e(c[(r >> 4) & 3]), e(c[r >> 6])), a chunk one slot.
+// Centroids come through uniform addresses (scalar loads); per-wave parts are
+// chosen by a scalar switch so that constant indices keep them in SGPRs.
+template <int BITS>
+__device__ inline void fill_tables(uint8_t *tab, const float *kcen, const float *vcen, int wave, int lane, int tid,
+                                   uint32_t *v_table) {
+  constexpr int NC = 1 << BITS;
+  float ck[16], cv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ck[i] = (i < NC) ? kcen[i] : 0.f;
+    cv[i] = (i < NC) ? vcen[i] : 0.f;
+  }
+  bool same = true;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) same = same && (ck[i] == cv[i]);
+  const int r4 = lane >> 4;
+  // entries of the row's low four bits: code t/16 (4-bit) or codes r4 and
+  // wave (2-bit)
+  float lk[4], lv[4];
+  if constexpr (BITS == 4) {
+    switch (wave) {
+      case 0: pick<0, 1>(ck, cv, lk, lv); break;
+      case 1: pick<4, 1>(ck, cv, lk, lv); break;
+      case 2: pick<8, 1>(ck, cv, lk, lv); break;
+      default: pick<12, 1>(ck, cv, lk, lv); break;
+    }
+  } else {
+    pick<0, 1>(ck, cv, lk, lv);
+  }
+  float lo_k = lk[0], lo_v = lv[0];
+#pragma unroll
+  for (int u = 1; u < 4; ++u) {
+    lo_k = (r4 == u) ? lk[u] : lo_k;
+    lo_v = (r4 == u) ? lv[u] : lo_v;
+  }
+  const uint32_t lok = split_entry(lo_k * kCodeScale), lov = split_entry(lo_v * kCodeScale);
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t hi = split_entry(ck[k] * kCodeScale);
+      *reinterpret_cast<uint4_t *>(tab + (tid + 256 * k) * 16) = (uint4_t){lok, hi, lok, hi};
+    }
+    if (!same) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t hi = split_entry(cv[k] * kCodeScale);
+        *reinterpret_cast<uint4_t *>(tab + 65536 + (tid + 256 * k) * 16) = (uint4_t){lov, hi, lov, hi};
+      }
+    }
+  } else {
+    float wk, wv;
+    switch (wave) {
+      case 0: wk = ck[0]; wv = cv[0]; break;
+      case 1: wk = ck[1]; wv = cv[1]; break;
+      case 2: wk = ck[2]; wv = cv[2]; break;
+      default: wk = ck[3]; wv = cv[3]; break;
+    }
+    const uint32_t mk = split_entry(wk * kCodeScale), mv = split_entry(wv * kCodeScale);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t e2 = split_entry(ck[k & 3] * kCodeScale), e3 = split_entry(ck[k >> 2] * kCodeScale);
+      *reinterpret_cast<uint4_t *>(tab + (tid + 256 * k) * 16) = (uint4_t){lok, mk, e2, e3};
+    }
+    if (!same) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t e2 = split_entry(cv[k & 3] * kCodeScale), e3 = split_entry(cv[k >> 2] * kCodeScale);
+        *reinterpret_cast<uint4_t *>(tab + 65536 + (tid + 256 * k) * 16) = (uint4_t){lov, mv, e2, e3};
+      }
+    }
+  }
+  if (tid == 0) v_table[0] = same ? 0u : 0x10000u;
+}
+
+template <int BITS>
 __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams P) {
+  using TileT = Tile<D, BITS>;
+  constexpr int kRow = TileT::kRow;
+  // s_waitcnt vmcnt(loads of one tile) expcnt(7) lgkmcnt(15)
+  constexpr int kWaitOlderTile = 0x0F70 | kTileLoads<D, BITS>;
+  static_assert(kTileLoads<D, BITS> <= 15, "tile loads");
   // pair tables during the loop, the waves' value rows afterwards
   __shared__ __attribute__((aligned(16))) uint8_t tab[2 * 65536];
   __shared__ __attribute__((aligned(16))) uint32_t qtab[2 * kGMax + 1][kRowPad];
@@ -98,68 +185,22 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
   src.vn = P.v_norms + (size_t)pr * cap;
   src.code_bytes = cap * kRow;
   src.norm_bytes = cap * 2;
-  set_offsets<D>(src, g, n);
+  set_offsets<D, BITS>(src, g, n);
 
   // ---- set-up ----
-  // Waves 0-3 build the pair tables and the rotated queries; waves 4-7 first
+  // Waves 0-3 build the code tables and the rotated queries; waves 4-7 first
   // request their first two tiles (so the set-up waves' own requests do not
   // sit ahead of the table work in their issue queues).  Readiness is an LDS
   // count the set-up waves bump, not a barrier.
-  static_assert(kSetupWaves * 64 * 16 * 16 == 65536, "pair-table fill layout");
+  static_assert(kSetupWaves * 64 * 16 * 16 == 65536, "table fill layout");
   if (tid < kWaves) next_tile[tid] = 2 * gw;
   if (tid == 0) ready = 0u;
   __syncthreads();                                   // cheap here: no wave has memory requests yet
 
   int ia = gwave, ic = gwave + gw;                   // first tiles of this wave; later ones from its group's counter
-  Tile<D> ta, tc;
+  TileT ta, tc;
   if (wave < kSetupWaves) {
-    float ck[16], cv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ck[i] = P.k_centroids[i];
-      cv[i] = P.v_centroids[i];
-    }
-    bool same = true;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) same = same && (ck[i] == cv[i]);
-
-    // ---- pair tables: key table in the first 64 KB, value table in the next ----
-    // Row (code byte) r of a table holds 32 slots of the 8-byte entry
-    // (e(c[r % 16]), e(c[r / 16])).  Thread t < 256 writes the 16-byte
-    // chunks (two slots) t + 256k, k = 0..15: row t/16 + 16k, so low nibble
-    // t/16 = 4 wave + lane/16 for every k and high nibble k.
-    {
-      const int r4 = lane >> 4;
-      float lk[4], lv[4];
-      switch (wave) {
-        case 0: pick<0, 1>(ck, cv, lk, lv); break;
-        case 1: pick<4, 1>(ck, cv, lk, lv); break;
-        case 2: pick<8, 1>(ck, cv, lk, lv); break;
-        default: pick<12, 1>(ck, cv, lk, lv); break;
-      }
-      float lo_k = lk[0], lo_v = lv[0];
-#pragma unroll
-      for (int u = 1; u < 4; ++u) {
-        lo_k = (r4 == u) ? lk[u] : lo_k;
-        lo_v = (r4 == u) ? lv[u] : lo_v;
-      }
-      const uint32_t lok = split_entry(lo_k * kCodeScale), lov = split_entry(lo_v * kCodeScale);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t hi = split_entry(ck[k] * kCodeScale);
-        const uint4_t e = {lok, hi, lok, hi};
-        *reinterpret_cast<uint4_t *>(tab + (tid + 256 * k) * 16) = e;
-      }
-      if (!same) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const uint32_t hi = split_entry(cv[k] * kCodeScale);
-          const uint4_t e = {lov, hi, lov, hi};
-          *reinterpret_cast<uint4_t *>(tab + 65536 + (tid + 256 * k) * 16) = e;
-        }
-      }
-      if (tid == 0) v_table[0] = same ? 0u : 0x10000u;
-    }
+    fill_tables<BITS>(tab, P.k_centroids, P.v_centroids, wave, lane, tid, v_table);
     if (tid < D) qtab[kZeroRow][tid] = 0u;
 
     // ---- rotated queries: rows r = wave and wave + 4 (head r % G of the
@@ -220,9 +261,9 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
     if (lane == 0) __hip_atomic_fetch_add(&ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __builtin_amdgcn_sched_barrier(0);
-  load_tile<D>(ta, src, t0 + ia * kTile, ia >= ntiles);
+  load_tile<D, BITS>(ta, src, t0 + ia * kTile, ia >= ntiles);
   __builtin_amdgcn_sched_barrier(0);
-  load_tile<D>(tc, src, t0 + ic * kTile, ic >= ntiles);
+  load_tile<D, BITS>(tc, src, t0 + ic * kTile, ic >= ntiles);
   __builtin_amdgcn_sched_barrier(0);
 
   // Wait for the set-up counts (bounded: every set-up wave reaches its count
@@ -243,7 +284,9 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
 #pragma unroll
   for (int kb = 0; kb < D / 16; ++kb) bk[kb] = *reinterpret_cast<const uint4_t *>(&qtab[qrow][g * 64 + 4 * kb]);
   const float sfac = col ? qfac[grp * G + (n >> 1)] : 0.f;
-  const uint32_t kslot = (uint32_t)(lane & 31) * 8, vslot = kslot | v_table[0];
+  // table slot: lane % 32 of 8-byte pair entries, lane % 16 of 16-byte quad entries
+  const uint32_t kslot = (BITS == 4) ? (uint32_t)(lane & 31) * 8 : (uint32_t)(lane & 15) * 16;
+  const uint32_t vslot = kslot | v_table[0];
   float m1 = -1.f;
   asm volatile("" : "+s"(m1));                       // no instruction: keeps -1 from being folded
 
@@ -261,27 +304,27 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
     uint32_t nx = 0u;
     if (lane == 0) nx = atomicAdd(&next_tile[grp], 1u);
     __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-    process_tile<D, false>(ta, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
+    process_tile<D, BITS, false>(ta, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
     asm volatile("" : "+v"(nx));                     // keeps the read of the answer here
     const int na = __builtin_amdgcn_readfirstlane(nx);
-    load_tile<D>(ta, src, t0 + na * kTile, na >= ntiles);
+    load_tile<D, BITS>(ta, src, t0 + na * kTile, na >= ntiles);
     int nc = ntiles;
     if (ic < ntiles) {
       uint32_t ny = 0u;
       if (lane == 0) ny = atomicAdd(&next_tile[grp], 1u);
       __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-      process_tile<D, false>(tc, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run, l_run, m_top);
+      process_tile<D, BITS, false>(tc, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run, l_run, m_top);
       asm volatile("" : "+v"(ny));
       nc = __builtin_amdgcn_readfirstlane(ny);
     }
-    load_tile<D>(tc, src, t0 + nc * kTile, nc >= ntiles);
+    load_tile<D, BITS>(tc, src, t0 + nc * kTile, nc >= ntiles);
     ia = na;
     ic = nc;
   }
   // the last split's partial tile [t1f, t1)
   if (gwave == 0 && t1f < t1) {
-    load_tile<D>(ta, src, t1f, false);
-    process_tile<D, true>(ta, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
+    load_tile<D, BITS>(ta, src, t1f, false);
+    process_tile<D, BITS, true>(ta, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
   }
 
   // ---- wave epilogue: (m, l) per head to LDS; after the barrier (the
@@ -367,10 +410,10 @@ int wide_group_log2(int64_t units, int G, int cus) {
 
 bool wide_attend_supported(const AttendArgs &a) {
   const int G = a.q_heads / a.kv_heads;
-  const bool fits = (int64_t)a.capacity * a.head_dim / 2 < (1ll << 31) &&
+  const bool fits = (int64_t)a.capacity * a.head_dim * a.k_format / 8 < (1ll << 31) &&
                     (int64_t)a.batch * a.kv_heads * a.num_splits < (1ll << 30);
-  return a.head_dim == D && a.k_format == 4 && a.v_format == 4 && a.num_near_splits == 0 && G >= 1 &&
-         G <= kGMax && fits;
+  return a.head_dim == D && (a.k_format == 4 || a.k_format == 2) && a.v_format == a.k_format &&
+         a.num_near_splits == 0 && G >= 1 && G <= kGMax && fits;
 }
 
 hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream) {
@@ -384,7 +427,8 @@ hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream) {
   WParams P{a.q, a.q_f16, a.kv_heads, a.capacity, a.seq_len, a.num_splits, G, chunk, lg, (int)units,
             a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids, a.part_o, a.part_ml};
   dim3 grid((unsigned)((units + (1 << lg) - 1) >> lg));
-  hipLaunchKernelGGL(attend_wide_kernel, grid, dim3(kBlock), 0, stream, P);
+  if (a.k_format == 4) hipLaunchKernelGGL(attend_wide_kernel<4>, grid, dim3(kBlock), 0, stream, P);
+  else hipLaunchKernelGGL(attend_wide_kernel<2>, grid, dim3(kBlock), 0, stream, P);
   return hipGetLastError();
 }
 

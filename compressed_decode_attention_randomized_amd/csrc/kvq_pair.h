@@ -138,14 +138,16 @@ __device__ inline void split_pair(float w0, float w1, float m1, uint32_t &hp, ui
   lp = __builtin_bit_cast(uint32_t, l);
 }
 
-// Registers of one tile for head dimension D (128 or 256).
-template <int D>
+// Registers of one tile for head dimension D (128 or 256) and BITS-bit
+// codes (4, or 2 with quad entries: see quad_addr).
+template <int D, int BITS = 4>
 struct Tile {
-  static constexpr int kKeyWords = D / 32;     // key slice: token n, bytes [D/8 g, D/8 (g+1))
-  static constexpr int kValWords = D / 128;    // value words per token: bytes [D/32 n, D/32 (n+1))
+  static constexpr int kRow = D * BITS / 8;       // packed bytes per vector
+  static constexpr int kKeyWords = kRow / 16;     // key slice: token n, bytes [kRow/4 g, kRow/4 (g+1))
+  static constexpr int kValWords = kRow / 64;     // value words per token: bytes [kRow/16 n, kRow/16 (n+1))
   uint32_t kw[kKeyWords];
-  uint32_t vw[4][kValWords];                   // tokens 4g+i
-  uint2_t kn, vn;                              // fp16 norms of tokens 4g..4g+3
+  uint32_t vw[4][kValWords];                      // tokens 4g+i
+  uint2_t kn, vn;                                 // fp16 norms of tokens 4g..4g+3
 };
 
 // Per (b, KV head) cache slices; a tile's loads use a per-lane constant
@@ -158,37 +160,40 @@ struct Sources {
   uint32_t ko, vo, no;                 // per-lane offsets: key slice, value word, norm pair
 };
 
-template <int D>
+// Both code widths give lane (g, n) the key coordinates [D/4 g, D/4 (g+1))
+// of token n and the value coordinates [D/16 n, D/16 (n+1)) of tokens
+// 4g..4g+3.
+template <int D, int BITS = 4>
 __device__ inline void set_offsets(Sources &src, int g, int n) {
-  constexpr int kRow = D / 2;
-  src.ko = n * kRow + g * (D / 8);
-  src.vo = 4 * g * kRow + n * (D / 32);
+  constexpr int kRow = Tile<D, BITS>::kRow;
+  src.ko = n * kRow + g * (kRow / 4);
+  src.vo = 4 * g * kRow + n * (kRow / 16);
   src.no = 4 * g * 2;
 }
 
 // Loads of the tile at token tb.  A skipped tile reads through descriptors
 // of size zero, where buffer loads return zeros without touching memory, so
 // loads need no branch and a tile's wait sits at its first use.
-template <int D>
-__device__ inline void load_tile(Tile<D> &t, const Sources &src, int tb, bool skip) {
-  constexpr int kRow = D / 2;
+template <int D, int BITS = 4>
+__device__ inline void load_tile(Tile<D, BITS> &t, const Sources &src, int tb, bool skip) {
+  using T = Tile<D, BITS>;
   const __amdgpu_buffer_rsrc_t kc = make_rsrc(src.kc, skip ? 0u : src.code_bytes);
   const __amdgpu_buffer_rsrc_t vc = make_rsrc(src.vc, skip ? 0u : src.code_bytes);
   const __amdgpu_buffer_rsrc_t kn = make_rsrc(src.kn, skip ? 0u : src.norm_bytes);
   const __amdgpu_buffer_rsrc_t vn = make_rsrc(src.vn, skip ? 0u : src.norm_bytes);
-  const int cs = tb * kRow, ns = tb * 2;
+  const int cs = tb * T::kRow, ns = tb * 2;
 #pragma unroll
-  for (int i = 0; i < Tile<D>::kKeyWords / 4; ++i) {
+  for (int i = 0; i < T::kKeyWords / 4; ++i) {
     const uint4_t k = __builtin_amdgcn_raw_buffer_load_b128(kc, src.ko + 16 * i, cs, kStream);
 #pragma unroll
     for (int e = 0; e < 4; ++e) t.kw[4 * i + e] = k[e];
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if constexpr (Tile<D>::kValWords == 1) {
-      t.vw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(vc, src.vo + i * kRow, cs, kStream);
+    if constexpr (T::kValWords == 1) {
+      t.vw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(vc, src.vo + i * T::kRow, cs, kStream);
     } else {
-      const uint2_t v = __builtin_amdgcn_raw_buffer_load_b64(vc, src.vo + i * kRow, cs, kStream);
+      const uint2_t v = __builtin_amdgcn_raw_buffer_load_b64(vc, src.vo + i * T::kRow, cs, kStream);
       t.vw[i][0] = v.x;
       t.vw[i][1] = v.y;
     }
@@ -198,36 +203,102 @@ __device__ inline void load_tile(Tile<D> &t, const Sources &src, int tb, bool sk
 }
 
 // Buffer loads one tile issues (the s_waitcnt vmcnt that leaves one tile in flight).
-template <int D>
-constexpr int kTileLoads = Tile<D>::kKeyWords / 4 + 4 + 2;
+template <int D, int BITS = 4>
+constexpr int kTileLoads = Tile<D, BITS>::kKeyWords / 4 + 4 + 2;
 
-// Key block kb: coordinates 4kb..4kb+3 of the lane's slice = bytes 2kb, 2kb+1.
-template <int D, int KB = 0>
-__device__ inline void key_scores(const uint32_t (&kw)[D / 32], const uint4_t (&bk)[D / 16], const uint8_t *tab,
-                                  uint32_t slot8, float4_t &dk) {   // slot8: key slot register
+// 2-bit codes: a byte holds four codes, and the quad table maps it to
+// (e(c[b & 3]), e(c[(b >> 2) & 3]), e(c[(b >> 4) & 3]), e(c[b >> 6])), 16
+// bytes: one 128-bit LDS read gives a whole 8-half MFMA operand.  The table
+// is replicated over 16 lane slots (address = byte*256 + slot*16, slot =
+// lane % 16): an LDS cycle serves 16 lanes of a 128-bit read, which then use
+// all 64 banks.
+__device__ inline uint4_t quad_read(const uint8_t *tab, uint32_t addr) {
+  return *reinterpret_cast<const uint4_t *>(tab + addr);
+}
+
+// Key block kb: coordinates 4kb..4kb+3 of the lane's slice = bytes 2kb, 2kb+1
+// (4-bit) or byte kb (2-bit).
+template <int D, int BITS, int KB = 0>
+__device__ inline void key_scores(const uint32_t (&kw)[Tile<D, BITS>::kKeyWords], const uint4_t (&bk)[D / 16],
+                                  const uint8_t *tab, uint32_t slot, float4_t &dk) {   // slot: key slot register
   if constexpr (KB < D / 16) {
-    const uint32_t w = kw[KB / 2];
-    const uint2_t e0 = table_read(tab, pair_addr<2 * (KB % 2)>(w, slot8));
-    const uint2_t e1 = table_read(tab, pair_addr<2 * (KB % 2) + 1>(w, slot8));
-    dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(e0, e1), __builtin_bit_cast(half8_t, bk[KB]), dk, 0, 0, 0);
-    key_scores<D, KB + 1>(kw, bk, tab, slot8, dk);
+    half8_t a;
+    if constexpr (BITS == 4) {
+      const uint32_t w = kw[KB / 2];
+      const uint2_t e0 = table_read(tab, pair_addr<2 * (KB % 2)>(w, slot));
+      const uint2_t e1 = table_read(tab, pair_addr<2 * (KB % 2) + 1>(w, slot));
+      a = as_half8(e0, e1);
+    } else {
+      a = __builtin_bit_cast(half8_t, quad_read(tab, pair_addr<KB % 4>(kw[KB / 4], slot)));
+    }
+    dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8_t, bk[KB]), dk, 0, 0, 0);
+    key_scores<D, BITS, KB + 1>(kw, bk, tab, slot, dk);
   }
 }
 
-// Value coordinate tiles 8w + 2m (low nibbles) and 8w + 2m + 1 (high
-// nibbles) from byte m of word w of the token-pair bytes.
-template <int D, int M = 0>
-__device__ inline void value_update(const uint32_t (&ev)[D / 128][2], const uint32_t (&od)[D / 128][2],
-                                    const uint8_t *tab, uint32_t slot8, const half8_t &aw, float4_t (&dv)[D / 16]) {
-  if constexpr (M < D / 32) {
-    constexpr int W = M / 4, B = M % 4;
-    const uint2_t a0 = table_read(tab, pair_addr<B>(ev[W][0], slot8));
-    const uint2_t a1 = table_read(tab, pair_addr<B>(ev[W][1], slot8));
-    dv[2 * M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(a0, a1), dv[2 * M], 0, 0, 0);
-    const uint2_t b0 = table_read(tab, pair_addr<B>(od[W][0], slot8));
-    const uint2_t b1 = table_read(tab, pair_addr<B>(od[W][1], slot8));
-    dv[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(b0, b1), dv[2 * M + 1], 0, 0, 0);
-    value_update<D, M + 1>(ev, od, tab, slot8, aw, dv);
+// Value bytes of one coordinate across the lane group's tokens, and the
+// coordinate tiles they feed.
+//   4-bit: byte m of word w of ev[w][p] (od[w][p]) holds coordinate
+//          8w + 2m (8w + 2m + 1) of tokens 4g+2p (low nibble) and 4g+2p+1;
+//          two pair-table reads give the operand of tile 8w + 2m (+1).
+//   2-bit: byte j of x[r] holds coordinate 4j + r of tokens 4g..4g+3 (2 bits
+//          each, token 4g lowest); one quad-table read gives the operand of
+//          tile 4j + r.
+template <int D, int BITS>
+struct ValueBytes {
+  static constexpr int kWords = (BITS == 4) ? D / 128 : 1;
+  uint32_t ev[kWords][2], od[kWords][2];
+  uint32_t x[4];
+};
+
+template <int D, int BITS>
+__device__ inline void value_bytes(const Tile<D, BITS> &t, ValueBytes<D, BITS> &vb) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int w = 0; w < D / 128; ++w) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        vb.ev[w][p] = (t.vw[2 * p][w] & kNib) | ((t.vw[2 * p + 1][w] << 4) & ~kNib);
+        vb.od[w][p] = ((t.vw[2 * p][w] >> 4) & kNib) | (t.vw[2 * p + 1][w] & ~kNib);
+      }
+    }
+  } else {
+    static_assert(Tile<D, BITS>::kValWords == 1, "one value word per token");
+    constexpr uint32_t kCrumb = 0x33333333u;
+    // nibble k of a01: coordinate 2k of tokens 0 (bits 0-1) and 1 (bits
+    // 2-3); of b01: coordinate 2k+1; likewise a23, b23 for tokens 2, 3
+    const uint32_t w0 = t.vw[0][0], w1 = t.vw[1][0], w2 = t.vw[2][0], w3 = t.vw[3][0];
+    const uint32_t a01 = (w0 & kCrumb) | ((w1 << 2) & ~kCrumb), b01 = ((w0 >> 2) & kCrumb) | (w1 & ~kCrumb);
+    const uint32_t a23 = (w2 & kCrumb) | ((w3 << 2) & ~kCrumb), b23 = ((w2 >> 2) & kCrumb) | (w3 & ~kCrumb);
+    // byte j: coordinates 4j (x[0]), 4j+1 (x[1]), 4j+2 (x[2]), 4j+3 (x[3])
+    vb.x[0] = (a01 & kNib) | ((a23 << 4) & ~kNib);
+    vb.x[2] = ((a01 >> 4) & kNib) | (a23 & ~kNib);
+    vb.x[1] = (b01 & kNib) | ((b23 << 4) & ~kNib);
+    vb.x[3] = ((b01 >> 4) & kNib) | (b23 & ~kNib);
+  }
+}
+
+template <int D, int BITS, int M = 0>
+__device__ inline void value_update(const ValueBytes<D, BITS> &vb, const uint8_t *tab, uint32_t slot,
+                                    const half8_t &aw, float4_t (&dv)[D / 16]) {
+  if constexpr (BITS == 4) {
+    if constexpr (M < D / 32) {
+      constexpr int W = M / 4, B = M % 4;
+      const uint2_t a0 = table_read(tab, pair_addr<B>(vb.ev[W][0], slot));
+      const uint2_t a1 = table_read(tab, pair_addr<B>(vb.ev[W][1], slot));
+      dv[2 * M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(a0, a1), dv[2 * M], 0, 0, 0);
+      const uint2_t b0 = table_read(tab, pair_addr<B>(vb.od[W][0], slot));
+      const uint2_t b1 = table_read(tab, pair_addr<B>(vb.od[W][1], slot));
+      dv[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(b0, b1), dv[2 * M + 1], 0, 0, 0);
+      value_update<D, BITS, M + 1>(vb, tab, slot, aw, dv);
+    }
+  } else {
+    if constexpr (M < D / 16) {
+      constexpr int J = M / 4, R = M % 4;          // tile M = 4J + R
+      const uint4_t e = quad_read(tab, pair_addr<J>(vb.x[R], slot));
+      dv[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, e), dv[M], 0, 0, 0);
+      value_update<D, BITS, M + 1>(vb, tab, slot, aw, dv);
+    }
   }
 }
 
@@ -239,12 +310,12 @@ __device__ inline void value_update(const uint32_t (&ev)[D / 128][2], const uint
 // (one exponential per score), then they trade weight halves: A row 2h takes
 // the high fp16 parts of all four weights, row 2h+1 the low parts.  Both
 // lanes of a head keep the same softmax reference.
-template <int D, bool TAIL>
-__device__ inline void process_tile(const Tile<D> &t, const uint4_t (&bk)[D / 16], const uint8_t *tab, uint32_t kslot,
-                                    uint32_t vslot, float sfac, float m1, int tb, int t1, int g, int n,
+template <int D, int BITS, bool TAIL>
+__device__ inline void process_tile(const Tile<D, BITS> &t, const uint4_t (&bk)[D / 16], const uint8_t *tab,
+                                    uint32_t kslot, uint32_t vslot, float sfac, float m1, int tb, int t1, int g, int n,
                                     float4_t (&dv)[D / 16], float &m_run, float &l_run, float &m_top) {
   float4_t dk = {0.f, 0.f, 0.f, 0.f};
-  key_scores<D>(t.kw, bk, tab, kslot, dk);
+  key_scores<D, BITS>(t.kw, bk, tab, kslot, dk);
 
   const bool odd = n & 1;
   const uint32_t knp = odd ? t.kn.y : t.kn.x;        // fp16 norms of this lane's two tokens
@@ -279,17 +350,8 @@ __device__ inline void process_tile(const Tile<D> &t, const uint4_t (&bk)[D / 16
     }
   }
 
-  // value bytes of token pairs (4g, 4g+1) and (4g+2, 4g+3): even coordinates
-  // from the low nibbles, odd coordinates from the high nibbles
-  uint32_t ev[D / 128][2], od[D / 128][2];
-#pragma unroll
-  for (int w = 0; w < D / 128; ++w) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      ev[w][p] = (t.vw[2 * p][w] & kNib) | ((t.vw[2 * p + 1][w] << 4) & ~kNib);
-      od[w][p] = ((t.vw[2 * p][w] >> 4) & kNib) | (t.vw[2 * p + 1][w] & ~kNib);
-    }
-  }
+  ValueBytes<D, BITS> vb;
+  value_bytes<D, BITS>(t, vb);
 
   // weights w = exp2(s - m) * norm of the lane's two tokens, split as
   // w = hi + lo (fp16 each, about 22 bits together) into the packed pairs
@@ -310,7 +372,7 @@ __device__ inline void process_tile(const Tile<D> &t, const uint4_t (&bk)[D / 16
   const uint4_t a4 = {__builtin_amdgcn_perm(first, first, 0x01000100u), __builtin_amdgcn_perm(first, first, 0x03020302u),
                       __builtin_amdgcn_perm(second, second, 0x01000100u),
                       __builtin_amdgcn_perm(second, second, 0x03020302u)};
-  value_update<D>(ev, od, tab, vslot, __builtin_bit_cast(half8_t, a4), dv);
+  value_update<D, BITS>(vb, tab, vslot, __builtin_bit_cast(half8_t, a4), dv);
 }
 
 }  // namespace pair

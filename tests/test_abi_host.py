@@ -120,7 +120,7 @@ def test_attention_kernel_choice():
     assert name(hq=32) == "attend_kernel"                                # G=16: above the matrix-core limit
     assert name(head_dim=256) == "attend_wide_kernel"                     # 4-bit, d=256, G <= 8
     assert name(head_dim=256, hq=16) == "attend_wide_kernel"             # G=8
-    assert name(head_dim=256, k_format=2, v_format=2) == "attend_mfma_kernel"
+    assert name(head_dim=256, k_format=2, v_format=2) == "attend_wide_kernel"
     assert name(k_format=2, v_format=2) == "attend_mfma_kernel"
     assert name(k_format=3, v_format=3) == "attend_kernel"
     assert name(head_dim=64) == "attend_kernel"

@@ -204,12 +204,13 @@ def test_mha_and_gqa2(dev):
         run_case(dev, wl)
 
 
-@pytest.mark.parametrize("d,kernel", [(128, "attend_pair_kernel"), (256, "attend_wide_kernel")])
-def test_distinct_value_codebook(dev, d, kernel):
+@pytest.mark.parametrize("d,bits,kernel", [(128, 4, "attend_pair_kernel"), (256, 4, "attend_wide_kernel"),
+                                           (256, 2, "attend_wide_kernel")])
+def test_distinct_value_codebook(dev, d, bits, kernel):
     """Keys and values decoded through different codebooks (the value table
     replaced after the append by 1.2 times the Lloyd-Max centroids): the
     attention kernels must not assume one table for both."""
-    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, head_dim=d, seq_len=300, splits=3)
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, head_dim=d, seq_len=300, splits=3).with_bits(bits)
     inp = W.generate(wl)
     d, T = wl.head_dim, wl.seq_len
     cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, d, T, _fmt(wl.k_bits), _fmt(wl.v_bits),
@@ -233,14 +234,15 @@ def test_distinct_value_codebook(dev, d, kernel):
     _rows_close("distinct value codebook", out.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("hq", [8, 16, 24, 64])
-def test_head_dim_256_unit_groups(dev, hq):
-    """Head dimension 256, 4-bit, G = 1, 2, 3, 8 query heads per KV head, with
+@pytest.mark.parametrize("hq,bits", [(8, 4), (16, 4), (24, 4), (64, 4), (8, 2), (24, 2), (64, 2)])
+def test_head_dim_256_unit_groups(dev, hq, bits):
+    """Head dimension 256, 4- and 2-bit, G = 1, 2, 3, 8 query heads per KV head, with
     512 (b * Hkv, split) units: more than the compute units, so a work-group
     serves several units (for G <= 4), with ragged and empty splits (200
     tokens in chunks of 32 over 8 splits) and every head checked."""
-    wl = W.WORKLOADS["bitwidth_sweep"].scaled(batch=8, q_heads=hq, kv_heads=8, seq_len=200, splits=8)
-    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, wl.seq_len, seed=W.SIGN_SEED, device=dev)
+    wl = W.WORKLOADS["bitwidth_sweep"].scaled(batch=8, q_heads=hq, kv_heads=8, seq_len=200, splits=8).with_bits(bits)
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, wl.seq_len, _fmt(bits), _fmt(bits),
+                                 seed=W.SIGN_SEED, device=dev)
     assert cache.attention_kernel(wl.q_heads) == "attend_wide_kernel"
     run_case(dev, wl)
 
