@@ -87,7 +87,7 @@ def copy_probe(mib: int):
 def read_traffic(workload: str, kernel_sha: str):
     """HBM bytes per attention launch from the committed counter summary, or
     None if it is missing or was taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"attend_{workload}_hbm_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"attend_{workload.replace('@', '_')}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
