@@ -71,6 +71,31 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
+def copy_rate(mib: int = 1024, reps: int = 5) -> dict:
+    """Achievable HBM rate on this machine: a plain device-to-device copy of
+    `mib` MiB (torch's blit kernel), median of `reps` timed copies, as bytes
+    read plus bytes written per second."""
+    import torch
+    n = mib * 1024 * 1024
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+    t = float(np.median(ts))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_read": n, "bytes_written": n, "us": round(t * 1e6, 1), "GBps": round(2 * n / t / 1e9, 1)}
+
+
 def copy_probe(mib: int):
     import torch
     n = mib * 1024 * 1024
@@ -338,6 +363,7 @@ def main(argv=None) -> int:
                      "avg_us": round(att_avg * 1e3, 3),
                      "event_pair_avg_us": round(float(np.mean(att_ms)) * 1e3, 3),
                      "event_pair_min_us": round(min(att_ms) * 1e3, 3)},
+        "copy_probe": copy_rate(),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp)

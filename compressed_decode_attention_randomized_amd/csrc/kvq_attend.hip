@@ -224,35 +224,50 @@ struct NearTier {
   }
 };
 
-template <int G, int DPL, int LPT, typename Tier>
-__device__ void token_loop(Tier &tier, const float (&qr)[G][DPL], State<G, DPL> &st, int t0, int t1) {
+// Online softmax over tokens [t0, t1): each lane slot takes every TPB-th
+// token.  PIPE: the next block's rows are requested before this block's
+// arithmetic (two blocks of loads in flight per wave, at the cost of the
+// second block's registers).
+template <int G, int DPL, int LPT, bool PIPE, typename Tier>
+__device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G, DPL> &st, int t0, int t1) {
   constexpr int TPW = 64 / LPT;
   constexpr int TPB = TPW * kWaves;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ds = lane % LPT, ts = lane / LPT;
+  if (t0 >= t1) return;                       // empty split: no row to read
+  Tier cur = proto;
+  int t = t0 + wave * TPW + ts;
+  if constexpr (PIPE) cur.load(t < t1 ? t : t0, ds);
   for (int base = t0; base < t1; base += TPB) {
-    const int t = base + wave * TPW + ts;
     const bool valid = t < t1;
-    tier.load(valid ? t : t0, ds);
+    const int tn = t + TPB;
+    Tier nxt = proto;
+    if constexpr (PIPE) nxt.load(tn < t1 ? tn : t0, ds);
+    else cur.load(valid ? t : t0, ds);
     float part[G];
-    tier.score(qr, part);
+    cur.score(qr, part);
 #pragma unroll
     for (int m = 1; m < LPT; m <<= 1) {
 #pragma unroll
       for (int h = 0; h < G; ++h) part[h] += __shfl_xor(part[h], m);
     }
     float s[G], p[G];
-    const float ks = tier.key_scale();
+    const float ks = cur.key_scale();
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
     st.add_scores(s, p);
-    tier.accumulate(p, st);
+    cur.accumulate(p, st);
+    if constexpr (PIPE) cur = nxt;
+    t = tn;
   }
 }
 
 template <int D, int KB, int VB, int G>
 __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
-  constexpr int DPL = (G == 1) ? 32 : 16;
+  // G = 1: 32 coordinates per lane, except with fp8 keys (their near-tier
+  // fp16 rows would double the pipelined registers); loads pipelined
+  constexpr int DPL = (G == 1 && KB != 8) ? 32 : 16;
+  constexpr bool kPipe = (G == 1);
   constexpr int LPT = D / DPL;
   static_assert(LPT >= 1 && LPT <= 64, "lane mapping");
 
@@ -318,7 +333,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     const size_t base = (size_t)bh * P.near_len * D * 2;
     tier.krow0 = reinterpret_cast<const uint8_t *>(P.near_k) + base;
     tier.vrow0 = reinterpret_cast<const uint8_t *>(P.near_v) + base;
-    token_loop<G, DPL, LPT>(tier, qr, st, t0, t1);
+    token_loop<G, DPL, LPT, kPipe>(tier, qr, st, t0, t1);
   } else {
     const int fs = split - P.num_near_splits;
     const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + 31) / 32 * 32;
@@ -330,7 +345,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     tier.vn0 = P.v_norms + (size_t)bh * P.capacity;
     tier.lutk = lutk;
     tier.lutv = lutv;
-    token_loop<G, DPL, LPT>(tier, qr, st, t0, t1);
+    token_loop<G, DPL, LPT, kPipe>(tier, qr, st, t0, t1);
   }
 
   // ---- merge the lane slots of this wave, then the four waves ----
