@@ -11,8 +11,10 @@
 //      or log2(e)/d (far: rotation normalisation times the softmax scale);
 //   2. each token row is processed by D/DPL lanes, each lane owning DPL
 //      consecutive coordinates: the lane reads its slice of the packed key row
-//      (one vector load), looks each code up in an LDS centroid table and
-//      accumulates q~ . c[code] for the G heads; the slice sums are combined by
+//      (one vector load), looks its codes up in LDS (two 2- or 3-bit codes
+//      per read from a pair table, 4-bit codes one per read; fp8 keys are
+//      converted in hardware, two per instruction) and accumulates
+//      q~ . c[code] for the G heads; the slice sums are combined by
 //      xor-shuffles and multiplied by the fp16 norm;
 //   3. online softmax per lane slot in base 2 (one exp2 per score, the running
 //      state rescaled only when the maximum grows); values are accumulated in
@@ -23,7 +25,7 @@
 // Sources: "The Engineering Behind AdapTQ", "Engineering the Hot Path" (rotate
 // q once, score from codes through a table, no dequantize pass); "FoveatedKV",
 // "Making it fast" (fused split-K dispatch over both tiers, q pre-scaled,
-// online softmax with one exp per score, fp8 decode through a 256-entry table).
+// online softmax with one exp per score, fp8 keys for the far tier).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -92,15 +94,6 @@ __device__ inline float half_to_float(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-// OCP E4M3FN decode (for the LDS table): bias 7, subnormals m * 2^-9.
-__device__ inline float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float mag = (e == 0) ? (float)m * 0.001953125f
-                       : __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
-  if ((c & 0x7Fu) == 0x7Fu) mag = __builtin_nanf("");
-  return (c & 0x80u) ? -mag : mag;
-}
-
 // Running softmax state of one lane slot for G heads (base-2 logits).
 template <int G, int DPL>
 struct State {
@@ -150,14 +143,41 @@ struct State {
   }
 };
 
+// Codes 2p and 2p+1 (one 2B-bit field) of an LSB-first bit stream.
+template <int B>
+__device__ inline uint32_t pair_at(const uint32_t *w, int p) {
+  constexpr uint32_t kMask = (1u << (2 * B)) - 1u;
+  const int o = 2 * B * p, wi = o >> 5, sh = o & 31;
+  if (sh + 2 * B <= 32) return (w[wi] >> sh) & kMask;
+  return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & kMask;
+}
+
+// 2- and 3-bit codes are looked up two at a time: a pair table maps the
+// 2B-bit field f of two consecutive codes to (c[f & (2^B - 1)], c[f >> B]),
+// replicated over 32 lane slots (entry f of slot s at byte (32 f + s) * 8,
+// so the 32 lanes an LDS cycle serves never share a bank).
+template <int B>
+constexpr int pair_table_bytes() { return (B == 2 || B == 3) ? (1 << (2 * B)) * 32 * 8 : 0; }
+
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline float2_t pair_entry(const uint8_t *tab, uint32_t f, uint32_t slot8) {
+  return *reinterpret_cast<const float2_t *>(tab + ((f << 8) | slot8));
+}
+
 // Far tier: packed Lloyd-Max (KB in 2..4) or fp8 (KB = 8) keys, Lloyd-Max values.
+// fp8 keys decode in hardware (v_cvt_pk_f32_fp8: OCP E4M3FN, exact in fp32),
+// 2- and 3-bit codes through pair tables, 4-bit codes one table read each.
 template <int D, int KB, int VB, int G, int DPL>
 struct FarTier {
   static constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
   static constexpr int KNB = DPL * KB / 8, VNB = DPL * VB / 8;
+  static constexpr bool kKeyPairs = KB == 2 || KB == 3, kValPairs = VB == 2 || VB == 3;
   const uint8_t *krow0, *vrow0;
   const uint16_t *kn0, *vn0;
   const float *lutk, *lutv;
+  const uint8_t *pairk, *pairv;
+  uint32_t slot8;
   uint32_t kw[(KNB + 3) / 4], vw[(VNB + 3) / 4];
   float nk, nv;
 
@@ -170,11 +190,28 @@ struct FarTier {
   __device__ void score(const float (&qr)[G][DPL], float (&part)[G]) const {
 #pragma unroll
     for (int h = 0; h < G; ++h) part[h] = 0.f;
+    if constexpr (KB == 8) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      const float c = lutk[code_at<KB>(kw, e)];
+      for (int e = 0; e < DPL; e += 2) {
+        const float2_t c = (e & 2) ? __builtin_amdgcn_cvt_pk_f32_fp8((int)kw[e >> 2], true)
+                                   : __builtin_amdgcn_cvt_pk_f32_fp8((int)kw[e >> 2], false);
 #pragma unroll
-      for (int h = 0; h < G; ++h) part[h] = fmaf(qr[h][e], c, part[h]);
+        for (int h = 0; h < G; ++h) part[h] = fmaf(qr[h][e + 1], c.y, fmaf(qr[h][e], c.x, part[h]));
+      }
+    } else if constexpr (kKeyPairs) {
+#pragma unroll
+      for (int e = 0; e < DPL; e += 2) {
+        const float2_t c = pair_entry(pairk, pair_at<KB>(kw, e >> 1), slot8);
+#pragma unroll
+        for (int h = 0; h < G; ++h) part[h] = fmaf(qr[h][e + 1], c.y, fmaf(qr[h][e], c.x, part[h]));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const float c = lutk[code_at<KB>(kw, e)];
+#pragma unroll
+        for (int h = 0; h < G; ++h) part[h] = fmaf(qr[h][e], c, part[h]);
+      }
     }
   }
   __device__ float key_scale() const { return nk; }
@@ -182,11 +219,23 @@ struct FarTier {
     float w[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) w[h] = p[h] * nv;
+    if constexpr (kValPairs) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      const float c = lutv[code_at<VB>(vw, e)];
+      for (int e = 0; e < DPL; e += 2) {
+        const float2_t c = pair_entry(pairv, pair_at<VB>(vw, e >> 1), slot8);
 #pragma unroll
-      for (int h = 0; h < G; ++h) st.acc[h][e] = fmaf(w[h], c, st.acc[h][e]);
+        for (int h = 0; h < G; ++h) {
+          st.acc[h][e] = fmaf(w[h], c.x, st.acc[h][e]);
+          st.acc[h][e + 1] = fmaf(w[h], c.y, st.acc[h][e + 1]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const float c = lutv[code_at<VB>(vw, e)];
+#pragma unroll
+        for (int h = 0; h < G; ++h) st.acc[h][e] = fmaf(w[h], c, st.acc[h][e]);
+      }
     }
   }
 };
@@ -272,8 +321,10 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
   static_assert(LPT >= 1 && LPT <= 64, "lane mapping");
 
   __shared__ float qs[G][D];
-  __shared__ float lutk[KB == 8 ? 256 : 16];
+  constexpr int kPairK = pair_table_bytes<KB>(), kPairV = pair_table_bytes<VB>();
+  __shared__ float lutk[16];
   __shared__ float lutv[16];
+  __shared__ __attribute__((aligned(16))) uint8_t pairtab[(kPairK + kPairV) > 0 ? kPairK + kPairV : 16];
   __shared__ float red_ml[kWaves][G][2];
   __shared__ float red_acc[kWaves][G][D];
 
@@ -293,12 +344,23 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     qs[h][j] = v;
   }
   if (!near) {
-    if (KB == 8) {
-      for (int i = tid; i < 256; i += kBlock) lutk[i] = e4m3_value(i);
-    } else if (tid < (1 << KB)) {
-      lutk[tid] = P.k_centroids[tid];
-    }
+    if (KB != 8 && tid < (1 << KB)) lutk[tid] = P.k_centroids[tid];
     if (tid < (1 << VB)) lutv[tid] = P.v_centroids[tid];
+    // pair tables: entry (c[f & m], c[f >> B]) of field f in 32 slots
+    if constexpr (kPairK > 0) {
+      for (int i = tid; i < kPairK / 8; i += kBlock) {
+        const int f = i >> 5;
+        *reinterpret_cast<float2_t *>(pairtab + i * 8) =
+            (float2_t){P.k_centroids[f & ((1 << KB) - 1)], P.k_centroids[f >> KB]};
+      }
+    }
+    if constexpr (kPairV > 0) {
+      for (int i = tid; i < kPairV / 8; i += kBlock) {
+        const int f = i >> 5;
+        *reinterpret_cast<float2_t *>(pairtab + kPairK + i * 8) =
+            (float2_t){P.v_centroids[f & ((1 << VB) - 1)], P.v_centroids[f >> VB]};
+      }
+    }
   }
   __syncthreads();
   if (!near) {
@@ -345,6 +407,9 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     tier.vn0 = P.v_norms + (size_t)bh * P.capacity;
     tier.lutk = lutk;
     tier.lutv = lutv;
+    tier.pairk = pairtab;
+    tier.pairv = pairtab + kPairK;
+    tier.slot8 = (uint32_t)(tid & 31) * 8;
     token_loop<G, DPL, LPT, kPipe>(tier, qr, st, t0, t1);
   }
 
