@@ -284,8 +284,8 @@ __device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ds = lane % LPT, ts = lane / LPT;
   if (t0 >= t1) return;                       // empty split: no row to read
-  Tier cur = proto;
   int t = t0 + wave * TPW + ts;
+  Tier cur = proto;
   if constexpr (PIPE) cur.load(t < t1 ? t : t0, ds);
   for (int base = t0; base < t1; base += TPB) {
     const bool valid = t < t1;
@@ -311,11 +311,13 @@ __device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G
   }
 }
 
-template <int D, int KB, int VB, int G>
+// NEAR: the launch has near-tier splits (without them the kernel carries no
+// registers for the near path).
+template <int D, int KB, int VB, int G, bool NEAR>
 __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
-  // G = 1: 32 coordinates per lane, except with fp8 keys (their near-tier
-  // fp16 rows would double the pipelined registers); loads pipelined
-  constexpr int DPL = (G == 1 && KB != 8) ? 32 : 16;
+  // G = 1: 32 coordinates per lane, except where near-tier fp16 rows would
+  // double the pipelined registers; loads pipelined
+  constexpr int DPL = (G == 1 && !NEAR) ? 32 : 16;
   constexpr bool kPipe = (G == 1);
   constexpr int LPT = D / DPL;
   static_assert(LPT >= 1 && LPT <= 64, "lane mapping");
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / P.kv_heads, hkv = bh - b * P.kv_heads;
-  const bool near = split < P.num_near_splits;
+  const bool near = NEAR && split < P.num_near_splits;
   const int total_splits = P.num_near_splits + P.num_splits;
 
   // ---- query heads hkv*G .. hkv*G+G-1 into LDS, rotated for far splits ----
@@ -389,13 +391,15 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
   State<G, DPL> st;
   st.init();
   if (near) {
-    const int chunk = ((P.near_len + P.num_near_splits - 1) / P.num_near_splits + 31) / 32 * 32;
-    const int t0 = min(P.near_len, split * chunk), t1 = min(P.near_len, t0 + chunk);
-    NearTier<D, G, DPL> tier;
-    const size_t base = (size_t)bh * P.near_len * D * 2;
-    tier.krow0 = reinterpret_cast<const uint8_t *>(P.near_k) + base;
-    tier.vrow0 = reinterpret_cast<const uint8_t *>(P.near_v) + base;
-    token_loop<G, DPL, LPT, kPipe>(tier, qr, st, t0, t1);
+    if constexpr (NEAR) {
+      const int chunk = ((P.near_len + P.num_near_splits - 1) / P.num_near_splits + 31) / 32 * 32;
+      const int t0 = min(P.near_len, split * chunk), t1 = min(P.near_len, t0 + chunk);
+      NearTier<D, G, DPL> tier;
+      const size_t base = (size_t)bh * P.near_len * D * 2;
+      tier.krow0 = reinterpret_cast<const uint8_t *>(P.near_k) + base;
+      tier.vrow0 = reinterpret_cast<const uint8_t *>(P.near_v) + base;
+      token_loop<G, DPL, LPT, kPipe>(tier, qr, st, t0, t1);
+    }
   } else {
     const int fs = split - P.num_near_splits;
     const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + 31) / 32 * 32;
@@ -456,7 +460,8 @@ hipError_t go(const AttendArgs &a, hipStream_t stream) {
            a.near_len, a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids,
            a.near_k, a.near_v, a.part_o, a.part_ml};
   dim3 grid(a.num_near_splits + a.num_splits, a.batch * a.kv_heads);
-  hipLaunchKernelGGL((attend_kernel<D, KB, VB, G>), grid, dim3(kBlock), 0, stream, P);
+  if (a.num_near_splits > 0) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true>), grid, dim3(kBlock), 0, stream, P);
+  else hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false>), grid, dim3(kBlock), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -247,6 +247,14 @@ def test_head_dim_256_unit_groups(dev, hq, bits):
     run_case(dev, wl)
 
 
+@pytest.mark.parametrize("hq", [4, 8])
+def test_fp8_keys_without_near_tier(dev, hq):
+    """fp8 keys and 4-bit values with no near tier (far-only launch of the
+    two-tier formats), G = 1 and 2, ragged splits."""
+    wl = W.WORKLOADS["two_tier"].scaled(batch=2, q_heads=hq, kv_heads=4, seq_len=700, splits=3, near_fraction=0.0)
+    run_case(dev, wl)
+
+
 def test_head_dim_64(dev):
     wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, head_dim=64, seq_len=200, splits=3)
     run_case(dev, wl)
