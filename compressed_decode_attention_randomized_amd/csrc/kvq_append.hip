@@ -118,20 +118,24 @@ __device__ void encode(const Stream &st, const int8_t *__restrict__ signs, int n
   constexpr int L = 1 << (BITS == 8 ? 1 : BITS);
   constexpr int ROW = D * BITS / 8;
 
+  // the vector and sign loads go out before the midpoint table's barrier,
+  // so a one-token append waits for memory once
+  const int lv = threadIdx.x % LPV;
+  const int vec = blockIdx.x * VPB + threadIdx.x / LPV;
+  const bool live = vec < nvec;
+  double x[8];
+  uint2 sraw = make_uint2(0u, 0u);
+  if (live) {
+    load8<T>(static_cast<const T *>(st.in) + (size_t)vec * D + lv * 8, x);
+    sraw = *reinterpret_cast<const uint2 *>(signs + lv * 8);
+  }
   if (BITS != 8) {
     if (threadIdx.x < L - 1) {
       mids[threadIdx.x] = 0.5 * ((double)st.centroids[threadIdx.x] + (double)st.centroids[threadIdx.x + 1]);
     }
     __syncthreads();
   }
-
-  const int lv = threadIdx.x % LPV;
-  const int vec = blockIdx.x * VPB + threadIdx.x / LPV;
-  if (vec >= nvec) return;
-
-  const T *src = static_cast<const T *>(st.in) + (size_t)vec * D + lv * 8;
-  double x[8];
-  load8<T>(src, x);
+  if (!live) return;
 
   // squared norm from the original coordinates
   double ss = 0.0;
@@ -139,7 +143,6 @@ __device__ void encode(const Stream &st, const int8_t *__restrict__ signs, int n
   for (int e = 0; e < 8; ++e) ss = fma(x[e], x[e], ss);
 
   // sign flip
-  const uint2 sraw = *reinterpret_cast<const uint2 *>(signs + lv * 8);
   const uint32_t sw[2] = {sraw.x, sraw.y};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {

@@ -1,5 +1,5 @@
 // Split-merge kernel: one wave per (b, query head) row; the merge itself is
-// merge_row (shared with the attention kernels that merge in place).
+// merge_row.
 // Source: "FoveatedKV", "Making it fast" (split-K partial states merged after
 // the fused pass; near and far tiers share one softmax).
 #include <hip/hip_runtime.h>
