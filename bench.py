@@ -241,7 +241,7 @@ def main(argv=None) -> int:
     if wl.near_fraction:
         kn, vn = inp.tier("near")
         kf, vf = inp.tier("far")
-        near_splits = max(1, wl.splits // 8)
+        near_splits = wl.near_split_count
     else:
         kf, vf, kn, vn, near_splits = inp.k, inp.v, None, None, 0
     T = kf.shape[2]

@@ -459,7 +459,7 @@ hipError_t go(const AttendArgs &a, hipStream_t stream) {
   Params P{a.q, a.q_f16, a.kv_heads, a.q_heads, a.capacity, a.seq_len, a.num_splits, a.num_near_splits,
            a.near_len, a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids,
            a.near_k, a.near_v, a.part_o, a.part_ml};
-  dim3 grid(a.num_near_splits + a.num_splits, a.batch * a.kv_heads);
+  dim3 grid(a.near_only ? a.num_near_splits : a.num_near_splits + a.num_splits, a.batch * a.kv_heads);
   if (a.num_near_splits > 0) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true>), grid, dim3(kBlock), 0, stream, P);
   else hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false>), grid, dim3(kBlock), 0, stream, P);
   return hipGetLastError();
@@ -488,9 +488,35 @@ hipError_t by_format(const AttendArgs &a, hipStream_t stream, bool *ok) {
   return hipSuccess;
 }
 
+hipError_t launch_valu(const AttendArgs &a, hipStream_t stream, bool *supported) {
+  *supported = true;
+  switch (a.head_dim) {
+    case 64: return by_format<64>(a, stream, supported);
+    case 128: return by_format<128>(a, stream, supported);
+    case 256: return by_format<256>(a, stream, supported);
+  }
+  *supported = false;
+  return hipSuccess;
+}
+
+// The far tier of a cache with a near tier, as a launch of its own: no near
+// splits, partial rows starting at the first far split.
+AttendArgs far_part(const AttendArgs &a) {
+  AttendArgs f = a;
+  f.num_near_splits = 0;
+  f.near_len = 0;
+  f.near_k = f.near_v = nullptr;
+  return f;
+}
+
 }  // namespace
 
 const char *attend_kernel_name(const AttendArgs &a) {
+  if (a.num_near_splits > 0) {
+    const AttendArgs f = far_part(a);
+    if (pair_attend_supported(f)) return "attend_pair_kernel+attend_kernel";
+    if (wide_attend_supported(f)) return "attend_wide_kernel+attend_kernel";
+  }
   if (pair_attend_supported(a)) return "attend_pair_kernel";
   if (wide_attend_supported(a)) return "attend_wide_kernel";
   if (mfma_attend_supported(a)) return "attend_mfma_kernel";
@@ -498,6 +524,21 @@ const char *attend_kernel_name(const AttendArgs &a) {
 }
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported) {
+  // A near tier (fp16 rows, original domain) beside 4-bit or 2-bit far codes
+  // that a pair-table kernel covers: the near splits run on the VALU kernel
+  // and the far splits on the pair-table kernel, two launches on the stream
+  // writing disjoint partial rows.
+  if (a.num_near_splits > 0) {
+    const AttendArgs f = far_part(a);
+    const bool pair = pair_attend_supported(f), wide = !pair && wide_attend_supported(f);
+    if (pair || wide) {
+      AttendArgs n = a;
+      n.near_only = 1;
+      const hipError_t e = launch_valu(n, stream, supported);
+      if (e != hipSuccess || !*supported) return e;
+      return pair ? launch_attend_pair(f, stream, a.num_near_splits) : launch_attend_wide(f, stream, a.num_near_splits);
+    }
+  }
   if (pair_attend_supported(a)) {
     *supported = true;
     return launch_attend_pair(a, stream);
@@ -507,14 +548,7 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supporte
     return launch_attend_wide(a, stream);
   }
   if (mfma_attend_supported(a)) return launch_attend_mfma(a, stream, supported);
-  *supported = true;
-  switch (a.head_dim) {
-    case 64: return by_format<64>(a, stream, supported);
-    case 128: return by_format<128>(a, stream, supported);
-    case 256: return by_format<256>(a, stream, supported);
-  }
-  *supported = false;
-  return hipSuccess;
+  return launch_valu(a, stream, supported);
 }
 
 }  // namespace kvq

@@ -47,6 +47,7 @@ struct PParams {
   int group_size;                  // query heads per KV head
   int chunk;                       // tokens per split (a multiple of 32)
   int group_log2;                  // log2 of the splits one work-group covers (its wave groups)
+  int part_stride;                 // splits per (b, query head) row of the partial buffers
   const uint8_t *k_codes, *v_codes;
   const uint16_t *k_norms, *v_norms;
   const int8_t *signs;
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
     if (gw > 8) Mt = fmaxf(Mt, xor_lane<8>(Mt, lane));
     const int sp = (blockIdx.x << lg) + (w >> (4 - lg));
     if ((w & (gw - 1)) == 0 && h < G && sp < P.num_splits) {
-      const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * P.num_splits + sp;
+      const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * P.part_stride + sp;
       const bool any = L > 0.f;
       P.part_ml[row * 2 + 0] = any ? Mt * kLn2 : -INFINITY;
       P.part_ml[row * 2 + 1] = any ? L * exp2f(M - Mt) : 0.f;
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
       case 2: o = merge_rows<4>(red_acc, wfac, gi * 4, h, j); break;
       default: o = merge_rows<2>(red_acc, wfac, gi * 2, h, j); break;
     }
-    const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * P.num_splits + sp;
+    const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * P.part_stride + sp;
     P.part_o[row * D + j] = o;
   }
 }
@@ -392,7 +393,7 @@ bool pair_attend_supported(const AttendArgs &a) {
          G <= kGMax && fits;
 }
 
-hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream) {
+hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream, int part_base) {
   // One work-group fills a compute unit.  When the splits outnumber the
   // compute units, a work-group takes 2, 4 or 8 consecutive splits of one
   // (b, KV head) with a wave group each instead of running in several rounds.
@@ -404,7 +405,8 @@ hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream) {
   while (lg < 3 && pairs * ((a.num_splits + (1 << lg) - 1) >> lg) > (int64_t)cus) ++lg;
   const int chunk = ((a.seq_len + a.num_splits - 1) / a.num_splits + kChunkTok - 1) / kChunkTok * kChunkTok;
   PParams P{a.q, a.q_f16, a.kv_heads, a.q_heads, a.capacity, a.seq_len, a.num_splits, a.q_heads / a.kv_heads, chunk, lg,
-            a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids, a.part_o, a.part_ml};
+            part_base + a.num_splits, a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids,
+            a.part_o + (size_t)part_base * D, a.part_ml + (size_t)part_base * 2};
   dim3 grid((a.num_splits + (1 << lg) - 1) >> lg, a.kv_heads, a.batch);
   hipLaunchKernelGGL(attend_pair_kernel, grid, dim3(kBlock), 0, stream, P);
   return hipGetLastError();

@@ -47,6 +47,7 @@ struct WParams {
   int chunk;                       // tokens per split (a multiple of 32)
   int group_log2;                  // log2 of the units one work-group covers (its wave groups)
   int units;                       // (b, KV head) pairs times splits
+  int part_stride;                 // splits per (b, query head) row of the partial buffers
   const uint8_t *k_codes, *v_codes;
   const uint16_t *k_norms, *v_norms;
   const int8_t *signs;
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
     const int u = (blockIdx.x << lg) + (w >> (3 - lg));
     if ((w & (gw - 1)) == 0 && h < G && u < P.units) {
       const int upr = u / S, usp = u - upr * S;
-      const size_t row = ((size_t)upr * G + h) * S + usp;
+      const size_t row = ((size_t)upr * G + h) * P.part_stride + usp;
       const bool any = L > 0.f;
       P.part_ml[row * 2 + 0] = any ? Mt * kLn2 : -INFINITY;
       P.part_ml[row * 2 + 1] = any ? L * exp2f(M - Mt) : 0.f;
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
       const int h = i / D, j = i & (D - 1);
       float o = 0.f;
       for (int w = gi * gw; w < (gi + 1) * gw; ++w) o += red_acc[(size_t)(w * kGMax + h) * D + j] * wfac[w][h];
-      P.part_o[(((size_t)upr * G + h) * S + usp) * D + j] = o;
+      P.part_o[(((size_t)upr * G + h) * P.part_stride + usp) * D + j] = o;
     }
   }
 }
@@ -416,7 +417,7 @@ bool wide_attend_supported(const AttendArgs &a) {
          a.num_near_splits == 0 && G >= 1 && G <= kGMax && fits;
 }
 
-hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream) {
+hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream, int part_base) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
@@ -425,7 +426,8 @@ hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream) {
   const int lg = wide_group_log2(units, G, cus);
   const int chunk = ((a.seq_len + a.num_splits - 1) / a.num_splits + kChunkTok - 1) / kChunkTok * kChunkTok;
   WParams P{a.q, a.q_f16, a.kv_heads, a.capacity, a.seq_len, a.num_splits, G, chunk, lg, (int)units,
-            a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids, a.part_o, a.part_ml};
+            part_base + a.num_splits, a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids,
+            a.v_centroids, a.part_o + (size_t)part_base * D, a.part_ml + (size_t)part_base * 2};
   dim3 grid((unsigned)((units + (1 << lg) - 1) >> lg));
   if (a.k_format == 4) hipLaunchKernelGGL(attend_wide_kernel<4>, grid, dim3(kBlock), 0, stream, P);
   else hipLaunchKernelGGL(attend_wide_kernel<2>, grid, dim3(kBlock), 0, stream, P);

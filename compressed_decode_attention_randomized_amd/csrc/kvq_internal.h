@@ -42,19 +42,24 @@ struct AttendArgs {
   const float *k_centroids, *v_centroids;
   const uint16_t *near_k, *near_v;
   float *part_o, *part_ml;
+  int32_t near_only = 0;    // launch only the near-tier splits (the far ones go to another kernel)
 };
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported);
-// Name of the kernel launch_attend picks for these arguments.
+// Name of the kernel launch_attend picks for these arguments (for a cache
+// with a near tier whose far splits go to a pair-table kernel, the far
+// kernel's name followed by "+attend_kernel").
 const char *attend_kernel_name(const AttendArgs &a);
 // Matrix-core variant (Lloyd-Max 2/4-bit keys and values, no near tier, G <= 8).
 bool mfma_attend_supported(const AttendArgs &a);
 hipError_t launch_attend_mfma(const AttendArgs &a, hipStream_t stream, bool *supported);
 // Pair-table variant (4-bit keys and values, head_dim 128, no near tier, G <= 8).
+// part_base: far split 0 goes to partial row index part_base of rows that
+// hold part_base + num_splits splits (the near-tier splits come first).
 bool pair_attend_supported(const AttendArgs &a);
-hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream);
-// Pair-table variant for head_dim 256 (4-bit keys and values, no near tier, G <= 8).
+hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream, int part_base = 0);
+// Pair-table variant for head_dim 256 (2- or 4-bit keys and values, no near tier, G <= 8).
 bool wide_attend_supported(const AttendArgs &a);
-hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream);
+hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream, int part_base = 0);
 
 // Split-merge launch (validated arguments).
 struct MergeArgs {

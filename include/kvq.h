@@ -163,7 +163,10 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q
 
 /* Name of the attention kernel kvq_decode_attention launches for this cache,
  * query-head count and near-split count (for profiles and reports): a static
- * string, or NULL if the cache description is invalid. */
+ * string, or NULL if the cache description is invalid.  A cache with a near
+ * tier whose far codes a pair-table kernel covers is served by two launches
+ * on the stream (near splits, then far splits); the name is then
+ * "<far kernel>+attend_kernel". */
 const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads, int32_t num_near_splits);
 
 /* Split merge and the single inverse rotation ("Making it fast": split-K

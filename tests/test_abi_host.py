@@ -125,6 +125,10 @@ def test_attention_kernel_choice():
     assert name(k_format=3, v_format=3) == "attend_kernel"
     assert name(head_dim=64) == "attend_kernel"
     assert name(k_format=8, k_norms=0, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_kernel"
+    # 4-bit codes beside an fp16 near tier: near splits on the VALU kernel, far on a pair-table kernel
+    assert name(near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_pair_kernel+attend_kernel"
+    assert name(head_dim=256, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_wide_kernel+attend_kernel"
+    assert name(k_format=3, v_format=3, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_kernel"
     assert name(hq=3) is None and name(head_dim=96) is None
 
 

@@ -20,7 +20,7 @@ def dev():
     return torch.device("cuda")
 
 
-@pytest.mark.parametrize("name", ["llama7b_layer", "two_tier"])
+@pytest.mark.parametrize("name", ["llama7b_layer", "two_tier", "decode_buffer"])
 def test_decode_step_graph_replays_match_eager(dev, name):
     wl = W.WORKLOADS[name].scaled(batch=1, seq_len=700, splits=8)
     inp = W.generate(wl)

@@ -89,7 +89,7 @@ def run_case(dev, wl: W.Workload, splits=None, near_splits=None, inp=None, check
     if wl.near_fraction:
         kn, vn = inp.tier("near")
         kf, vf = inp.tier("far")
-        near_splits = near_splits or max(1, splits // 8)
+        near_splits = near_splits or wl.near_split_count
     else:
         kf, vf = inp.k, inp.v
         kn = vn = None
@@ -158,8 +158,8 @@ def _check_partials(wl, inp, po, pml, k_rot, v_rot, kn, vn, S, SN):
 
 
 # ---------------------------------------------------------------------------
-# the five workloads at sizes the oracle finishes in seconds (several tiles
-# per split and a ragged tail)
+# the five workloads and the decode buffer at sizes the oracle finishes in
+# seconds (several tiles per split and a ragged tail)
 # ---------------------------------------------------------------------------
 
 SMALL = {
@@ -168,10 +168,11 @@ SMALL = {
     "long_context": dict(seq_len=2111),
     "bitwidth_sweep": dict(batch=2, q_heads=4, kv_heads=4, seq_len=517),
     "two_tier": dict(batch=2, q_heads=4, kv_heads=4, seq_len=1303),
+    "decode_buffer": dict(batch=2, seq_len=1000),
 }
 
 
-@pytest.mark.parametrize("name", ["single_head_fp32", "llama7b_layer", "long_context", "two_tier"])
+@pytest.mark.parametrize("name", ["single_head_fp32", "llama7b_layer", "long_context", "two_tier", "decode_buffer"])
 def test_workload_small(dev, name):
     wl = W.WORKLOADS[name].scaled(**SMALL[name])
     run_case(dev, wl)
@@ -255,6 +256,44 @@ def test_fp8_keys_without_near_tier(dev, hq):
     run_case(dev, wl)
 
 
+@pytest.mark.parametrize("d,bits,hq,kernel", [(128, 4, 32, "attend_pair_kernel+attend_kernel"),
+                                              (128, 4, 8, "attend_pair_kernel+attend_kernel"),
+                                              (256, 4, 8, "attend_wide_kernel+attend_kernel"),
+                                              (256, 2, 8, "attend_wide_kernel+attend_kernel"),
+                                              (64, 4, 32, "attend_kernel")])
+def test_decode_buffer_shapes(dev, d, bits, hq, kernel):
+    """The 10% most recent tokens kept in fp16 beside 4- or 2-bit codes, at
+    three head sizes; with a pair-table kernel for the codes the near and far
+    splits are two launches writing one set of partial rows."""
+    wl = W.WORKLOADS["decode_buffer"].scaled(batch=2, q_heads=hq, head_dim=d, seq_len=613, splits=5,
+                                             near_fraction=0.1).with_bits(bits)
+    cache = kvq.KVCache.allocate(1, wl.kv_heads, d, 8, _fmt(bits), _fmt(bits), seed=W.SIGN_SEED, device=dev,
+                                 near_k=torch.zeros((1, wl.kv_heads, 4, d), dtype=torch.float16, device=dev),
+                                 near_v=torch.zeros((1, wl.kv_heads, 4, d), dtype=torch.float16, device=dev))
+    assert cache.attention_kernel(wl.q_heads, 2) == kernel
+    run_case(dev, wl, near_splits=2)
+
+
+@pytest.mark.parametrize("hq", [8, 32])
+def test_near_tier_only_is_fp16_attention(dev, hq):
+    """A short context kept entirely in fp16 (every token in the near tier, no
+    codes): the fused pass is plain attention over the fp16 rows in the
+    original domain."""
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=2, q_heads=hq, seq_len=300)
+    inp = W.generate(wl)
+    T, d = wl.seq_len, wl.head_dim
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, d, 1, seed=W.SIGN_SEED, device=dev,
+                                 near_k=_t(inp.k, dev), near_v=_t(inp.v, dev))
+    lse = torch.empty((wl.batch, wl.q_heads), dtype=torch.float32, device=dev)
+    out = cache.decode(_t(inp.q, dev), 0, 4, 3, lse=lse)
+    torch.cuda.synchronize()
+    empty = np.zeros((wl.batch, wl.kv_heads, 0, d))
+    ref, ref_lse = O.two_tier_attention(inp.q.astype(np.float64), inp.k.astype(np.float64), inp.v.astype(np.float64),
+                                        empty, empty, _signs(d), lse=True)
+    _rows_close("near tier only", out.cpu().numpy(), ref)
+    assert np.allclose(lse.cpu().numpy(), ref_lse, atol=2e-4, rtol=0)
+
+
 def test_head_dim_64(dev):
     wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, head_dim=64, seq_len=200, splits=3)
     run_case(dev, wl)
@@ -336,7 +375,7 @@ def _full_size(dev, name, bits=None, sample_heads=2):
     if wl.near_fraction:
         kn, vn = inp.tier("near")
         kf, vf = inp.tier("far")
-        SN = max(1, wl.splits // 8)
+        SN = wl.near_split_count
     else:
         kf, vf, kn, vn, SN = inp.k, inp.v, None, None, 0
     T = kf.shape[2]
@@ -374,7 +413,7 @@ def _full_size(dev, name, bits=None, sample_heads=2):
         _rows_close(f"{name} full b{b} hkv{hk}", out[b:b + 1, hk * G:(hk + 1) * G], ref)
 
 
-@pytest.mark.parametrize("name", ["single_head_fp32", "llama7b_layer", "long_context", "two_tier"])
+@pytest.mark.parametrize("name", ["single_head_fp32", "llama7b_layer", "long_context", "two_tier", "decode_buffer"])
 def test_full_size_sampled(dev, name):
     _full_size(dev, name)
 

@@ -5,7 +5,8 @@ method's arithmetic (no rotation, no norms, no codebook, no attention), so
 both sides of every parity test receive identical inputs without either side
 importing the other.
 
-Five workloads, named by what they are:
+Five workloads, named by what they are, and one more for the fp16 decode
+buffer:
 
   single_head_fp32   1 head, d=128, batch 1, context 1024, fp32 K/V ~N(0,1),
                      2 key channels scaled x20
@@ -21,6 +22,9 @@ Five workloads, named by what they are:
                      the near tier, chosen as the top 10% of a seeded random
                      per-token score; the rest is the far tier (fp8 keys,
                      4-bit values)
+  decode_buffer      llama7b_layer's shapes and draws; the 256 most recent
+                     tokens stay fp16 (near tier, original domain), the rest
+                     is 4-bit
 
 Recipe (all draws from numpy PCG64, ``default_rng(1000 + index)``):
   1. K drawn N(0,1) in float32, shape [B, Hkv, T, d]; then V the same.
@@ -34,6 +38,7 @@ Recipe (all draws from numpy PCG64, ``default_rng(1000 + index)``):
   6. two_tier only: a per-(b, h, t) uniform score is drawn last; the near tier
      is the floor(0.1*T) tokens with the highest score (ties to the lower
      index), in ascending token order; the far tier is the rest, in order.
+     decode_buffer draws no score: its near tier is the last 256 positions.
 """
 from __future__ import annotations
 
@@ -62,6 +67,10 @@ class Workload:
     outlier_scale: float = 1.0
     lognormal_sigma: float = 0.0
     near_fraction: float = 0.0
+    # near tier = the most recent near_len tokens (an fp16 decode buffer)
+    # instead of the seeded score mask
+    near_recent: bool = False
+    near_splits: int = 0   # near-tier split-K partitions (0: one per 8 far splits, at least 1)
 
     @property
     def group(self) -> int:
@@ -70,6 +79,12 @@ class Workload:
     @property
     def near_len(self) -> int:
         return int(np.floor(self.near_fraction * self.seq_len)) if self.near_fraction else 0
+
+    @property
+    def near_split_count(self) -> int:
+        if not self.near_fraction:
+            return 0
+        return self.near_splits or max(1, self.splits // 8)
 
     @property
     def far_len(self) -> int:
@@ -100,6 +115,12 @@ WORKLOADS = {
     "two_tier": Workload("two_tier", 5, batch=16, q_heads=16, kv_heads=16, head_dim=128,
                          seq_len=16384, k_bits=8, v_bits=4, dtype="f16", splits=8,
                          near_fraction=0.1),
+    # the llama7b_layer cache with its 256 most recent tokens kept in fp16 (a
+    # decode buffer scored in the same pass through the near-tier path)
+    "decode_buffer": Workload("decode_buffer", 6, batch=8, q_heads=32, kv_heads=8,
+                              head_dim=128, seq_len=8192, k_bits=4, v_bits=4, dtype="f16",
+                              splits=4, outlier_channels=4, outlier_scale=20.0,
+                              near_fraction=256 / 8192, near_recent=True, near_splits=4),
 }
 
 
@@ -142,7 +163,12 @@ def generate(wl: Workload, seed_offset: int = 0) -> Inputs:
     dt = _np_dtype(wl.dtype)
     out = Inputs(wl, k.astype(dt), v.astype(dt), q.astype(dt))
     del k, v
-    if wl.near_fraction:
+    if wl.near_fraction and wl.near_recent:
+        pos = np.arange(wl.seq_len, dtype=np.int64)
+        grid = (wl.batch, wl.kv_heads)
+        out.near_idx = np.broadcast_to(pos[wl.far_len:], grid + (wl.near_len,)).copy()
+        out.far_idx = np.broadcast_to(pos[:wl.far_len], grid + (wl.far_len,)).copy()
+    elif wl.near_fraction:
         score = rng.random((wl.batch, wl.kv_heads, wl.seq_len))
         order = np.argsort(-score, axis=-1, kind="stable")
         near = np.sort(order[..., : wl.near_len], axis=-1)
