@@ -556,3 +556,59 @@ def two_tier_attention(q, near_k, near_v, far_k_rot, far_v_rot, signs, lse: bool
     if lse:
         return o, (m + np.log(l))[..., 0]
     return o
+
+
+# Score gate and spike flags ([Foveated] "Making it fast": value loading is
+# skipped for a token whose score falls below exp(-16), i.e. whose weight is
+# below e^-16 of the reference; a far-tier token scoring above the near tier
+# is flagged for promotion).  Reading: the reference is given per (b, query
+# head) in natural-log score units (a previous step's log-sum-exp, say); a
+# gated token keeps its weight in the softmax sum and only its value is left
+# out; flags mark far tokens whose score exceeds a given threshold.
+GATE_LOG = 16.0
+
+
+def far_scores(q, far_k_rot, signs):
+    """s[b, h, t] = (R q_h) . khat_t / sqrt(d) for the far tier, natural-log units."""
+    B, Hq, d = q.shape
+    G = Hq // far_k_rot.shape[1]
+    fk = np.repeat(np.asarray(far_k_rot, np.float64), G, axis=1)
+    return np.einsum("bhd,bhtd->bht", rotate(q, signs), fk) / math.sqrt(d)
+
+
+def gated_two_tier_attention(q, near_k, near_v, far_k_rot, far_v_rot, signs, gate_ref, lse: bool = False):
+    """two_tier_attention with the score gate on the far tier: far token t's
+    value is left out of head h's sum when s[b,h,t] < gate_ref[b,h] - 16,
+    its weight still counting in the normaliser.  gate_ref: [B, Hq]."""
+    B, Hq, d = q.shape
+    G = Hq // far_k_rot.shape[1]
+    sf = far_scores(q, far_k_rot, signs)
+    keep = sf >= np.asarray(gate_ref, np.float64)[..., None] - GATE_LOG
+    q64 = np.asarray(q, np.float64)
+    nk = np.repeat(np.asarray(near_k, np.float64), G, axis=1)
+    nv = np.repeat(np.asarray(near_v, np.float64), G, axis=1)
+    fv = np.repeat(np.asarray(far_v_rot, np.float64), G, axis=1)
+    sn = np.einsum("bhd,bhtd->bht", q64, nk) / math.sqrt(d)
+    m = np.maximum(sn.max(axis=-1, initial=-np.inf), sf.max(axis=-1, initial=-np.inf))[..., None]
+    en, ef = np.exp(sn - m), np.exp(sf - m)
+    l = en.sum(axis=-1, keepdims=True) + ef.sum(axis=-1, keepdims=True)
+    o = np.einsum("bht,bhtd->bhd", en, nv) + rotate_inverse(np.einsum("bht,bhtd->bhd", ef * keep, fv), signs)
+    o = o / l
+    if lse:
+        return o, (m + np.log(l))[..., 0]
+    return o
+
+
+def spike_flags(q, far_k_rot, signs, spike_ref):
+    """bool [B, Hq, Tf]: far token t of head h scores above spike_ref[b, h]."""
+    return far_scores(q, far_k_rot, signs) > np.asarray(spike_ref, np.float64)[..., None]
+
+
+def pack_flags(flags):
+    """bool [..., T] -> uint32 [..., ceil(T/32)], token t at bit t % 32 of word t // 32."""
+    T = flags.shape[-1]
+    W = -(-T // 32)
+    pad = np.zeros(flags.shape[:-1] + (W * 32,), dtype=np.uint64)
+    pad[..., :T] = flags
+    bits = pad.reshape(flags.shape[:-1] + (W, 32)) << np.arange(32, dtype=np.uint64)
+    return bits.sum(axis=-1).astype(np.uint32)

@@ -155,3 +155,82 @@ def test_end_to_end_quality_report():
     oe = O.attention(q, O.rotate(k.astype(np.float64), s), O.rotate(v.astype(np.float64), s), s)
     cos = np.sum(oq * oe, -1) / np.linalg.norm(oq, axis=-1) / np.linalg.norm(oe, axis=-1)
     assert np.all(cos > 0.9)
+
+
+def _tiny_two_tier(seed, B=1, H=2, Tn=3, Tf=6, d=8, scale=4.0):
+    rng = np.random.default_rng(seed)
+    s = O.rademacher_signs(42, d)
+    nk = rng.standard_normal((B, H, Tn, d)).astype(np.float16).astype(np.float64)
+    nv = rng.standard_normal((B, H, Tn, d)).astype(np.float16).astype(np.float64)
+    fk = rng.standard_normal((B, H, Tf, d)) * scale
+    fv = rng.standard_normal((B, H, Tf, d))
+    q = rng.standard_normal((B, H, d)) * scale
+    return q, nk, nv, fk, fv, s
+
+
+def test_score_gate_limits():
+    """gate_ref = -inf gates nothing (the ungated pass); +inf gates every far
+    value, which equals the ungated pass with the far values zeroed and
+    leaves the log-sum-exp unchanged ([Foveated] "Making it fast")."""
+    q, nk, nv, fk, fv, s = _tiny_two_tier(21)
+    B, H = q.shape[:2]
+    ref, ref_lse = O.two_tier_attention(q, nk, nv, fk, fv, s, lse=True)
+    lo, lo_lse = O.gated_two_tier_attention(q, nk, nv, fk, fv, s, np.full((B, H), -np.inf), lse=True)
+    assert np.allclose(lo, ref, atol=1e-13) and np.allclose(lo_lse, ref_lse, atol=1e-13)
+    hi, hi_lse = O.gated_two_tier_attention(q, nk, nv, fk, fv, s, np.full((B, H), np.inf), lse=True)
+    zero, zero_lse = O.two_tier_attention(q, nk, nv, fk, np.zeros_like(fv), s, lse=True)
+    assert np.allclose(hi, zero, atol=1e-13) and np.allclose(hi_lse, ref_lse, atol=1e-13)
+
+
+def test_score_gate_brute_force():
+    """Tiny two-tier cases, scores spread wide: every head's output summed
+    token by token in plain Python loops, the far values of tokens scoring
+    below gate_ref - 16 left out of the numerator only."""
+    for seed in range(6):
+        q, nk, nv, fk, fv, s = _tiny_two_tier(30 + seed, scale=6.0)
+        B, H, d = q.shape
+        sf = O.far_scores(q, fk, s)
+        gate = sf.max(axis=-1) - 3.0 + seed          # a threshold inside the score range
+        gated = sf < gate[..., None] - 16.0
+        assert gated.any() and (~gated).any()
+        got = O.gated_two_tier_attention(q, nk, nv, fk, fv, s, gate)
+        H_ = O.hadamard(d)
+        for b in range(B):
+            for h in range(H):
+                qr = [sum(H_[i][j] * s[j] * q[b, h, j] for j in range(d)) / math.sqrt(d) for i in range(d)]
+                scores, vals, near = [], [], []
+                for t in range(nk.shape[2]):
+                    scores.append(sum(q[b, h, j] * nk[b, h, t, j] for j in range(d)) / math.sqrt(d))
+                    vals.append(list(nv[b, h, t])); near.append(True)
+                for t in range(fk.shape[2]):
+                    scores.append(sum(qr[j] * fk[b, h, t, j] for j in range(d)) / math.sqrt(d))
+                    vals.append(list(fv[b, h, t])); near.append(False)
+                m = max(scores)
+                w = [math.exp(x - m) for x in scores]
+                L = sum(w)
+                num_near = [sum(w[i] * vals[i][j] for i in range(len(w)) if near[i]) for j in range(d)]
+                num_far = [sum(w[i] * vals[i][j] for i in range(len(w))
+                               if not near[i] and scores[i] >= gate[b, h] - 16.0) for j in range(d)]
+                far_orig = [s[i] * sum(H_[i][j] * num_far[j] for j in range(d)) / math.sqrt(d) for i in range(d)]
+                want = [(num_near[j] + far_orig[j]) / L for j in range(d)]
+                assert np.allclose(got[b, h], want, atol=1e-12)
+
+
+def test_spike_flags_brute_force_and_packing():
+    """Flags equal a per-token comparison written out in loops; the packed
+    words put token t at bit t % 32 of word t // 32; with the threshold at the
+    k-th largest score exactly k - 1 tokens are flagged (distinct scores)."""
+    q, nk, nv, fk, fv, s = _tiny_two_tier(50, Tf=70, scale=3.0)
+    B, H, d = q.shape
+    sf = O.far_scores(q, fk, s)
+    ref = np.sort(sf, axis=-1)[..., -5]                    # the 5th largest
+    flags = O.spike_flags(q, fk, s, ref)
+    assert np.all(flags.sum(axis=-1) == 4)
+    words = O.pack_flags(flags)
+    assert words.shape == (B, H, 3) and words.dtype == np.uint32
+    for b in range(B):
+        for h in range(H):
+            for t in range(fk.shape[2]):
+                bit = (int(words[b, h, t // 32]) >> (t % 32)) & 1
+                assert bit == int(sf[b, h, t] > ref[b, h])
+    assert np.array_equal(O.pack_flags(np.array([True] + [False] * 31 + [True, True])), np.array([1, 3], np.uint32))
