@@ -21,7 +21,8 @@ KVQ_F32, KVQ_F16 = 0, 1
 KVQ_LM2, KVQ_LM3, KVQ_LM4, KVQ_FP8_E4M3 = 2, 3, 4, 8
 
 EXPORTED = ("kvq_row_bytes", "kvq_lloyd_max", "kvq_make_signs", "kvq_quantize_append",
-            "kvq_decode_attention", "kvq_decode_attention_kernel", "kvq_merge", "kvq_partials_floats",
+            "kvq_decode_attention", "kvq_decode_attention_gated", "kvq_decode_attention_kernel", "kvq_merge",
+            "kvq_partials_floats",
             "kvq_status_string", "kvq_last_error")
 
 
@@ -64,6 +65,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvq_make_signs": (I32, [U64, I32, P]),
         "kvq_quantize_append": (I32, [CP, P, P, I32, I32, I32, P]),
         "kvq_decode_attention": (I32, [CP, P, I32, I32, I32, I32, I32, P, P, P]),
+        "kvq_decode_attention_gated": (I32, [CP, P, I32, I32, I32, I32, I32, P, P, P, P, P, P]),
         "kvq_decode_attention_kernel": (ctypes.c_char_p, [CP, I32, I32]),
         "kvq_merge": (I32, [CP, P, P, I32, I32, I32, P, P, P]),
         "kvq_partials_floats": (SZ, [I32, I32, I32, I32]),
@@ -209,7 +211,11 @@ class KVCache:
         return (torch.empty((self.batch, q_heads, S, self.head_dim), dtype=torch.float32, device=dev),
                 torch.empty((self.batch, q_heads, S, 2), dtype=torch.float32, device=dev))
 
-    def attend(self, q, seq_len: int, num_splits: int, num_near_splits: int = 0, part_o=None, part_ml=None):
+    def attend(self, q, seq_len: int, num_splits: int, num_near_splits: int = 0, part_o=None, part_ml=None,
+               gate_ref=None, spike_ref=None, spike_bits=None):
+        """kvq_decode_attention, or kvq_decode_attention_gated when a gate or
+        spike reference ([B, Hq] float32) is given (spike_bits: [B, Hq,
+        ceil(seq_len/32)] int32, zeroed by the caller)."""
         q_heads = int(q.shape[1])
         _need(q, "q", (self.batch, q_heads, self.head_dim))
         if part_o is None:
@@ -218,9 +224,26 @@ class KVCache:
         _need(part_o, "part_o", (self.batch, q_heads, S, self.head_dim))
         _need(part_ml, "part_ml", (self.batch, q_heads, S, 2))
         cs = self.struct()
-        _check(load().kvq_decode_attention(ctypes.byref(cs), q.data_ptr(), _dtype_code(q), q_heads, seq_len,
-                                           num_splits, num_near_splits, part_o.data_ptr(), part_ml.data_ptr(),
-                                           _stream_handle(q.device)), "kvq_decode_attention")
+        if gate_ref is None and spike_ref is None:
+            _check(load().kvq_decode_attention(ctypes.byref(cs), q.data_ptr(), _dtype_code(q), q_heads, seq_len,
+                                               num_splits, num_near_splits, part_o.data_ptr(), part_ml.data_ptr(),
+                                               _stream_handle(q.device)), "kvq_decode_attention")
+            return part_o, part_ml
+        import torch
+        for name, ref in (("gate_ref", gate_ref), ("spike_ref", spike_ref)):
+            if ref is not None:
+                _need(ref, name, (self.batch, q_heads))
+                if ref.dtype != torch.float32:
+                    raise TypeError(f"{name} must be float32")
+        if spike_bits is not None:
+            _need(spike_bits, "spike_bits", (self.batch, q_heads, (seq_len + 31) // 32))
+            if spike_bits.dtype != torch.int32:
+                raise TypeError("spike_bits must be int32 (the bits of uint32 words)")
+        p = lambda t: 0 if t is None else t.data_ptr()
+        _check(load().kvq_decode_attention_gated(ctypes.byref(cs), q.data_ptr(), _dtype_code(q), q_heads, seq_len,
+                                                 num_splits, num_near_splits, p(gate_ref), p(spike_ref),
+                                                 p(spike_bits), part_o.data_ptr(), part_ml.data_ptr(),
+                                                 _stream_handle(q.device)), "kvq_decode_attention_gated")
         return part_o, part_ml
 
     # -- kvq_merge ------------------------------------------------------------

@@ -73,11 +73,12 @@ kvq_status kvq_quantize_append(const kvq_cache *cache, const void *k, const void
   return hip_status(e, fn);
 }
 
-kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q_dtype, int32_t q_heads,
-                                int32_t seq_len, int32_t num_splits, int32_t num_near_splits, float *part_o,
-                                float *part_ml, hipStream_t stream) {
-  const char *fn = "kvq_decode_attention";
-  kvq::clear_error();
+namespace {
+
+// Validation shared by the decode-attention calls; fills the launch arguments.
+kvq_status attend_args(const char *fn, const kvq_cache *cache, const void *q, int32_t q_dtype, int32_t q_heads,
+                       int32_t seq_len, int32_t num_splits, int32_t num_near_splits, float *part_o, float *part_ml,
+                       kvq::AttendArgs *out) {
   kvq_status st = check_cache(cache, fn);
   if (st != KVQ_OK) return st;
   if (!q || !part_o || !part_ml) return kvq::fail(KVQ_EINVAL, "%s: NULL q or partial buffer", fn);
@@ -98,17 +99,58 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q
     return kvq::fail(KVQ_EINVAL, "%s: the cache has a near tier; give it at least one split", fn);
   if ((int64_t)cache->batch * cache->kv_heads > 65535)
     return kvq::fail(KVQ_EINVAL, "%s: batch*kv_heads above 65535", fn);
-  kvq::AttendArgs a{q, q_dtype == KVQ_F16, cache->batch, cache->kv_heads, q_heads, cache->head_dim,
-                    cache->capacity, seq_len, num_splits, num_near_splits, cache->near_len, cache->k_format,
-                    cache->v_format, static_cast<const uint8_t *>(cache->k_codes),
-                    static_cast<const uint8_t *>(cache->v_codes), cache->k_norms, cache->v_norms, cache->signs,
-                    cache->k_centroids, cache->v_centroids, cache->near_k, cache->near_v, part_o, part_ml};
-  bool ok = true;
-  hipError_t e = kvq::launch_attend(a, stream, &ok);
+  *out = kvq::AttendArgs{q, q_dtype == KVQ_F16, cache->batch, cache->kv_heads, q_heads, cache->head_dim,
+                         cache->capacity, seq_len, num_splits, num_near_splits, cache->near_len, cache->k_format,
+                         cache->v_format, static_cast<const uint8_t *>(cache->k_codes),
+                         static_cast<const uint8_t *>(cache->v_codes), cache->k_norms, cache->v_norms, cache->signs,
+                         cache->k_centroids, cache->v_centroids, cache->near_k, cache->near_v, part_o, part_ml};
+  return KVQ_OK;
+}
+
+kvq_status attend_status(const char *fn, const kvq_cache *cache, int32_t q_heads, bool ok, hipError_t e) {
   if (!ok)
     return kvq::fail(KVQ_EUNSUPPORTED, "%s: group %d with formats (%d,%d) at head_dim %d not built", fn,
                      q_heads / cache->kv_heads, cache->k_format, cache->v_format, cache->head_dim);
   return hip_status(e, fn);
+}
+
+}  // namespace
+
+kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q_dtype, int32_t q_heads,
+                                int32_t seq_len, int32_t num_splits, int32_t num_near_splits, float *part_o,
+                                float *part_ml, hipStream_t stream) {
+  const char *fn = "kvq_decode_attention";
+  kvq::clear_error();
+  kvq::AttendArgs a;
+  const kvq_status st = attend_args(fn, cache, q, q_dtype, q_heads, seq_len, num_splits, num_near_splits, part_o,
+                                    part_ml, &a);
+  if (st != KVQ_OK) return st;
+  bool ok = true;
+  const hipError_t e = kvq::launch_attend(a, stream, &ok);
+  return attend_status(fn, cache, q_heads, ok, e);
+}
+
+kvq_status kvq_decode_attention_gated(const kvq_cache *cache, const void *q, int32_t q_dtype, int32_t q_heads,
+                                      int32_t seq_len, int32_t num_splits, int32_t num_near_splits,
+                                      const float *gate_ref, const float *spike_ref, uint32_t *spike_bits,
+                                      float *part_o, float *part_ml, hipStream_t stream) {
+  const char *fn = "kvq_decode_attention_gated";
+  kvq::clear_error();
+  kvq::AttendArgs a;
+  const kvq_status st = attend_args(fn, cache, q, q_dtype, q_heads, seq_len, num_splits, num_near_splits, part_o,
+                                    part_ml, &a);
+  if (st != KVQ_OK) return st;
+  if (!gate_ref && !spike_ref) return kvq::fail(KVQ_EINVAL, "%s: neither gate_ref nor spike_ref given", fn);
+  if ((spike_ref == nullptr) != (spike_bits == nullptr))
+    return kvq::fail(KVQ_EINVAL, "%s: spike_ref and spike_bits go together", fn);
+  if (!aligned(gate_ref, 4) || !aligned(spike_ref, 4) || !aligned(spike_bits, 4))
+    return kvq::fail(KVQ_EINVAL, "%s: references and flag words must be 4-byte aligned", fn);
+  a.gate_ref = gate_ref;
+  a.spike_ref = spike_ref;
+  a.spike_bits = spike_bits;
+  bool ok = true;
+  const hipError_t e = kvq::launch_attend_gated(a, stream, &ok);
+  return attend_status(fn, cache, q_heads, ok, e);
 }
 
 const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads, int32_t num_near_splits) {

@@ -50,6 +50,18 @@ struct Params {
   const float *k_centroids, *v_centroids;
   const uint16_t *near_k, *near_v;
   float *part_o, *part_ml;
+  const float *gate_ref, *spike_ref;   // [B][Hq] natural-log references or NULL (gated launches)
+  uint32_t *spike_bits;                // [B][Hq][spike_words]
+  int spike_words;
+};
+
+// Score gate and spike flags of the far tier for one block of tokens, the G
+// heads of one KV head (log2 score units, as the kernel keeps them).
+template <int G>
+struct FarGate {
+  float gate[G], spike[G];              // thresholds: -inf gate / +inf spike when not asked for
+  uint32_t *bits;                       // this (b, KV head)'s first head row of flag words, or NULL
+  int words;
 };
 
 // Loads NB bytes (NB a multiple of 2) at p into 32-bit words, using the widest
@@ -173,6 +185,7 @@ struct FarTier {
   static constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
   static constexpr int KNB = DPL * KB / 8, VNB = DPL * VB / 8;
   static constexpr bool kKeyPairs = KB == 2 || KB == 3, kValPairs = VB == 2 || VB == 3;
+  static constexpr bool kFar = true;
   const uint8_t *krow0, *vrow0;
   const uint16_t *kn0, *vn0;
   const float *lutk, *lutv;
@@ -243,6 +256,7 @@ struct FarTier {
 // Near tier: exact fp16 rows in the original domain.
 template <int D, int G, int DPL>
 struct NearTier {
+  static constexpr bool kFar = false;
   static constexpr int NB = DPL * 2;
   const uint8_t *krow0, *vrow0;
   uint32_t kw[NB / 4], vw[NB / 4];
@@ -277,8 +291,16 @@ struct NearTier {
 // token.  PIPE: the next block's rows are requested before this block's
 // arithmetic (two blocks of loads in flight per wave, at the cost of the
 // second block's registers).
-template <int G, int DPL, int LPT, bool PIPE, typename Tier>
-__device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G, DPL> &st, int t0, int t1) {
+//
+// GATED (far tier): a token whose score is below fg.gate[h] keeps its weight
+// in the sum l but adds nothing to head h's values (the value decode is
+// skipped when every head gates it), and the wave's flags of tokens scoring
+// above fg.spike[h] are or-ed into head h's flag words (a wave's TPW
+// consecutive tokens never straddle a 32-token word: blocks start at
+// multiples of 32).
+template <int G, int DPL, int LPT, bool PIPE, bool GATED = false, typename Tier>
+__device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G, DPL> &st, int t0, int t1,
+                           const FarGate<G> *fg = nullptr) {
   constexpr int TPW = 64 / LPT;
   constexpr int TPB = TPW * kWaves;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -304,8 +326,33 @@ __device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G
     const float ks = cur.key_scale();
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
+    if constexpr (GATED && Tier::kFar) {
+      if (fg->bits) {
+        const int tw = t - ts;                     // the wave's first token of the block
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const uint64_t ball = __builtin_amdgcn_ballot_w64(ds == 0 && s[h] > fg->spike[h]);
+          uint32_t m = 0u;
+#pragma unroll
+          for (int k = 0; k < TPW; ++k) m |= (uint32_t)((ball >> (k * LPT)) & 1ull) << k;
+          if (m != 0u && lane == 0)
+            atomicOr(fg->bits + (size_t)h * fg->words + (tw >> 5), m << (tw & 31));
+        }
+      }
+    }
     st.add_scores(s, p);
-    cur.accumulate(p, st);
+    if constexpr (GATED && Tier::kFar) {
+      bool any = false;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const bool keep = s[h] >= fg->gate[h];
+        p[h] = keep ? p[h] : 0.f;
+        any = any || keep;
+      }
+      if (any) cur.accumulate(p, st);
+    } else {
+      cur.accumulate(p, st);
+    }
     if constexpr (PIPE) cur = nxt;
     t = tn;
   }
@@ -313,7 +360,7 @@ __device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G
 
 // NEAR: the launch has near-tier splits (without them the kernel carries no
 // registers for the near path).
-template <int D, int KB, int VB, int G, bool NEAR>
+template <int D, int KB, int VB, int G, bool NEAR, bool GATED>
 __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
   // G = 1: 32 coordinates per lane, except where near-tier fp16 rows would
   // double the pipelined registers; loads pipelined
@@ -414,7 +461,21 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     tier.pairk = pairtab;
     tier.pairv = pairtab + kPairK;
     tier.slot8 = (uint32_t)(tid & 31) * 8;
-    token_loop<G, DPL, LPT, kPipe>(tier, qr, st, t0, t1);
+    if constexpr (GATED) {
+      constexpr float kGate2 = 16.f * kLog2e;     // e^-16 in log2 units
+      FarGate<G> fg;
+      const size_t row0 = (size_t)b * P.q_heads + (size_t)hkv * G;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        fg.gate[h] = P.gate_ref ? P.gate_ref[row0 + h] * kLog2e - kGate2 : -INFINITY;
+        fg.spike[h] = P.spike_ref ? P.spike_ref[row0 + h] * kLog2e : INFINITY;
+      }
+      fg.bits = P.spike_ref ? P.spike_bits + row0 * P.spike_words : nullptr;
+      fg.words = P.spike_words;
+      token_loop<G, DPL, LPT, kPipe, true>(tier, qr, st, t0, t1, &fg);
+    } else {
+      token_loop<G, DPL, LPT, kPipe>(tier, qr, st, t0, t1);
+    }
   }
 
   // ---- merge the lane slots of this wave, then the four waves ----
@@ -458,10 +519,13 @@ template <int D, int KB, int VB, int G>
 hipError_t go(const AttendArgs &a, hipStream_t stream) {
   Params P{a.q, a.q_f16, a.kv_heads, a.q_heads, a.capacity, a.seq_len, a.num_splits, a.num_near_splits,
            a.near_len, a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids,
-           a.near_k, a.near_v, a.part_o, a.part_ml};
+           a.near_k, a.near_v, a.part_o, a.part_ml, a.gate_ref, a.spike_ref, a.spike_bits, (a.seq_len + 31) / 32};
   dim3 grid(a.near_only ? a.num_near_splits : a.num_near_splits + a.num_splits, a.batch * a.kv_heads);
-  if (a.num_near_splits > 0) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true>), grid, dim3(kBlock), 0, stream, P);
-  else hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false>), grid, dim3(kBlock), 0, stream, P);
+  const bool near = a.num_near_splits > 0, gated = a.gated != 0;
+  if (near && gated) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true, true>), grid, dim3(kBlock), 0, stream, P);
+  else if (near) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true, false>), grid, dim3(kBlock), 0, stream, P);
+  else if (gated) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false, true>), grid, dim3(kBlock), 0, stream, P);
+  else hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false, false>), grid, dim3(kBlock), 0, stream, P);
   return hipGetLastError();
 }
 
@@ -521,6 +585,12 @@ const char *attend_kernel_name(const AttendArgs &a) {
   if (wide_attend_supported(a)) return "attend_wide_kernel";
   if (mfma_attend_supported(a)) return "attend_mfma_kernel";
   return "attend_kernel";
+}
+
+hipError_t launch_attend_gated(const AttendArgs &a, hipStream_t stream, bool *supported) {
+  AttendArgs g = a;
+  g.gated = 1;
+  return launch_valu(g, stream, supported);
 }
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported) {

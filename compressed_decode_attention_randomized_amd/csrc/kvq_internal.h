@@ -43,8 +43,14 @@ struct AttendArgs {
   const uint16_t *near_k, *near_v;
   float *part_o, *part_ml;
   int32_t near_only = 0;    // launch only the near-tier splits (the far ones go to another kernel)
+  int32_t gated = 0;        // score gate / spike flags (VALU kernel only)
+  const float *gate_ref = nullptr, *spike_ref = nullptr;
+  uint32_t *spike_bits = nullptr;
 };
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported);
+// Score-gated attention with spike flags (a.gate_ref / a.spike_ref / a.spike_bits):
+// always the VALU kernel.
+hipError_t launch_attend_gated(const AttendArgs &a, hipStream_t stream, bool *supported);
 // Name of the kernel launch_attend picks for these arguments (for a cache
 // with a near tier whose far splits go to a pair-table kernel, the far
 // kernel's name followed by "+attend_kernel").

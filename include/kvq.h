@@ -161,6 +161,32 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q
                                 int32_t num_near_splits, float *part_o, float *part_ml,
                                 hipStream_t stream);
 
+/* kvq_decode_attention with the far tier's score gate and spike flags
+ * ("FoveatedKV", "Making it fast": value loading skipped for a token whose
+ * score falls below e^-16 of the reference; far-tier tokens that outscore the
+ * near tier detected during the softmax).  Same arguments, layout and
+ * partial outputs as kvq_decode_attention, plus:
+ *   gate_ref    device float [batch][q_heads] or NULL: far token t adds
+ *               nothing to head h's values when s_t < gate_ref[b][h] - 16
+ *               (natural-log score units, those of part_ml's m; a previous
+ *               step's log-sum-exp is a natural reference); its weight still
+ *               counts in l.  Near-tier tokens are never gated.
+ *   spike_ref   device float [batch][q_heads] or NULL: bit t % 32 of
+ *               spike_bits[b][h][t / 32] is or-ed to 1 when far token
+ *               t < seq_len scores s_t > spike_ref[b][h];
+ *   spike_bits  device uint32 [batch][q_heads][ceil(seq_len / 32)], zeroed by
+ *               the caller before the call (bits are or-ed in); required
+ *               exactly when spike_ref is given.
+ * At least one of gate_ref and spike_ref must be given.  All three are
+ * caller-owned and 4-byte aligned.  Served by the VALU kernel for every
+ * format (query groups G = 1, 2, 4; 3-bit codes at G = 1).  Errors as
+ * kvq_decode_attention, and KVQ_EINVAL for a missing or unpaired reference. */
+kvq_status kvq_decode_attention_gated(const kvq_cache *cache, const void *q, int32_t q_dtype,
+                                      int32_t q_heads, int32_t seq_len, int32_t num_splits,
+                                      int32_t num_near_splits, const float *gate_ref,
+                                      const float *spike_ref, uint32_t *spike_bits, float *part_o,
+                                      float *part_ml, hipStream_t stream);
+
 /* Name of the attention kernel kvq_decode_attention launches for this cache,
  * query-head count and near-split count (for profiles and reports): a static
  * string, or NULL if the cache description is invalid.  A cache with a near

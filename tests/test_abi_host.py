@@ -71,6 +71,23 @@ def _attend(cs, q=0x8000, qd=1, hq=4, T=8, S=2, SN=0, po=0xA000, pml=0xB000):
                                            po, pml, None)
 
 
+def _gated(cs, gate=0xE000, spike=0, bits=0, T=8, **kw):
+    return kvq.load().kvq_decode_attention_gated(ctypes.byref(cs), 0x8000, 1, 4, T, 2, 0, gate, spike, bits,
+                                                 0xA000, 0xB000, None)
+
+
+def test_gated_attention_validation():
+    """The gated call's own argument checks (host only: every case fails
+    before a launch)."""
+    cs = _fake_cache()
+    assert _gated(cs, gate=0, spike=0) == kvq.KVQ_EINVAL                   # neither reference
+    assert _gated(cs, gate=0, spike=0xE000, bits=0) == kvq.KVQ_EINVAL      # spike_ref without flag words
+    assert _gated(cs, gate=0xE000, spike=0, bits=0xF000) == kvq.KVQ_EINVAL # flag words without spike_ref
+    assert _gated(cs, gate=0xE002) == kvq.KVQ_EINVAL                       # misaligned reference
+    assert _gated(cs, gate=0, spike=0xE000, bits=0xF001) == kvq.KVQ_EINVAL # misaligned flag words
+    assert _gated(cs, T=1000) == kvq.KVQ_ERANGE                             # the plain call's checks come first
+
+
 def test_append_validation():
     assert _append(None) == kvq.KVQ_EINVAL
     assert _append(_fake_cache(), start=60, n=5) == kvq.KVQ_ERANGE

@@ -294,6 +294,80 @@ def test_near_tier_only_is_fp16_attention(dev, hq):
     assert np.allclose(lse.cpu().numpy(), ref_lse, atol=2e-4, rtol=0)
 
 
+@pytest.mark.parametrize("name,hq,kv,d", [("two_tier", 4, 4, 128), ("two_tier", 8, 4, 128),
+                                         ("llama7b_layer", 8, 2, 128), ("bitwidth_sweep@b3", 4, 4, 256),
+                                         ("bitwidth_sweep@b2", 8, 2, 64)])
+def test_score_gate_and_spike_flags(dev, name, hq, kv, d):
+    """Score-gated attention and spike flags against the oracle, on a peaked
+    query (x 8: far scores spread over tens of units, so the gate at the
+    row's largest score drops a large share of the far values and the
+    flags at the 75th percentile mark a quarter of the far tokens).  Flags
+    are compared bit for bit except within 1e-3 of the threshold."""
+    base, _, bits = name.partition("@b")
+    wl = W.WORKLOADS[base].scaled(batch=2, q_heads=hq, kv_heads=kv, head_dim=d, seq_len=700, splits=3)
+    if bits:
+        wl = wl.with_bits(int(bits))
+    inp = W.generate(wl)
+    q64 = inp.q.astype(np.float64) * 8.0
+    q = _t(q64.astype(inp.q.dtype), dev)
+    q64 = q.cpu().numpy().astype(np.float64)
+    if wl.near_fraction:
+        kn, vn = inp.tier("near")
+        kf, vf = inp.tier("far")
+        SN = wl.near_split_count
+    else:
+        kf, vf = inp.k, inp.v
+        kn = vn = np.zeros(kf.shape[:2] + (0, d), np.float16)
+        SN = 0
+    T = kf.shape[2]
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, d, T, _fmt(wl.k_bits), _fmt(wl.v_bits),
+                                 seed=W.SIGN_SEED, device=dev,
+                                 near_k=_t(kn, dev) if SN else None, near_v=_t(vn, dev) if SN else None)
+    cache.append(_t(kf, dev), _t(vf, dev), start_pos=0)
+    s = _signs(d)
+    k_rot = _dequant_gpu_cache(cache.k_codes[:, :, :T].cpu().numpy(), cache.k_norms[:, :, :T].cpu().numpy(),
+                               wl.k_bits, d)
+    v_rot = _dequant_gpu_cache(cache.v_codes[:, :, :T].cpu().numpy(), cache.v_norms[:, :, :T].cpu().numpy(),
+                               wl.v_bits, d)
+    sf = O.far_scores(q64, k_rot, s)
+    G = hq // kv
+    sn = np.einsum("bhd,bhtd->bht", q64, np.repeat(kn.astype(np.float64), G, axis=1)) / math.sqrt(d)
+    top = np.maximum(sf.max(axis=-1), sn.max(axis=-1, initial=-np.inf))
+    gate = top.astype(np.float32)
+    spike = np.percentile(sf, 75, axis=-1).astype(np.float32)
+    gated = sf < gate.astype(np.float64)[..., None] - O.GATE_LOG
+    assert gated.mean() > 0.2 and (~gated).any()
+
+    words = torch.zeros((wl.batch, hq, (T + 31) // 32), dtype=torch.int32, device=dev)
+    part_o, part_ml = cache.attend(q, T, wl.splits, SN, gate_ref=_t(gate, dev), spike_ref=_t(spike, dev),
+                                   spike_bits=words)
+    out = cache.merge(part_o, part_ml, wl.splits, SN)
+    torch.cuda.synchronize()
+    ref = O.gated_two_tier_attention(q64, kn.astype(np.float64), vn.astype(np.float64), k_rot, v_rot, s,
+                                     gate.astype(np.float64))
+    _rows_close(f"{name} gated", out.cpu().numpy(), ref)
+    # A reference 14 above the top score gates every far value with weight
+    # below e^-2: far from the ungated answer, so a kernel that ignored the
+    # gate would fail here.
+    hard = (top + 14.0).astype(np.float32)
+    part_o, part_ml = cache.attend(q, T, wl.splits, SN, gate_ref=_t(hard, dev))
+    out2 = cache.merge(part_o, part_ml, wl.splits, SN)
+    torch.cuda.synchronize()
+    ref2 = O.gated_two_tier_attention(q64, kn.astype(np.float64), vn.astype(np.float64), k_rot, v_rot, s,
+                                      hard.astype(np.float64))
+    plain = O.two_tier_attention(q64, kn.astype(np.float64), vn.astype(np.float64), k_rot, v_rot, s)
+    assert np.abs(plain - ref2).max() > 5 * ATOL
+    _rows_close(f"{name} hard gate", out2.cpu().numpy(), ref2)
+
+    want = O.spike_flags(q64, k_rot, s, spike.astype(np.float64))
+    got_words = words.cpu().numpy().view(np.uint32)
+    got = ((got_words[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(wl.batch, hq, -1)[..., :T]
+    near_thr = np.abs(sf - spike.astype(np.float64)[..., None]) <= 1e-3
+    bad = (got.astype(bool) != want) & ~near_thr
+    assert not bad.any(), f"{int(bad.sum())} spike flags differ"
+    assert got.sum() > 0
+
+
 def test_head_dim_64(dev):
     wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, head_dim=64, seq_len=200, splits=3)
     run_case(dev, wl)
