@@ -66,6 +66,11 @@ def parse(argv=None):
     ap.add_argument("--bits", type=int, default=None, help="override code bits (bitwidth_sweep)")
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gate", action="store_true",
+                    help="score-gated attention with spike flags (kvq_decode_attention_gated): gate reference "
+                         "= the query's own log-sum-exp from an ungated pass, spike threshold 4 below it")
+    ap.add_argument("--query-scale", type=float, default=1.0,
+                    help="multiply the decode query (a larger scale gives a more peaked softmax)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this size (HBM counter calibration)")
     return ap.parse_args(argv)
@@ -249,6 +254,8 @@ def main(argv=None) -> int:
     k_dev = torch.from_numpy(np.ascontiguousarray(kf)).to(dev)
     v_dev = torch.from_numpy(np.ascontiguousarray(vf)).to(dev)
     q_dev = torch.from_numpy(inp.q).to(dev)
+    if args.query_scale != 1.0:
+        q_dev = (q_dev.float() * args.query_scale).to(q_dev.dtype)
     kn_dev = None if kn is None else torch.from_numpy(np.ascontiguousarray(kn)).to(dev)
     vn_dev = None if vn is None else torch.from_numpy(np.ascontiguousarray(vn)).to(dev)
     R = max(1, math.ceil((1 << 30) / by["cache"]))
@@ -284,11 +291,24 @@ def main(argv=None) -> int:
     bufs = [c.partial_buffers(wl.q_heads, S, near_splits) for c in caches[:2]]
     out = torch.empty((wl.batch, wl.q_heads, wl.head_dim), dtype=torch.float32, device=dev)
 
+    gate_kw = {}
+    if args.gate:
+        # the references a decode loop would carry over from its previous step
+        lse = torch.empty((wl.batch, wl.q_heads), dtype=torch.float32, device=dev)
+        caches[0].decode(q_dev, T, S, near_splits, lse=lse)
+        gate_kw = {"gate_ref": lse, "spike_ref": lse - 4.0,
+                   "spike_bits": torch.zeros((wl.batch, wl.q_heads, (T + 31) // 32), dtype=torch.int32, device=dev)}
+
+    def attend(c, po, pml):
+        c.attend(q_dev, T, S, near_splits, po, pml, **gate_kw)
+
     def step(i):
         c = caches[i % R]
         po, pml = bufs[i % 2]
         c.append(k_new, v_new, T - 1)
-        c.attend(q_dev, T, S, near_splits, po, pml)
+        if args.gate:
+            gate_kw["spike_bits"].zero_()
+        attend(c, po, pml)
         c.merge(po, pml, S, near_splits, out=out)
 
     for i in range(args.warmup):
@@ -315,18 +335,18 @@ def main(argv=None) -> int:
     # event pair (average launch duration), then one event pair per launch ----
     n_att = max(50, min(args.steps, 400))
     for i in range(5):
-        caches[i % R].attend(q_dev, T, S, near_splits, *bufs[0])
+        attend(caches[i % R], *bufs[0])
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(n_att):
-        caches[i % R].attend(q_dev, T, S, near_splits, *bufs[0])
+        attend(caches[i % R], *bufs[0])
     e1.record(stream)
     torch.cuda.synchronize()
     att_avg = e0.elapsed_time(e1) / n_att
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_att)]
     for i, (a, b) in enumerate(evs):
         a.record(stream)
-        caches[i % R].attend(q_dev, T, S, near_splits, *bufs[0])
+        attend(caches[i % R], *bufs[0])
         b.record(stream)
     torch.cuda.synchronize()
     att_ms = [a.elapsed_time(b) for a, b in evs]
@@ -334,7 +354,7 @@ def main(argv=None) -> int:
     att_bytes = by["cache"] + by["q"] + by["out"]
     step_bytes = att_bytes + by["append_token"]
     achieved = att_bytes / (att_avg / 1e3) / 1e9
-    kernel = caches[0].attention_kernel(wl.q_heads, near_splits)
+    kernel = "attend_kernel" if args.gate else caches[0].attention_kernel(wl.q_heads, near_splits)
     traffic = read_traffic(wl.name, kernel_source_sha(kernel))
     result = {
         "metric": METRIC,
@@ -352,6 +372,7 @@ def main(argv=None) -> int:
         "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.q_heads, "kv_heads": wl.kv_heads,
                    "head_dim": wl.head_dim, "seq_len": wl.seq_len, "k_bits": wl.k_bits, "v_bits": wl.v_bits,
                    "splits": S, "near_splits": near_splits, "layer_replicas": R, "launch": "hip_graph",
+                   "gated": bool(args.gate), "query_scale": args.query_scale,
                    "step_bytes": step_bytes},
         "pct_of_hbm_peak": round(100 * step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
         "append_tokens_per_s": round(append_tok_s, 1),
@@ -365,6 +386,10 @@ def main(argv=None) -> int:
                      "event_pair_min_us": round(min(att_ms) * 1e3, 3)},
         "copy_probe": copy_rate(),
     }
+    if args.gate:
+        # a gated launch skips the value rows of gated tokens: its rate is
+        # quoted against the ungated algorithmic bytes (an effective rate)
+        result["roofline"]["bytes_basis"] = "ungated"
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(result), flush=True)

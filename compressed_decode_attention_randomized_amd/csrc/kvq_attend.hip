@@ -195,9 +195,15 @@ struct FarTier {
   float nk, nv;
 
   __device__ void load(int t, int ds) {
+    load_keys(t, ds);
+    load_values(t, ds);
+  }
+  __device__ void load_keys(int t, int ds) {
     load_slice<KNB>(krow0 + (size_t)t * KROW + ds * KNB, kw);
-    load_slice<VNB>(vrow0 + (size_t)t * VROW + ds * VNB, vw);
     nk = (KB == 8) ? 1.f : half_to_float(kn0[t]);
+  }
+  __device__ void load_values(int t, int ds) {
+    load_slice<VNB>(vrow0 + (size_t)t * VROW + ds * VNB, vw);
     nv = half_to_float(vn0[t]);
   }
   __device__ void score(const float (&qr)[G][DPL], float (&part)[G]) const {
@@ -291,16 +297,9 @@ struct NearTier {
 // token.  PIPE: the next block's rows are requested before this block's
 // arithmetic (two blocks of loads in flight per wave, at the cost of the
 // second block's registers).
-//
-// GATED (far tier): a token whose score is below fg.gate[h] keeps its weight
-// in the sum l but adds nothing to head h's values (the value decode is
-// skipped when every head gates it), and the wave's flags of tokens scoring
-// above fg.spike[h] are or-ed into head h's flag words (a wave's TPW
-// consecutive tokens never straddle a 32-token word: blocks start at
-// multiples of 32).
-template <int G, int DPL, int LPT, bool PIPE, bool GATED = false, typename Tier>
-__device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G, DPL> &st, int t0, int t1,
-                           const FarGate<G> *fg = nullptr) {
+
+template <int G, int DPL, int LPT, bool PIPE, typename Tier>
+__device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G, DPL> &st, int t0, int t1) {
   constexpr int TPW = 64 / LPT;
   constexpr int TPB = TPW * kWaves;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -326,36 +325,89 @@ __device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G
     const float ks = cur.key_scale();
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
-    if constexpr (GATED && Tier::kFar) {
-      if (fg->bits) {
-        const int tw = t - ts;                     // the wave's first token of the block
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const uint64_t ball = __builtin_amdgcn_ballot_w64(ds == 0 && s[h] > fg->spike[h]);
-          uint32_t m = 0u;
-#pragma unroll
-          for (int k = 0; k < TPW; ++k) m |= (uint32_t)((ball >> (k * LPT)) & 1ull) << k;
-          if (m != 0u && lane == 0)
-            atomicOr(fg->bits + (size_t)h * fg->words + (tw >> 5), m << (tw & 31));
-        }
-      }
-    }
     st.add_scores(s, p);
-    if constexpr (GATED && Tier::kFar) {
-      bool any = false;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const bool keep = s[h] >= fg->gate[h];
-        p[h] = keep ? p[h] : 0.f;
-        any = any || keep;
-      }
-      if (any) cur.accumulate(p, st);
-    } else {
-      cur.accumulate(p, st);
-    }
+    cur.accumulate(p, st);
     if constexpr (PIPE) cur = nxt;
     t = tn;
   }
+}
+
+// Far-tier loop with the score gate and spike flags.  A token whose score is
+// below fg.gate[h] keeps its weight in l but adds nothing to head h's
+// values; a lane slot whose token every head gates does not even load its
+// value row (the value loads of a block go out after the block's scores,
+// and are accumulated one block later, before the next block's softmax
+// update, so the running state they were weighted against still holds).
+// Flags of tokens scoring above fg.spike[h] are or-ed into head h's words
+// (a wave's TPW consecutive tokens never straddle a 32-token word: blocks
+// start at multiples of 32).  Two tier buffers alternate so no register
+// with a load in flight is ever copied.
+template <int G, int DPL, int LPT, typename Tier>
+__device__ void token_loop_gated(const Tier &proto, const float (&qr)[G][DPL], State<G, DPL> &st, int t0, int t1,
+                                 const FarGate<G> &fg) {
+  constexpr int TPW = 64 / LPT;
+  constexpr int TPB = TPW * kWaves;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ds = lane % LPT, ts = lane / LPT;
+  if (t0 >= t1) return;
+  auto row = [&](int t) { return t < t1 ? t : t0; };
+  // one block: X has its keys loaded; Y holds the previous block's values
+  // (pending, weights py) and takes the next block's keys
+  auto block = [&](Tier &X, Tier &Y, float (&px)[G], const float (&py)[G], bool &vx, bool vy, int t) {
+    Y.load_keys(row(t + TPB), ds);
+    float part[G];
+    X.score(qr, part);
+#pragma unroll
+    for (int m = 1; m < LPT; m <<= 1) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) part[h] += __shfl_xor(part[h], m);
+    }
+    const bool valid = t < t1;
+    float s[G];
+    const float ks = X.key_scale();
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
+    if (vy) Y.accumulate(py, st);
+    if (fg.bits) {
+      const int tw = t - ts;                       // the wave's first token of the block
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint64_t ball = __builtin_amdgcn_ballot_w64(ds == 0 && s[h] > fg.spike[h]);
+        uint32_t m = 0u;
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) m |= (uint32_t)((ball >> (k * LPT)) & 1ull) << k;
+        if (m != 0u && lane == 0) atomicOr(fg.bits + (size_t)h * fg.words + (tw >> 5), m << (tw & 31));
+      }
+    }
+    st.add_scores(s, px);
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const bool keep = s[h] >= fg.gate[h];
+      px[h] = keep ? px[h] : 0.f;
+      any = any || keep;
+    }
+    if (any) X.load_values(row(t), ds);
+    vx = any;
+  };
+  Tier A = proto, B = proto;
+  float pa[G], pb[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) pa[h] = pb[h] = 0.f;
+  bool va = false, vb = false;
+  int t = t0 + wave * TPW + ts;
+  A.load_keys(row(t), ds);
+  for (int base = t0; base < t1; base += 2 * TPB) {
+    block(A, B, pa, pb, va, vb, t);
+    t += TPB;
+    if (base + TPB >= t1) {
+      if (va) A.accumulate(pa, st);
+      return;
+    }
+    block(B, A, pb, pa, vb, va, t);
+    t += TPB;
+  }
+  if (vb) B.accumulate(pb, st);
 }
 
 // NEAR: the launch has near-tier splits (without them the kernel carries no
@@ -472,7 +524,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
       }
       fg.bits = P.spike_ref ? P.spike_bits + row0 * P.spike_words : nullptr;
       fg.words = P.spike_words;
-      token_loop<G, DPL, LPT, kPipe, true>(tier, qr, st, t0, t1, &fg);
+      token_loop_gated<G, DPL, LPT>(tier, qr, st, t0, t1, fg);
     } else {
       token_loop<G, DPL, LPT, kPipe>(tier, qr, st, t0, t1);
     }
