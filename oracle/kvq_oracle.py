@@ -612,3 +612,82 @@ def pack_flags(flags):
     pad[..., :T] = flags
     bits = pad.reshape(flags.shape[:-1] + (W, 32)) << np.arange(32, dtype=np.uint64)
     return bits.sum(axis=-1).astype(np.uint32)
+
+
+# Outlier two-stream key cache ([Velox] "Outlier Two-Stream Cache"): a
+# calibration over the first tokens picks, per (b, KV head), the channels of
+# largest variance; those channels of every key are kept as int8 with a
+# per-token scale and zeroed in the vector that goes through the rotation
+# codec; a score adds the codec part and the int8 part.  Readings: 8
+# channels (the page's benchmark), population variance over the calibration
+# tokens with ties to the lower channel, indices ascending; scale =
+# RN_fp32(max |x_o| / 127) in float32 arithmetic (fp32: the page fixes no
+# precision), code = RNE(x_o / scale) clamped to +-127, zero scale -> zero
+# codes.
+OUTLIER_COUNT = 8
+
+
+def calibrate_outliers(k_calib: np.ndarray, count: int = OUTLIER_COUNT) -> np.ndarray:
+    """[B, H, N, d] calibration keys -> int64 [B, H, count]: the channels of
+    largest variance over the N tokens, ascending."""
+    x = np.asarray(k_calib, np.float64)
+    var = x.var(axis=2)
+    order = np.argsort(-var, axis=-1, kind="stable")[..., :count]
+    return np.sort(order, axis=-1)
+
+
+def split_outliers(x: np.ndarray, idx: np.ndarray):
+    """x [B, H, T, d], idx [B, H, K] -> (x with those channels zeroed, the
+    channels' values [B, H, T, K]); both in x's dtype."""
+    sel = np.broadcast_to(idx[:, :, None, :], x.shape[:3] + (idx.shape[-1],))
+    xo = np.take_along_axis(x, sel, axis=3)
+    xi = x.copy()
+    np.put_along_axis(xi, sel, np.zeros((), x.dtype), axis=3)
+    return xi, xo
+
+
+def quantize_outliers(xo: np.ndarray):
+    """[..., K] outlier values -> (codes int8 [..., K], scale float32 [...])."""
+    a = np.abs(np.asarray(xo, np.float32)).max(axis=-1)
+    scale = (a / np.float32(127.0)).astype(np.float32)          # one float32 rounding
+    s64 = scale.astype(np.float64)[..., None]
+    x64 = np.asarray(xo, np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = np.where(s64 > 0, x64 / s64, 0.0)
+    code = np.rint(u)
+    # quotients within 1e-9 of a half-integer: decide the rounding exactly
+    frac = np.abs(u - np.floor(u) - 0.5)
+    for i in zip(*np.nonzero((frac < 1e-9) & (s64 > 0))):
+        q = Fraction(float(x64[i])) / Fraction(float(s64[i[:-1] + (0,)]))
+        fl = q.numerator // q.denominator
+        r = q - fl
+        code[i] = fl + (1 if (r > Fraction(1, 2) or (r == Fraction(1, 2) and fl % 2 == 1)) else 0)
+    return np.clip(code, -127, 127).astype(np.int8), scale
+
+
+def dequantize_outliers(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    return codes.astype(np.float64) * np.asarray(scale, np.float64)[..., None]
+
+
+def two_stream_attention(q, k_rot, v_rot, idx, out_codes, out_scale, signs, lse: bool = False):
+    """Decode attention over a two-stream key cache, by definition, float64:
+    s_t = (R q) . khat_t / sqrt(d) + q[idx] . xhat_o,t / sqrt(d), with
+    khat the codec reconstruction of the key whose outlier channels were
+    zeroed and xhat_o the int8 reconstruction; values as in attention().
+    idx [B, Hkv, K]; out_codes [B, Hkv, T, K]; out_scale [B, Hkv, T]."""
+    B, Hq, d = q.shape
+    Hkv = k_rot.shape[1]
+    G = Hq // Hkv
+    qr = rotate(q, signs)
+    kk = np.repeat(np.asarray(k_rot, np.float64), G, axis=1)
+    vv = np.repeat(np.asarray(v_rot, np.float64), G, axis=1)
+    xo = np.repeat(dequantize_outliers(out_codes, out_scale), G, axis=1)          # [B, Hq, T, K]
+    qo = np.take_along_axis(np.asarray(q, np.float64), np.repeat(idx, G, axis=1), axis=2)   # [B, Hq, K]
+    s = (np.einsum("bhd,bhtd->bht", qr, kk) + np.einsum("bhk,bhtk->bht", qo, xo)) / math.sqrt(d)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=-1, keepdims=True)
+    o = rotate_inverse(np.einsum("bht,bhtd->bhd", e / l, vv), signs)
+    if lse:
+        return o, (m + np.log(l))[..., 0]
+    return o
