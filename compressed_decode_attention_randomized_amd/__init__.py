@@ -22,6 +22,7 @@ KVQ_LM2, KVQ_LM3, KVQ_LM4, KVQ_FP8_E4M3 = 2, 3, 4, 8
 
 EXPORTED = ("kvq_row_bytes", "kvq_lloyd_max", "kvq_make_signs", "kvq_quantize_append",
             "kvq_decode_attention", "kvq_decode_attention_gated", "kvq_decode_attention_kernel", "kvq_merge",
+            "kvq_calibrate_outliers",
             "kvq_partials_floats",
             "kvq_status_string", "kvq_last_error")
 
@@ -41,7 +42,8 @@ class CacheStruct(ctypes.Structure):
         ("v_codes", ctypes.c_void_p), ("v_norms", ctypes.c_void_p),
         ("signs", ctypes.c_void_p), ("k_centroids", ctypes.c_void_p), ("v_centroids", ctypes.c_void_p),
         ("near_k", ctypes.c_void_p), ("near_v", ctypes.c_void_p),
-        ("near_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("near_len", ctypes.c_int32), ("outlier_count", ctypes.c_int32),
+        ("outlier_idx", ctypes.c_void_p), ("outlier_codes", ctypes.c_void_p), ("outlier_scales", ctypes.c_void_p),
     ]
 
 
@@ -66,6 +68,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvq_quantize_append": (I32, [CP, P, P, I32, I32, I32, P]),
         "kvq_decode_attention": (I32, [CP, P, I32, I32, I32, I32, I32, P, P, P]),
         "kvq_decode_attention_gated": (I32, [CP, P, I32, I32, I32, I32, I32, P, P, P, P, P, P]),
+        "kvq_calibrate_outliers": (I32, [CP, P, I32, I32, P, P]),
         "kvq_decode_attention_kernel": (ctypes.c_char_p, [CP, I32, I32]),
         "kvq_merge": (I32, [CP, P, P, I32, I32, I32, P, P, P]),
         "kvq_partials_floats": (SZ, [I32, I32, I32, I32]),
@@ -156,10 +159,15 @@ class KVCache:
     v_centroids: object
     near_k: object = None
     near_v: object = None
+    outlier_idx: object = None       # key outlier stream: [B, Hkv, 8] int32, codes [B, Hkv, cap, 8] int8,
+    outlier_codes: object = None     # scales [B, Hkv, cap] float32 (None: stream off)
+    outlier_scales: object = None
 
     @classmethod
     def allocate(cls, batch, kv_heads, head_dim, capacity, k_format=KVQ_LM4, v_format=KVQ_LM4,
-                 seed=42, device="cuda", near_k=None, near_v=None):
+                 seed=42, device="cuda", near_k=None, near_v=None, outliers: int = 0):
+        """outliers: 0, or 8 for the key outlier stream (its channels are
+        chosen by calibrate())."""
         import torch
         kr, vr = row_bytes(k_format, head_dim), row_bytes(v_format, head_dim)
         if not kr or not vr:
@@ -174,8 +182,13 @@ class KVCache:
         kc = torch.from_numpy(lloyd_max(k_format, head_dim)).to(dev) if k_format != KVQ_FP8_E4M3 else \
             torch.zeros(16, dtype=torch.float32, device=dev)
         vc = torch.from_numpy(lloyd_max(v_format, head_dim)).to(dev)
+        oi = oc = osc = None
+        if outliers:
+            oi = torch.zeros((batch, kv_heads, outliers), dtype=torch.int32, device=dev)
+            oc = torch.zeros((batch, kv_heads, capacity, outliers), dtype=torch.int8, device=dev)
+            osc = torch.zeros((batch, kv_heads, capacity), dtype=torch.float32, device=dev)
         return cls(batch, kv_heads, head_dim, capacity, k_format, v_format, k_codes, k_norms, v_codes,
-                   v_norms, signs, kc, vc, near_k, near_v)
+                   v_norms, signs, kc, vc, near_k, near_v, oi, oc, osc)
 
     @property
     def near_len(self) -> int:
@@ -189,7 +202,9 @@ class KVCache:
         return CacheStruct(self.batch, self.kv_heads, self.head_dim, self.capacity, self.k_format,
                            self.v_format, p(self.k_codes), p(self.k_norms), p(self.v_codes), p(self.v_norms),
                            p(self.signs), p(self.k_centroids), p(self.v_centroids), p(self.near_k),
-                           p(self.near_v), self.near_len, 0)
+                           p(self.near_v), self.near_len,
+                           0 if self.outlier_idx is None else int(self.outlier_idx.shape[-1]),
+                           p(self.outlier_idx), p(self.outlier_codes), p(self.outlier_scales))
 
     # -- kvq_quantize_append --------------------------------------------------
     def append(self, k, v, start_pos: int):
@@ -202,6 +217,19 @@ class KVCache:
         cs = self.struct()
         _check(load().kvq_quantize_append(ctypes.byref(cs), k.data_ptr(), v.data_ptr(), _dtype_code(k),
                                           start_pos, n_new, _stream_handle(k.device)), "kvq_quantize_append")
+
+    # -- kvq_calibrate_outliers -----------------------------------------------
+    def calibrate(self, k_calib):
+        """Pick the key outlier channels from calibration keys [B, Hkv, N, d]
+        (the context's first tokens) into outlier_idx."""
+        if self.outlier_idx is None:
+            raise ValueError("the cache has no outlier stream (allocate with outliers=8)")
+        n = int(k_calib.shape[2])
+        _need(k_calib, "k_calib", (self.batch, self.kv_heads, n, self.head_dim))
+        cs = self.struct()
+        _check(load().kvq_calibrate_outliers(ctypes.byref(cs), k_calib.data_ptr(), _dtype_code(k_calib), n,
+                                             self.outlier_idx.data_ptr(), _stream_handle(k_calib.device)),
+               "kvq_calibrate_outliers")
 
     # -- kvq_decode_attention -------------------------------------------------
     def partial_buffers(self, q_heads: int, num_splits: int, num_near_splits: int = 0):

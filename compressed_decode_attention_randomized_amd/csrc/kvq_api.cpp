@@ -34,7 +34,15 @@ kvq_status check_cache(const kvq_cache *c, const char *fn) {
     return fail(KVQ_EINVAL, "%s: near tier needs near_k and near_v", fn);
   if (c->near_len > 0 && (!aligned(c->near_k, 16) || !aligned(c->near_v, 16)))
     return fail(KVQ_EINVAL, "%s: near tier buffers must be 16-byte aligned", fn);
-  if (c->reserved != 0) return fail(KVQ_EINVAL, "%s: reserved field must be 0", fn);
+  if (c->outlier_count != 0 && c->outlier_count != kvq::kOutlierCount)
+    return fail(KVQ_EUNSUPPORTED, "%s: outlier_count %d (built: 0, %d)", fn, c->outlier_count, kvq::kOutlierCount);
+  if (c->outlier_count) {
+    if (!is_lm(c->k_format)) return fail(KVQ_EUNSUPPORTED, "%s: the outlier stream needs Lloyd-Max keys", fn);
+    if (!c->outlier_idx || !c->outlier_codes || !c->outlier_scales)
+      return fail(KVQ_EINVAL, "%s: outlier stream buffers are NULL", fn);
+    if (!aligned(c->outlier_idx, 16) || !aligned(c->outlier_codes, 16) || !aligned(c->outlier_scales, 16))
+      return fail(KVQ_EINVAL, "%s: outlier stream buffers must be 16-byte aligned", fn);
+  }
   return KVQ_OK;
 }
 
@@ -66,7 +74,8 @@ kvq_status kvq_quantize_append(const kvq_cache *cache, const void *k, const void
   kvq::AppendArgs a{k, v, dtype == KVQ_F16, cache->batch, cache->kv_heads, cache->head_dim, cache->capacity,
                     start_pos, n_new, cache->k_format, cache->v_format,
                     static_cast<uint8_t *>(cache->k_codes), static_cast<uint8_t *>(cache->v_codes),
-                    cache->k_norms, cache->v_norms, cache->signs, cache->k_centroids, cache->v_centroids};
+                    cache->k_norms, cache->v_norms, cache->signs, cache->k_centroids, cache->v_centroids,
+                    cache->outlier_count ? cache->outlier_idx : nullptr, cache->outlier_codes, cache->outlier_scales};
   bool ok = true;
   hipError_t e = kvq::launch_append(a, stream, &ok);
   if (!ok) return kvq::fail(KVQ_EUNSUPPORTED, "%s: format combination not built", fn);
@@ -104,6 +113,11 @@ kvq_status attend_args(const char *fn, const kvq_cache *cache, const void *q, in
                          cache->v_format, static_cast<const uint8_t *>(cache->k_codes),
                          static_cast<const uint8_t *>(cache->v_codes), cache->k_norms, cache->v_norms, cache->signs,
                          cache->k_centroids, cache->v_centroids, cache->near_k, cache->near_v, part_o, part_ml};
+  if (cache->outlier_count) {
+    out->outlier_idx = cache->outlier_idx;
+    out->outlier_codes = cache->outlier_codes;
+    out->outlier_scales = cache->outlier_scales;
+  }
   return KVQ_OK;
 }
 
@@ -141,6 +155,8 @@ kvq_status kvq_decode_attention_gated(const kvq_cache *cache, const void *q, int
                                     part_ml, &a);
   if (st != KVQ_OK) return st;
   if (!gate_ref && !spike_ref) return kvq::fail(KVQ_EINVAL, "%s: neither gate_ref nor spike_ref given", fn);
+  if (cache->outlier_count)
+    return kvq::fail(KVQ_EUNSUPPORTED, "%s: the gated pass is not built for a key outlier stream", fn);
   if ((spike_ref == nullptr) != (spike_bits == nullptr))
     return kvq::fail(KVQ_EINVAL, "%s: spike_ref and spike_bits go together", fn);
   if (!aligned(gate_ref, 4) || !aligned(spike_ref, 4) || !aligned(spike_bits, 4))
@@ -153,6 +169,22 @@ kvq_status kvq_decode_attention_gated(const kvq_cache *cache, const void *q, int
   return attend_status(fn, cache, q_heads, ok, e);
 }
 
+kvq_status kvq_calibrate_outliers(const kvq_cache *cache, const void *keys, int32_t dtype, int32_t n_tokens,
+                                  int32_t *idx_out, hipStream_t stream) {
+  const char *fn = "kvq_calibrate_outliers";
+  kvq::clear_error();
+  const kvq_status st = check_cache(cache, fn);
+  if (st != KVQ_OK) return st;
+  if (!keys || !idx_out) return kvq::fail(KVQ_EINVAL, "%s: NULL keys or idx_out", fn);
+  if (dtype != KVQ_F32 && dtype != KVQ_F16) return kvq::fail(KVQ_EINVAL, "%s: dtype %d", fn, dtype);
+  if (n_tokens < 1) return kvq::fail(KVQ_EINVAL, "%s: n_tokens=%d", fn, n_tokens);
+  if (!aligned(keys, 16) || !aligned(idx_out, 16))
+    return kvq::fail(KVQ_EINVAL, "%s: keys and idx_out must be 16-byte aligned", fn);
+  if ((int64_t)cache->batch * cache->kv_heads > (1ll << 31) - 1) return kvq::fail(KVQ_EINVAL, "%s: grid too large", fn);
+  return hip_status(kvq::launch_calibrate(keys, dtype == KVQ_F16, cache->batch, cache->kv_heads, cache->head_dim,
+                                          n_tokens, idx_out, stream), fn);
+}
+
 const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads, int32_t num_near_splits) {
   kvq::clear_error();
   if (check_cache(cache, "kvq_decode_attention_kernel") != KVQ_OK) return nullptr;
@@ -162,6 +194,7 @@ const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads,
                     static_cast<const uint8_t *>(cache->k_codes), static_cast<const uint8_t *>(cache->v_codes),
                     cache->k_norms, cache->v_norms, cache->signs, cache->k_centroids, cache->v_centroids,
                     cache->near_k, cache->near_v, nullptr, nullptr};
+  if (cache->outlier_count) a.outlier_idx = cache->outlier_idx;
   return kvq::attend_kernel_name(a);
 }
 

@@ -106,6 +106,12 @@ struct Stream {
   uint8_t *codes;
   uint16_t *norms;
   const float *centroids;
+  // key outlier stream ("Outlier Two-Stream Cache"; NULL idx: off): the
+  // vector's kOutlierCount channels idx are zeroed before the codec and
+  // stored as int8 codes with an fp32 per-token scale
+  const int32_t *out_idx;
+  int8_t *out_codes;
+  float *out_scales;
 };
 
 // Encode the vectors of one stream (keys or values).  BITS in {2,3,4} for
@@ -136,6 +142,40 @@ __device__ void encode(const Stream &st, const int8_t *__restrict__ signs, int n
     __syncthreads();
   }
   if (!live) return;
+
+  const int bvec = vec / n_new;                    // (b * Hkv + h)
+  const int t = start_pos + (vec - bvec * n_new);
+  const size_t slot = (size_t)bvec * capacity + t;
+
+  if (st.out_idx) {
+    // outlier channels of this vector: slot k of the stream holds channel
+    // idx[k]; the lane's coordinates lv*8 .. lv*8+7 are checked against all
+    const int4 i0 = reinterpret_cast<const int4 *>(st.out_idx + (size_t)bvec * kOutlierCount)[0];
+    const int4 i1 = reinterpret_cast<const int4 *>(st.out_idx + (size_t)bvec * kOutlierCount)[1];
+    const int idx[kOutlierCount] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+    int which[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      which[e] = -1;
+#pragma unroll
+      for (int k = 0; k < kOutlierCount; ++k) which[e] = (idx[k] == lv * 8 + e) ? k : which[e];
+      if (which[e] >= 0) amax = fmaxf(amax, fabsf((float)x[e]));
+    }
+#pragma unroll
+    for (int m = 1; m < LPV; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    const float scale = amax / 127.f;               // one float32 rounding
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (which[e] >= 0) {
+        const double u = (scale > 0.f) ? x[e] / (double)scale : 0.0;
+        const double c = fmin(fmax(rint(u), -127.0), 127.0);
+        st.out_codes[slot * kOutlierCount + which[e]] = (int8_t)(int)c;
+        x[e] = 0.0;
+      }
+    }
+    if (lv == 0) st.out_scales[slot] = scale;
+  }
 
   // squared norm from the original coordinates
   double ss = 0.0;
@@ -175,9 +215,6 @@ __device__ void encode(const Stream &st, const int8_t *__restrict__ signs, int n
 #pragma unroll
   for (int m = 1; m < LPV; m <<= 1) ss += __shfl_xor(ss, m);
 
-  const int bvec = vec / n_new;                    // (b * Hkv + h)
-  const int t = start_pos + (vec - bvec * n_new);
-  const size_t slot = (size_t)bvec * capacity + t;
   uint8_t *row = st.codes + slot * ROW;
 
   if (BITS == 8) {
@@ -238,8 +275,8 @@ hipError_t launch3(const AppendArgs &a, hipStream_t stream) {
   const int nvec = a.batch * a.kv_heads * a.n_new;
   constexpr int VPB = kBlock / (D / 8);
   dim3 grid((nvec + VPB - 1) / VPB, 2);
-  Stream ks{a.k, a.k_codes, a.k_norms, a.k_centroids};
-  Stream vs{a.v, a.v_codes, a.v_norms, a.v_centroids};
+  Stream ks{a.k, a.k_codes, a.k_norms, a.k_centroids, a.outlier_idx, a.outlier_codes, a.outlier_scales};
+  Stream vs{a.v, a.v_codes, a.v_norms, a.v_centroids, nullptr, nullptr, nullptr};
   if (a.in_f16) {
     hipLaunchKernelGGL((append_kernel<D, KB, VB, _Float16>), grid, dim3(kBlock), 0, stream, ks, vs, a.signs, nvec,
                        a.n_new, a.capacity, a.start_pos);

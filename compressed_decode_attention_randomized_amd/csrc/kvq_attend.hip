@@ -53,6 +53,9 @@ struct Params {
   const float *gate_ref, *spike_ref;   // [B][Hq] natural-log references or NULL (gated launches)
   uint32_t *spike_bits;                // [B][Hq][spike_words]
   int spike_words;
+  const int32_t *out_idx;              // key outlier stream ([B][Hkv][8] channels) or NULL
+  const int8_t *out_codes;             // [B][Hkv][capacity][8]
+  const float *out_scales;             // [B][Hkv][capacity]
 };
 
 // Score gate and spike flags of the far tier for one block of tokens, the G
@@ -180,7 +183,9 @@ __device__ inline float2_t pair_entry(const uint8_t *tab, uint32_t f, uint32_t s
 // Far tier: packed Lloyd-Max (KB in 2..4) or fp8 (KB = 8) keys, Lloyd-Max values.
 // fp8 keys decode in hardware (v_cvt_pk_f32_fp8: OCP E4M3FN, exact in fp32),
 // 2- and 3-bit codes through pair tables, 4-bit codes one table read each.
-template <int D, int KB, int VB, int G, int DPL>
+// OUT: the keys carry an outlier stream; every score gains
+// q[idx] . (code * scale) / sqrt(d) (qo holds q[idx] pre-scaled).
+template <int D, int KB, int VB, int G, int DPL, bool OUT = false>
 struct FarTier {
   static constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
   static constexpr int KNB = DPL * KB / 8, VNB = DPL * VB / 8;
@@ -193,6 +198,12 @@ struct FarTier {
   uint32_t slot8;
   uint32_t kw[(KNB + 3) / 4], vw[(VNB + 3) / 4];
   float nk, nv;
+  // outlier stream (OUT only)
+  const int8_t *oc0;
+  const float *os0;
+  float qo[G][kOutlierCount];
+  uint2 oc;
+  float osc;
 
   __device__ void load(int t, int ds) {
     load_keys(t, ds);
@@ -201,6 +212,25 @@ struct FarTier {
   __device__ void load_keys(int t, int ds) {
     load_slice<KNB>(krow0 + (size_t)t * KROW + ds * KNB, kw);
     nk = (KB == 8) ? 1.f : half_to_float(kn0[t]);
+    if constexpr (OUT) {
+      oc = *reinterpret_cast<const uint2 *>(oc0 + (size_t)t * kOutlierCount);
+      osc = os0[t];
+    }
+  }
+  // the outlier stream's part of head h's score (log2 units)
+  __device__ float extra(int h) const {
+    if constexpr (OUT) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < kOutlierCount; ++k) {
+        const uint32_t w = (k < 4) ? oc.x : oc.y;
+        const float c = (float)(int8_t)((w >> (8 * (k & 3))) & 0xFFu);
+        acc = fmaf(qo[h][k], c, acc);
+      }
+      return acc * osc;
+    } else {
+      return 0.f;
+    }
   }
   __device__ void load_values(int t, int ds) {
     load_slice<VNB>(vrow0 + (size_t)t * VROW + ds * VNB, vw);
@@ -283,6 +313,7 @@ struct NearTier {
     }
   }
   __device__ float key_scale() const { return 1.f; }
+  __device__ float extra(int) const { return 0.f; }
   __device__ void accumulate(const float (&p)[G], State<G, DPL> &st) const {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
@@ -324,7 +355,7 @@ __device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G
     float s[G], p[G];
     const float ks = cur.key_scale();
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
+    for (int h = 0; h < G; ++h) s[h] = valid ? fmaf(part[h], ks, cur.extra(h)) : -INFINITY;
     st.add_scores(s, p);
     cur.accumulate(p, st);
     if constexpr (PIPE) cur = nxt;
@@ -366,7 +397,7 @@ __device__ void token_loop_gated(const Tier &proto, const float (&qr)[G][DPL], S
     float s[G];
     const float ks = X.key_scale();
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
+    for (int h = 0; h < G; ++h) s[h] = valid ? fmaf(part[h], ks, X.extra(h)) : -INFINITY;
     if (vy) Y.accumulate(py, st);
     if (fg.bits) {
       const int tw = t - ts;                       // the wave's first token of the block
@@ -412,7 +443,8 @@ __device__ void token_loop_gated(const Tier &proto, const float (&qr)[G][DPL], S
 
 // NEAR: the launch has near-tier splits (without them the kernel carries no
 // registers for the near path).
-template <int D, int KB, int VB, int G, bool NEAR, bool GATED>
+// GATED: score gate and spike flags; OUT: key outlier stream.
+template <int D, int KB, int VB, int G, bool NEAR, bool GATED, bool OUT = false>
 __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
   // G = 1: 32 coordinates per lane, except where near-tier fp16 rows would
   // double the pipelined registers; loads pipelined
@@ -503,7 +535,25 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     const int fs = split - P.num_near_splits;
     const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + 31) / 32 * 32;
     const int t0 = min(P.seq_len, fs * chunk), t1 = min(P.seq_len, t0 + chunk);
-    FarTier<D, KB, VB, G, DPL> tier;
+    FarTier<D, KB, VB, G, DPL, OUT> tier;
+    if constexpr (OUT) {
+      // the query at the outlier channels (original domain), scaled to log2 units of s
+      const float sc = kLog2e / sqrtf((float)D);
+      const int32_t *oi = P.out_idx + (size_t)bh * kOutlierCount;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const size_t qrow = ((size_t)b * P.q_heads + hkv * G + h) * D;
+#pragma unroll
+        for (int k = 0; k < kOutlierCount; ++k) {
+          const int c = oi[k];
+          const float v = P.q_f16 ? half_to_float(static_cast<const uint16_t *>(P.q)[qrow + c])
+                                  : static_cast<const float *>(P.q)[qrow + c];
+          tier.qo[h][k] = v * sc;
+        }
+      }
+      tier.oc0 = P.out_codes + (size_t)bh * P.capacity * kOutlierCount;
+      tier.os0 = P.out_scales + (size_t)bh * P.capacity;
+    }
     tier.krow0 = P.k_codes + (size_t)bh * P.capacity * (D * KB / 8);
     tier.vrow0 = P.v_codes + (size_t)bh * P.capacity * (D * VB / 8);
     tier.kn0 = P.k_norms + (size_t)bh * P.capacity;
@@ -571,9 +621,17 @@ template <int D, int KB, int VB, int G>
 hipError_t go(const AttendArgs &a, hipStream_t stream) {
   Params P{a.q, a.q_f16, a.kv_heads, a.q_heads, a.capacity, a.seq_len, a.num_splits, a.num_near_splits,
            a.near_len, a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids,
-           a.near_k, a.near_v, a.part_o, a.part_ml, a.gate_ref, a.spike_ref, a.spike_bits, (a.seq_len + 31) / 32};
+           a.near_k, a.near_v, a.part_o, a.part_ml, a.gate_ref, a.spike_ref, a.spike_bits, (a.seq_len + 31) / 32,
+           a.outlier_idx, a.outlier_codes, a.outlier_scales};
   dim3 grid(a.near_only ? a.num_near_splits : a.num_near_splits + a.num_splits, a.batch * a.kv_heads);
   const bool near = a.num_near_splits > 0, gated = a.gated != 0;
+  if constexpr (KB != 8) {
+    if (a.outlier_idx) {
+      if (near) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true, false, true>), grid, dim3(kBlock), 0, stream, P);
+      else hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false, false, true>), grid, dim3(kBlock), 0, stream, P);
+      return hipGetLastError();
+    }
+  }
   if (near && gated) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true, true>), grid, dim3(kBlock), 0, stream, P);
   else if (near) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true, false>), grid, dim3(kBlock), 0, stream, P);
   else if (gated) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false, true>), grid, dim3(kBlock), 0, stream, P);
@@ -628,6 +686,7 @@ AttendArgs far_part(const AttendArgs &a) {
 }  // namespace
 
 const char *attend_kernel_name(const AttendArgs &a) {
+  if (a.outlier_idx) return "attend_kernel";
   if (a.num_near_splits > 0) {
     const AttendArgs f = far_part(a);
     if (pair_attend_supported(f)) return "attend_pair_kernel+attend_kernel";
@@ -646,6 +705,8 @@ hipError_t launch_attend_gated(const AttendArgs &a, hipStream_t stream, bool *su
 }
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported) {
+  // The key outlier stream is added to the scores by the VALU kernel only.
+  if (a.outlier_idx) return launch_valu(a, stream, supported);
   // A near tier (fp16 rows, original domain) beside 4-bit or 2-bit far codes
   // that a pair-table kernel covers: the near splits run on the VALU kernel
   // and the far splits on the pair-table kernel, two launches on the stream

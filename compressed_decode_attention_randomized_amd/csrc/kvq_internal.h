@@ -8,6 +8,8 @@
 
 namespace kvq {
 
+constexpr int kOutlierCount = 8;   // channels of the key outlier stream
+
 kvq_status fail(kvq_status st, const char *fmt, ...);
 void clear_error();
 bool valid_head_dim(int32_t d);
@@ -23,6 +25,11 @@ struct AppendArgs {
   uint16_t *k_norms, *v_norms;
   const int8_t *signs;
   const float *k_centroids, *v_centroids;
+  // key outlier stream (NULL idx: off): channels [B][Hkv][8], codes
+  // [B][Hkv][capacity][8], scales [B][Hkv][capacity]
+  const int32_t *outlier_idx = nullptr;
+  int8_t *outlier_codes = nullptr;
+  float *outlier_scales = nullptr;
 };
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream, bool *supported);
 // Bulk-throughput variant (Lloyd-Max keys and values, head_dim 64/128/256).
@@ -46,6 +53,10 @@ struct AttendArgs {
   int32_t gated = 0;        // score gate / spike flags (VALU kernel only)
   const float *gate_ref = nullptr, *spike_ref = nullptr;
   uint32_t *spike_bits = nullptr;
+  // key outlier stream (NULL idx: off)
+  const int32_t *outlier_idx = nullptr;
+  const int8_t *outlier_codes = nullptr;
+  const float *outlier_scales = nullptr;
 };
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported);
 // Score-gated attention with spike flags (a.gate_ref / a.spike_ref / a.spike_bits):
@@ -66,6 +77,10 @@ hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream, int part_
 // Pair-table variant for head_dim 256 (2- or 4-bit keys and values, no near tier, G <= 8).
 bool wide_attend_supported(const AttendArgs &a);
 hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream, int part_base = 0);
+
+// Outlier-channel calibration (validated arguments): keys [B][Hkv][n][head_dim].
+hipError_t launch_calibrate(const void *keys, int in_f16, int batch, int kv_heads, int head_dim, int n,
+                            int32_t *idx, hipStream_t stream);
 
 // Split-merge launch (validated arguments).
 struct MergeArgs {

@@ -79,6 +79,17 @@ typedef enum { KVQ_LM2 = 2, KVQ_LM3 = 3, KVQ_LM4 = 4, KVQ_FP8_E4M3 = 8 } kvq_for
  *            k_centroids is unused (may be NULL) for FP8 keys
  *   near_k, near_v  two-tier caches only: [batch][kv_heads][near_len][head_dim]
  *            fp16 bits in the original (unrotated) domain; NULL with near_len 0
+ *   outlier stream of the keys ("Outlier Two-Stream Cache"), Lloyd-Max keys
+ *   only, outlier_count 0 (off) or 8:
+ *     outlier_idx    [batch][kv_heads][8] int32 channel indices, ascending
+ *                    (kvq_calibrate_outliers fills them)
+ *     outlier_codes  [batch][kv_heads][capacity][8] int8
+ *     outlier_scales [batch][kv_heads][capacity] float32
+ *   With the stream on, kvq_quantize_append zeroes those channels of every
+ *   key before the rotation codec and stores them as int8 codes with the
+ *   per-token scale RN_fp32(max |x_o| / 127) (code = nearest integer of
+ *   x_o / scale, ties to even, zero scale gives zero codes); attention adds
+ *   q[idx] . (code * scale) / sqrt(d) to every far-tier score.
  * Code, norm and sign buffers must be 16-byte aligned and capacity a multiple of 16. */
 typedef struct kvq_cache {
   int32_t batch;
@@ -97,7 +108,10 @@ typedef struct kvq_cache {
   const uint16_t *near_k;
   const uint16_t *near_v;
   int32_t near_len;
-  int32_t reserved;          /* must be 0 */
+  int32_t outlier_count;     /* 0 or 8 */
+  const int32_t *outlier_idx;
+  int8_t *outlier_codes;
+  float *outlier_scales;
 } kvq_cache;
 
 /* Bytes of one packed row ("The Bit-Packing Problem"): head_dim*bits/8 for
@@ -186,6 +200,21 @@ kvq_status kvq_decode_attention_gated(const kvq_cache *cache, const void *q, int
                                       int32_t num_near_splits, const float *gate_ref,
                                       const float *spike_ref, uint32_t *spike_bits, float *part_o,
                                       float *part_ml, hipStream_t stream);
+
+/* Outlier-channel calibration for the key outlier stream ("I Ported a Google
+ * Research Paper to Apple Silicon", "Outlier Two-Stream Cache": calibration on
+ * the first tokens, then detection).  For every (b, KV head), the 8 channels
+ * with the largest population variance over keys[.., 0..n_tokens, ..]
+ * (float64: the mean first, then the mean squared deviation; ties to the
+ * lower channel) are written ascending to idx_out.
+ *   keys     device [batch][kv_heads][n_tokens][head_dim] in dtype
+ *            (KVQ_F32/F16), 16-byte aligned: the context's first tokens;
+ *   idx_out  device int32 [batch][kv_heads][8], 16-byte aligned (normally
+ *            the cache's outlier_idx).
+ * The cache supplies the shape only.  Errors: KVQ_EINVAL (NULL, misaligned,
+ * n_tokens < 1, bad dtype or cache), KVQ_EUNSUPPORTED, KVQ_EHIP. */
+kvq_status kvq_calibrate_outliers(const kvq_cache *cache, const void *keys, int32_t dtype,
+                                  int32_t n_tokens, int32_t *idx_out, hipStream_t stream);
 
 /* Name of the attention kernel kvq_decode_attention launches for this cache,
  * query-head count and near-split count (for profiles and reports): a static

@@ -57,7 +57,8 @@ def _fake_cache(**over):
     call below fails validation before any launch)."""
     base = dict(batch=2, kv_heads=2, head_dim=128, capacity=64, k_format=4, v_format=4,
                 k_codes=0x1000, k_norms=0x2000, v_codes=0x3000, v_norms=0x4000, signs=0x5000,
-                k_centroids=0x6000, v_centroids=0x7000, near_k=0, near_v=0, near_len=0, reserved=0)
+                k_centroids=0x6000, v_centroids=0x7000, near_k=0, near_v=0, near_len=0, outlier_count=0,
+                outlier_idx=0, outlier_codes=0, outlier_scales=0)
     base.update(over)
     return kvq.CacheStruct(**base)
 
@@ -88,6 +89,16 @@ def test_gated_attention_validation():
     assert _gated(cs, T=1000) == kvq.KVQ_ERANGE                             # the plain call's checks come first
 
 
+def test_calibration_validation():
+    lib = kvq.load()
+    cs = _fake_cache()
+    cal = lambda keys=0x8000, dt=1, n=4, out=0x9000: lib.kvq_calibrate_outliers(ctypes.byref(cs), keys, dt, n, out, None)
+    assert cal(n=0) == kvq.KVQ_EINVAL
+    assert cal(keys=0) == kvq.KVQ_EINVAL and cal(out=0) == kvq.KVQ_EINVAL
+    assert cal(keys=0x8008) == kvq.KVQ_EINVAL and cal(out=0x9004) == kvq.KVQ_EINVAL
+    assert cal(dt=7) == kvq.KVQ_EINVAL
+
+
 def test_append_validation():
     assert _append(None) == kvq.KVQ_EINVAL
     assert _append(_fake_cache(), start=60, n=5) == kvq.KVQ_ERANGE
@@ -99,7 +110,12 @@ def test_append_validation():
     assert _append(_fake_cache(head_dim=96)) == kvq.KVQ_EUNSUPPORTED
     assert _append(_fake_cache(v_format=8)) == kvq.KVQ_EINVAL
     assert _append(_fake_cache(k_norms=0)) == kvq.KVQ_EINVAL
-    assert _append(_fake_cache(reserved=1)) == kvq.KVQ_EINVAL
+    assert _append(_fake_cache(outlier_count=4)) == kvq.KVQ_EUNSUPPORTED                 # 0 or 8 only
+    assert _append(_fake_cache(outlier_count=8)) == kvq.KVQ_EINVAL                       # buffers missing
+    assert _append(_fake_cache(outlier_count=8, outlier_idx=0xC000, outlier_codes=0xD000,
+                               outlier_scales=0xE004)) == kvq.KVQ_EINVAL                 # misaligned scales
+    assert _append(_fake_cache(outlier_count=8, k_format=8, k_norms=0, outlier_idx=0xC000,
+                               outlier_codes=0xD000, outlier_scales=0xE000)) == kvq.KVQ_EUNSUPPORTED
     assert _append(_fake_cache(), n=0) == kvq.KVQ_OK                     # nothing to do, no launch
     assert "capacity" in kvq.load().kvq_last_error().decode() or True
 

@@ -368,6 +368,53 @@ def test_score_gate_and_spike_flags(dev, name, hq, kv, d):
     assert got.sum() > 0
 
 
+@pytest.mark.parametrize("d,bits,hq,kv", [(128, 4, 32, 8), (128, 4, 4, 4), (256, 3, 4, 4), (64, 2, 8, 4)])
+def test_outlier_two_stream(dev, d, bits, hq, kv):
+    """Key outlier stream: calibration on the first 128 tokens gives the
+    oracle's channels; appended keys have the inlier codes and norms of the
+    keys with those channels zeroed, and the int8 codes and scales of the
+    channels, bit for bit; attention matches the two-stream oracle; and the
+    stream brings the result closer to unquantised attention than the plain
+    codec (the workload's keys carry outlier channels)."""
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=2, q_heads=hq, kv_heads=kv, head_dim=d, seq_len=600,
+                                             splits=3).with_bits(bits)
+    inp = W.generate(wl)
+    T = wl.seq_len
+    s = _signs(d)
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, d, T, _fmt(bits), _fmt(bits), seed=W.SIGN_SEED,
+                                 device=dev, outliers=8)
+    cache.calibrate(_t(inp.k[:, :, :128], dev))
+    idx = O.calibrate_outliers(inp.k[:, :, :128])
+    assert np.array_equal(cache.outlier_idx.cpu().numpy(), idx)
+    assert cache.attention_kernel(wl.q_heads) == "attend_kernel"
+    cache.append(_t(inp.k, dev), _t(inp.v, dev), start_pos=0)
+    q = _t(inp.q, dev)
+    out = cache.decode(q, T, wl.splits).cpu().numpy()
+
+    ki, ko = O.split_outliers(inp.k, idx)
+    kp = cache.k_codes[:, :, :T].cpu().numpy()
+    kn16 = cache.k_norms[:, :, :T].cpu().numpy()
+    check_codes("two-stream K inlier", kp, kn16, ki, bits, d)
+    check_codes("two-stream V", cache.v_codes[:, :, :T].cpu().numpy(), cache.v_norms[:, :, :T].cpu().numpy(),
+                inp.v, bits, d)
+    oc_ref, os_ref = O.quantize_outliers(ko)
+    oc = cache.outlier_codes[:, :, :T].cpu().numpy()
+    osc = cache.outlier_scales[:, :, :T].cpu().numpy()
+    assert np.array_equal(osc, os_ref), "outlier scales differ"
+    assert np.array_equal(oc, oc_ref), f"{int((oc != oc_ref).sum())} outlier codes differ"
+
+    k_rot = _dequant_gpu_cache(kp, kn16, bits, d)
+    v_rot = _dequant_gpu_cache(cache.v_codes[:, :, :T].cpu().numpy(), cache.v_norms[:, :, :T].cpu().numpy(), bits, d)
+    ref = O.two_stream_attention(inp.q.astype(np.float64), k_rot, v_rot, idx, oc, osc, s)
+    _rows_close("two-stream attention", out, ref)
+
+    exact = O.attention_original_domain(inp.q.astype(np.float64), O.rotate(inp.k.astype(np.float64), s),
+                                        O.rotate(inp.v.astype(np.float64), s), s)
+    kc, kn_plain, _ = O.quantize_lm(inp.k, s, bits)
+    plain = O.attention(inp.q.astype(np.float64), O.dequantize_lm(kc, kn_plain, bits), v_rot, s)
+    assert np.linalg.norm(out - exact) < np.linalg.norm(plain - exact)
+
+
 def test_head_dim_64(dev):
     wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, head_dim=64, seq_len=200, splits=3)
     run_case(dev, wl)
