@@ -38,8 +38,9 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "packed-KV decode-attention HBM GB/s (% of peak) + quantize-append tokens/s"
 
 
-def cache_bytes(wl: W.Workload) -> dict:
-    """Algorithmic bytes of the decode read and of one appended token."""
+def cache_bytes(wl: W.Workload, outliers: int = 0) -> dict:
+    """Algorithmic bytes of the decode read and of one appended token (a key
+    outlier stream adds its int8 codes and fp32 scale per token)."""
     d = wl.head_dim
     kb = wl.k_bits
     krow = d * kb // 8
@@ -47,7 +48,7 @@ def cache_bytes(wl: W.Workload) -> dict:
     pairs = wl.batch * wl.kv_heads
     far = wl.far_len
     knorm = 0 if kb == 8 else 2
-    per_tok = krow + knorm + vrow + 2
+    per_tok = krow + knorm + vrow + 2 + (outliers + 4 if outliers else 0)
     near = wl.near_len * 2 * d * 2
     qb = wl.batch * wl.q_heads * d * (4 if wl.dtype == "f32" else 2)
     ob = wl.batch * wl.q_heads * d * 4
@@ -69,6 +70,8 @@ def parse(argv=None):
     ap.add_argument("--gate", action="store_true",
                     help="score-gated attention with spike flags (kvq_decode_attention_gated): gate reference "
                          "= the query's own log-sum-exp from an ungated pass, spike threshold 4 below it")
+    ap.add_argument("--outliers", type=int, default=0, choices=(0, 8),
+                    help="key outlier stream with this many channels, calibrated on the first 256 tokens")
     ap.add_argument("--query-scale", type=float, default=1.0,
                     help="multiply the decode query (a larger scale gives a more peaked softmax)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
@@ -239,7 +242,7 @@ def main(argv=None) -> int:
     if args.splits:
         wl = wl.scaled(splits=args.splits)
     dev = torch.device("cuda")
-    by = cache_bytes(wl)
+    by = cache_bytes(wl, args.outliers)
     print(f"# workload {wl.name}: cache {by['cache'] / 1e6:.1f} MB", file=sys.stderr, flush=True)
 
     inp = W.generate(wl)
@@ -264,7 +267,9 @@ def main(argv=None) -> int:
         c = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, T, fmt[wl.k_bits], fmt[wl.v_bits],
                                  seed=W.SIGN_SEED, device=dev,
                                  near_k=None if kn_dev is None else kn_dev.clone(),
-                                 near_v=None if vn_dev is None else vn_dev.clone())
+                                 near_v=None if vn_dev is None else vn_dev.clone(), outliers=args.outliers)
+        if args.outliers:
+            c.calibrate(k_dev[:, :, :min(256, T)].contiguous())
         caches.append(c)
     stream = torch.cuda.current_stream()
 
@@ -372,7 +377,7 @@ def main(argv=None) -> int:
         "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.q_heads, "kv_heads": wl.kv_heads,
                    "head_dim": wl.head_dim, "seq_len": wl.seq_len, "k_bits": wl.k_bits, "v_bits": wl.v_bits,
                    "splits": S, "near_splits": near_splits, "layer_replicas": R, "launch": "hip_graph",
-                   "gated": bool(args.gate), "query_scale": args.query_scale,
+                   "gated": bool(args.gate), "query_scale": args.query_scale, "outliers": args.outliers,
                    "step_bytes": step_bytes},
         "pct_of_hbm_peak": round(100 * step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
         "append_tokens_per_s": round(append_tok_s, 1),
