@@ -13,7 +13,8 @@ Sources (page titles as published; sections named in each docstring):
   [Foveated] "FoveatedKV" -- sections "The VR headset thing", "Making it fast".
   [Velox]    "I Ported a Google Research Paper to Apple Silicon" (VeloxQuant-MLX)
              -- sections "The Core Idea", "Stage 1: Random Rotation",
-             "Stage 2: Lloyd-Max Scalar Quantization", "The Bit-Packing Problem".
+             "Stage 2: Lloyd-Max Scalar Quantization", "Stage 3: QJL Residual
+             Correction", "The Bit-Packing Problem", "Outlier Two-Stream Cache".
 
 Readings taken where the pages are silent (each also listed in the design
 notes): signs from SplitMix64 (top bit), Sylvester-ordered Hadamard with
@@ -690,4 +691,121 @@ def two_stream_attention(q, k_rot, v_rot, idx, out_codes, out_scale, signs, lse:
     o = rotate_inverse(np.einsum("bht,bhtd->bhd", e / l, vv), signs)
     if lse:
         return o, (m + np.log(l))[..., 0]
+    return o
+
+
+# ----------------------------------------------------------------------------
+# QJL residual sketch  ([Velox] "Stage 3: QJL Residual Correction" and "Memory
+# Layout: What Actually Gets Stored"): the key codec's residual is not stored;
+# its sign sketch under a random Gaussian projection S (m x d) is, one bit per
+# row of S, beside the residual's fp16 norm.  A score adds an estimate of the
+# query's product with the residual.
+#
+# Readings (the page's estimator is garbled: with the query side reduced to
+# signs as printed, the expectation is a function of the angle, not of the
+# product, so it could not be unbiased as the page states it is):
+#   * residual in the rotated domain, r = R k - n16 * c[code] (R is orthonormal
+#     and S Gaussian, so S R is again Gaussian: the same sketch law as on the
+#     original-domain residual);
+#   * z_i = 1 if S_i . r >= 0 else 0 (sign(0) = +1), packed LSB-first;
+#   * the estimate of q~ . r is ||r||_16 * sqrt(pi/2) / m * sum_i (2 z_i - 1)
+#     (S_i . q~): for jointly Gaussian (S_i . q~, S_i . r),
+#     E[(S_i . q~) sign(S_i . r)] = sqrt(2/pi) (q~ . r) / ||r||, so this is the
+#     estimator linear in the stored bits that is unbiased over S;
+#   * m = d (the page's layout: 128 sketch bits at d = 128);
+#   * sign decisions in float64; a product within QJL_WINDOW * ||S_i|| ||r|| of
+#     zero is a boundary case (counted, like a code on a decision midpoint).
+QJL_WINDOW = 1e-12
+
+
+def qjl_residual(x: np.ndarray, signs: np.ndarray, bits: int):
+    """Rotated-domain residual of the Lloyd-Max codec for keys x[..., d]:
+    returns (r float64 [..., d], codes, norm bits, code window), where
+    r = R x - n16 * c[code] (rotation in float64, reconstruction exact)."""
+    codes, norms, window = quantize_lm(x, signs, bits)
+    r = rotate(x, signs) - dequantize_lm(codes, norms, bits)
+    return r, codes, norms, window
+
+
+def qjl_sketch_bits(r: np.ndarray, S: np.ndarray):
+    """Sign bits of S r for residuals r[..., d] and S [..., m, d] (broadcast
+    over the leading axes): (bits uint8 0/1 [..., m], window bool [..., m])."""
+    S64 = np.asarray(S, np.float64)
+    dots = np.einsum("...md,...d->...m", S64, np.asarray(r, np.float64))
+    bits = (dots >= 0.0).astype(np.uint8)
+    scale = np.linalg.norm(S64, axis=-1) * np.linalg.norm(r, axis=-1)[..., None]
+    window = (np.abs(dots) <= QJL_WINDOW * scale) & (scale > 0)
+    return bits, window
+
+
+def qjl_norm_bits(r: np.ndarray):
+    """fp16 bits of ||r|| (round to nearest even from the float64 norm) and a
+    flag for norms within 1e-12 (relative) of an fp16 rounding midpoint."""
+    n = np.sqrt(np.einsum("...d,...d->...", np.asarray(r, np.float64), np.asarray(r, np.float64)))
+    h = n.astype(np.float16)
+    bits = h.view(np.uint16)
+    hv = h.astype(np.float64)
+    up = np.nextafter(h, np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(h, np.float16(0)).astype(np.float64)
+    near = np.minimum(np.abs(n - (hv + up) / 2), np.abs(n - (hv + dn) / 2)) <= 1e-12 * n
+    return bits, near & (n > 0)
+
+
+def qjl_encode(x: np.ndarray, signs: np.ndarray, bits: int, S: np.ndarray):
+    """Key codec plus sketch for keys x[..., d] and S [m, d]: returns a dict
+    with codes, norms, the packed sketch (uint8 [..., m/8]), the sketch bits,
+    the residual norm bits and the three boundary windows (code, sketch, norm)."""
+    r, codes, norms, cwin = qjl_residual(x, signs, bits)
+    z, zwin = qjl_sketch_bits(r, S)
+    rn, rwin = qjl_norm_bits(r)
+    return dict(codes=codes, norms=norms, code_window=cwin, sketch=pack(z, 1), sketch_bits=z,
+                sketch_window=zwin, rnorm=rn, rnorm_window=rwin, residual=r)
+
+
+def qjl_estimate(q_rot: np.ndarray, r_norm, z: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """Estimate of q~ . r from the sketch: ||r|| sqrt(pi/2)/m sum_i (2 z_i - 1)
+    (S_i . q~).  q_rot [..., d], r_norm [...] (a float norm), z [..., m] bits,
+    S [..., m, d]; leading axes broadcast."""
+    S64 = np.asarray(S, np.float64)
+    m = S64.shape[-2]
+    sq = np.einsum("...md,...d->...m", S64, np.asarray(q_rot, np.float64))
+    pm = 2.0 * np.asarray(z, np.float64) - 1.0
+    return np.asarray(r_norm, np.float64) * math.sqrt(math.pi / 2.0) / m * np.einsum("...m,...m->...", pm, sq)
+
+
+def qjl_effective_keys(k_rot: np.ndarray, rnorm_bits: np.ndarray, z: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """Rotated-domain keys whose plain product with q~ is the corrected score:
+    khat + ||r||_16 sqrt(pi/2)/m S^T (2 z - 1)  (the estimate is linear in q~)."""
+    S64 = np.asarray(S, np.float64)
+    m = S64.shape[0]
+    pm = 2.0 * np.asarray(z, np.float64) - 1.0
+    corr = pm @ S64                                                          # [..., d]
+    rn = fp16_bits_to_f64(rnorm_bits)[..., None]
+    return np.asarray(k_rot, np.float64) + rn * math.sqrt(math.pi / 2.0) / m * corr
+
+
+def qjl_attention(q, k_rot, v_rot, rnorm_bits, z, S, signs, lse: bool = False):
+    """Decode attention with QJL-corrected scores, float64, by definition:
+    s_t = (q~ . khat_t + ||r_t||_16 sqrt(pi/2)/m sum_i (2 z_ti - 1)(S_i . q~)) / sqrt(d),
+    q~ = R q; softmax; values as in attention().  k_rot, v_rot [B, Hkv, T, d];
+    rnorm_bits [B, Hkv, T]; z [B, Hkv, T, m]; S [m, d]."""
+    B, Hq, d = q.shape
+    Hkv = k_rot.shape[1]
+    G = Hq // Hkv
+    qr = rotate(q, signs)                                                      # [B, Hq, d]
+    kk = np.repeat(np.asarray(k_rot, np.float64), G, axis=1)
+    vv = np.repeat(np.asarray(v_rot, np.float64), G, axis=1)
+    S64 = np.asarray(S, np.float64)
+    m = S64.shape[0]
+    sq = qr @ S64.T                                                            # [B, Hq, m]
+    pm = 2.0 * np.repeat(np.asarray(z, np.float64), G, axis=1) - 1.0           # [B, Hq, T, m]
+    rn = np.repeat(fp16_bits_to_f64(rnorm_bits), G, axis=1)                    # [B, Hq, T]
+    corr = rn * math.sqrt(math.pi / 2.0) / m * np.einsum("bhtm,bhm->bht", pm, sq)
+    s = (np.einsum("bhd,bhtd->bht", qr, kk) + corr) / math.sqrt(d)
+    mx = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - mx)
+    l = e.sum(axis=-1, keepdims=True)
+    o = rotate_inverse(np.einsum("bht,bhtd->bhd", e / l, vv), signs)
+    if lse:
+        return o, (mx + np.log(l))[..., 0]
     return o

@@ -88,3 +88,34 @@ def test_gqa_head_map_mod_instead_of_div_is_caught(monkeypatch):
         return np.tile(a, (1, G) + (1,) * (a.ndim - 2)) if axis == 1 else good(a, G, axis=axis)
     monkeypatch.setattr(O.np, "repeat", tile)
     _fails(TA.test_gqa_head_map_and_mha_reduction)
+
+
+def test_qjl_constant_pi_over_2_is_caught(monkeypatch):
+    from tests import test_oracle_qjl as TQ
+    good = O.qjl_estimate
+    monkeypatch.setattr(O, "qjl_estimate",
+                        lambda q, rn, z, S: good(q, rn, z, S) * math.sqrt(math.pi / 2))   # pi/2 in place of sqrt(pi/2)
+    _fails(TQ.test_estimator_is_unbiased_with_closed_form_variance)
+
+
+def test_qjl_residual_sign_is_caught(monkeypatch):
+    from tests import test_oracle_qjl as TQ
+    good = O.qjl_residual
+
+    def bad(x, signs, bits):
+        r, c, n, w = good(x, signs, bits)
+        return -r, c, n, w
+    monkeypatch.setattr(O, "qjl_residual", bad)
+    _fails(TQ.test_corrected_scores_have_unit_slope)
+
+
+def test_qjl_sign_of_zero_is_caught(monkeypatch):
+    from tests import test_oracle_qjl as TQ
+    good = O.qjl_sketch_bits
+
+    def bad(r, S):
+        z, w = good(r, S)
+        dots = np.einsum("...md,...d->...m", np.asarray(S, np.float64), np.asarray(r, np.float64))
+        return np.where(dots == 0.0, 0, z).astype(np.uint8), w
+    monkeypatch.setattr(O, "qjl_sketch_bits", bad)
+    _fails(TQ.test_identity_projection_by_hand)
