@@ -44,6 +44,8 @@ class CacheStruct(ctypes.Structure):
         ("near_k", ctypes.c_void_p), ("near_v", ctypes.c_void_p),
         ("near_len", ctypes.c_int32), ("outlier_count", ctypes.c_int32),
         ("outlier_idx", ctypes.c_void_p), ("outlier_codes", ctypes.c_void_p), ("outlier_scales", ctypes.c_void_p),
+        ("qjl_dim", ctypes.c_int32), ("qjl_proj", ctypes.c_void_p), ("qjl_signs", ctypes.c_void_p),
+        ("qjl_norms", ctypes.c_void_p),
     ]
 
 
@@ -162,12 +164,17 @@ class KVCache:
     outlier_idx: object = None       # key outlier stream: [B, Hkv, 8] int32, codes [B, Hkv, cap, 8] int8,
     outlier_codes: object = None     # scales [B, Hkv, cap] float32 (None: stream off)
     outlier_scales: object = None
+    qjl_proj: object = None          # QJL sketch: S^T [d, d] float32, sign bytes [B, Hkv, cap, d/8] uint8,
+    qjl_signs: object = None         # residual norms [B, Hkv, cap] float16 (None: sketch off)
+    qjl_norms: object = None
 
     @classmethod
     def allocate(cls, batch, kv_heads, head_dim, capacity, k_format=KVQ_LM4, v_format=KVQ_LM4,
-                 seed=42, device="cuda", near_k=None, near_v=None, outliers: int = 0):
+                 seed=42, device="cuda", near_k=None, near_v=None, outliers: int = 0, qjl_proj_t=None):
         """outliers: 0, or 8 for the key outlier stream (its channels are
-        chosen by calibrate())."""
+        chosen by calibrate()).  qjl_proj_t: the QJL projection transposed,
+        [head_dim, head_dim] float32 on the device (element (j, i) is
+        S[i][j]), or None for no sketch."""
         import torch
         kr, vr = row_bytes(k_format, head_dim), row_bytes(v_format, head_dim)
         if not kr or not vr:
@@ -187,8 +194,15 @@ class KVCache:
             oi = torch.zeros((batch, kv_heads, outliers), dtype=torch.int32, device=dev)
             oc = torch.zeros((batch, kv_heads, capacity, outliers), dtype=torch.int8, device=dev)
             osc = torch.zeros((batch, kv_heads, capacity), dtype=torch.float32, device=dev)
+        zs = zn = None
+        if qjl_proj_t is not None:
+            _need(qjl_proj_t, "qjl_proj_t", (head_dim, head_dim))
+            if qjl_proj_t.dtype != torch.float32:
+                raise ValueError("qjl_proj_t must be float32")
+            zs = torch.zeros((batch, kv_heads, capacity, head_dim // 8), dtype=torch.uint8, device=dev)
+            zn = torch.zeros((batch, kv_heads, capacity), dtype=torch.float16, device=dev)
         return cls(batch, kv_heads, head_dim, capacity, k_format, v_format, k_codes, k_norms, v_codes,
-                   v_norms, signs, kc, vc, near_k, near_v, oi, oc, osc)
+                   v_norms, signs, kc, vc, near_k, near_v, oi, oc, osc, qjl_proj_t, zs, zn)
 
     @property
     def near_len(self) -> int:
@@ -204,7 +218,9 @@ class KVCache:
                            p(self.signs), p(self.k_centroids), p(self.v_centroids), p(self.near_k),
                            p(self.near_v), self.near_len,
                            0 if self.outlier_idx is None else int(self.outlier_idx.shape[-1]),
-                           p(self.outlier_idx), p(self.outlier_codes), p(self.outlier_scales))
+                           p(self.outlier_idx), p(self.outlier_codes), p(self.outlier_scales),
+                           0 if self.qjl_proj is None else self.head_dim, p(self.qjl_proj), p(self.qjl_signs),
+                           p(self.qjl_norms))
 
     # -- kvq_quantize_append --------------------------------------------------
     def append(self, k, v, start_pos: int):

@@ -43,6 +43,15 @@ kvq_status check_cache(const kvq_cache *c, const char *fn) {
     if (!aligned(c->outlier_idx, 16) || !aligned(c->outlier_codes, 16) || !aligned(c->outlier_scales, 16))
       return fail(KVQ_EINVAL, "%s: outlier stream buffers must be 16-byte aligned", fn);
   }
+  if (c->qjl_dim != 0 && c->qjl_dim != c->head_dim)
+    return fail(KVQ_EUNSUPPORTED, "%s: qjl_dim %d (built: 0, head_dim)", fn, c->qjl_dim);
+  if (c->qjl_dim) {
+    if (!is_lm(c->k_format)) return fail(KVQ_EUNSUPPORTED, "%s: the QJL sketch needs Lloyd-Max keys", fn);
+    if (c->outlier_count) return fail(KVQ_EUNSUPPORTED, "%s: QJL sketch and outlier stream together", fn);
+    if (!c->qjl_proj || !c->qjl_signs || !c->qjl_norms) return fail(KVQ_EINVAL, "%s: QJL buffers are NULL", fn);
+    if (!aligned(c->qjl_proj, 16) || !aligned(c->qjl_signs, 16) || !aligned(c->qjl_norms, 16))
+      return fail(KVQ_EINVAL, "%s: QJL buffers must be 16-byte aligned", fn);
+  }
   return KVQ_OK;
 }
 
@@ -76,6 +85,11 @@ kvq_status kvq_quantize_append(const kvq_cache *cache, const void *k, const void
                     static_cast<uint8_t *>(cache->k_codes), static_cast<uint8_t *>(cache->v_codes),
                     cache->k_norms, cache->v_norms, cache->signs, cache->k_centroids, cache->v_centroids,
                     cache->outlier_count ? cache->outlier_idx : nullptr, cache->outlier_codes, cache->outlier_scales};
+  if (cache->qjl_dim) {
+    a.qjl_proj = cache->qjl_proj;
+    a.qjl_signs = cache->qjl_signs;
+    a.qjl_norms = cache->qjl_norms;
+  }
   bool ok = true;
   hipError_t e = kvq::launch_append(a, stream, &ok);
   if (!ok) return kvq::fail(KVQ_EUNSUPPORTED, "%s: format combination not built", fn);
@@ -118,6 +132,11 @@ kvq_status attend_args(const char *fn, const kvq_cache *cache, const void *q, in
     out->outlier_codes = cache->outlier_codes;
     out->outlier_scales = cache->outlier_scales;
   }
+  if (cache->qjl_dim) {
+    out->qjl_proj = cache->qjl_proj;
+    out->qjl_signs = cache->qjl_signs;
+    out->qjl_norms = cache->qjl_norms;
+  }
   return KVQ_OK;
 }
 
@@ -155,8 +174,8 @@ kvq_status kvq_decode_attention_gated(const kvq_cache *cache, const void *q, int
                                     part_ml, &a);
   if (st != KVQ_OK) return st;
   if (!gate_ref && !spike_ref) return kvq::fail(KVQ_EINVAL, "%s: neither gate_ref nor spike_ref given", fn);
-  if (cache->outlier_count)
-    return kvq::fail(KVQ_EUNSUPPORTED, "%s: the gated pass is not built for a key outlier stream", fn);
+  if (cache->outlier_count || cache->qjl_dim)
+    return kvq::fail(KVQ_EUNSUPPORTED, "%s: the gated pass is not built for an outlier stream or QJL sketch", fn);
   if ((spike_ref == nullptr) != (spike_bits == nullptr))
     return kvq::fail(KVQ_EINVAL, "%s: spike_ref and spike_bits go together", fn);
   if (!aligned(gate_ref, 4) || !aligned(spike_ref, 4) || !aligned(spike_bits, 4))
@@ -195,6 +214,7 @@ const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads,
                     cache->k_norms, cache->v_norms, cache->signs, cache->k_centroids, cache->v_centroids,
                     cache->near_k, cache->near_v, nullptr, nullptr};
   if (cache->outlier_count) a.outlier_idx = cache->outlier_idx;
+  if (cache->qjl_dim) a.qjl_proj = cache->qjl_proj;
   return kvq::attend_kernel_name(a);
 }
 

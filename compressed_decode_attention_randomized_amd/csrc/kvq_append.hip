@@ -16,9 +16,17 @@
 //      16 (2-bit) stream bits at byte offset lane*bits.
 // fp8 keys skip the norm: y = z / sqrt(D) is rounded to E4M3FN directly from
 // float64 (nearest-even, saturating at 448).
+// With a QJL sketch, each key's rotated-domain residual r = z / sqrt(D) -
+// n16 * c[code] is kept in LDS in float64 (the lane computes its 8
+// coordinates; the fp16 norm of r is decided exactly like the key norm); the
+// work-group then forms the D x D product of the projection with the
+// residuals of its vectors (one thread per sketch row and 8 vectors, the
+// projection column read coalesced, residuals as LDS broadcasts), and each
+// sign bit is S_i . r >= 0, gathered 64 rows at a time by a wave ballot.
 // Sources: "The Engineering Behind AdapTQ", "The Math Fix" (sign flip + FWHT,
 // add/sub only); VeloxQuant-MLX "Stage 2" (normalise, fp16 norm, nearest
-// centroid) and "The Bit-Packing Problem" (LSB-first layout); "FoveatedKV",
+// centroid) and "The Bit-Packing Problem" (LSB-first layout), "Stage 3: QJL Residual
+// Correction" (sign sketch of the residual, its fp16 norm); "FoveatedKV",
 // "The VR headset thing" (fp8 E4M3 far-tier keys).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -112,13 +120,22 @@ struct Stream {
   const int32_t *out_idx;
   int8_t *out_codes;
   float *out_scales;
+  // QJL residual sketch (keys; NULL proj: off): S^T [D][D] float32, sign
+  // bytes [..][capacity][D/8], fp16 residual norms [..][capacity]
+  const float *qjl_proj;
+  uint8_t *qjl_signs;
+  uint16_t *qjl_norms;
 };
+
+// Residuals of a work-group's vectors, [D][VPB] float64 (VPB * D = 2048).
+constexpr int kResidual = 2048;
 
 // Encode the vectors of one stream (keys or values).  BITS in {2,3,4} for
 // Lloyd-Max codes, 8 for fp8.
-template <int D, int BITS, typename T>
+template <int D, int BITS, typename T, bool QJL = false>
 __device__ void encode(const Stream &st, const int8_t *__restrict__ signs, int nvec, int n_new,
-                       int capacity, int start_pos, double *mids) {
+                       int capacity, int start_pos, double *mids, double *cents = nullptr,
+                       double *resid = nullptr) {
   constexpr int LPV = D / 8;            // lanes per vector
   constexpr int VPB = kBlock / LPV;     // vectors per block
   constexpr int L = 1 << (BITS == 8 ? 1 : BITS);
@@ -139,6 +156,7 @@ __device__ void encode(const Stream &st, const int8_t *__restrict__ signs, int n
     if (threadIdx.x < L - 1) {
       mids[threadIdx.x] = 0.5 * ((double)st.centroids[threadIdx.x] + (double)st.centroids[threadIdx.x + 1]);
     }
+    if (QJL && threadIdx.x < L) cents[threadIdx.x] = (double)st.centroids[threadIdx.x];
     __syncthreads();
   }
   if (!live) return;
@@ -229,7 +247,8 @@ __device__ void encode(const Stream &st, const int8_t *__restrict__ signs, int n
     return;
   }
 
-  if (lv == 0) st.norms[slot] = fp16_norm(ss);
+  const uint16_t n16 = fp16_norm(ss);
+  if (lv == 0) st.norms[slot] = n16;
 
   uint32_t packed = 0;
   if (ss > 0.0) {
@@ -257,14 +276,76 @@ __device__ void encode(const Stream &st, const int8_t *__restrict__ signs, int n
     row[lv * 3 + 1] = (uint8_t)((packed >> 8) & 0xFF);
     row[lv * 3 + 2] = (uint8_t)((packed >> 16) & 0xFF);
   }
+
+  if constexpr (QJL && BITS != 8) {
+    // residual in the rotated domain: y_j - n16 * c[code_j], y = z / sqrt(D)
+    // (n16 * c is exact in float64, so r takes two roundings: y's and the
+    // difference's)
+    const double n = (n16 == 0) ? 0.0 : half_bits_value(n16);
+    const int vloc = threadIdx.x / LPV;
+    double rss = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = (int)((packed >> (BITS * e)) & (uint32_t)(L - 1));
+      const double r = x[e] / sqrt((double)D) - n * cents[c];
+      rss = fma(r, r, rss);
+      resid[(lv * 8 + e) * VPB + vloc] = r;
+    }
+#pragma unroll
+    for (int m = 1; m < LPV; m <<= 1) rss += __shfl_xor(rss, m);
+    if (lv == 0) st.qjl_norms[slot] = fp16_norm(rss);
+  }
 }
 
-template <int D, int KB, int VB, typename T>
+// Sign sketch of the residuals in `resid` (the work-group's VPB vectors):
+// thread (i, g) forms S_i . r for sketch row i = tid % D and vectors
+// 8g .. 8g+7; a wave holds 64 consecutive rows of 8 vectors, and one ballot
+// per vector gives 64 sign bits, stored as one 8-byte word by lane k for
+// vector k.
+template <int D>
+__device__ void sketch(const Stream &st, const double *resid, int nvec, int n_new, int capacity, int start_pos) {
+  constexpr int LPV = D / 8, VPB = kBlock / LPV, kPer = 8;
+  static_assert(VPB * D == kResidual && kPer * kBlock == kResidual && D >= 64, "sketch mapping");
+  const int i = threadIdx.x % D, g = threadIdx.x / D;
+  const int lane = threadIdx.x & 63;
+  double acc[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) acc[k] = 0.0;
+  const float *col = st.qjl_proj + i;
+#pragma unroll 4
+  for (int j = 0; j < D; ++j) {
+    const double s = (double)col[(size_t)j * D];
+    const double *rv = resid + j * VPB + g * kPer;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) acc[k] = fma(s, rv[k], acc[k]);
+  }
+  const int i0 = i - lane;                       // the wave's first sketch row
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(acc[k] >= 0.0);
+    const int vec = blockIdx.x * VPB + g * kPer + k;
+    if (lane == k && vec < nvec) {
+      const int bvec = vec / n_new;
+      const size_t slot = (size_t)bvec * capacity + start_pos + (vec - bvec * n_new);
+      *reinterpret_cast<uint64_t *>(st.qjl_signs + slot * (D / 8) + i0 / 8) = bits;
+    }
+  }
+}
+
+template <int D, int KB, int VB, typename T, bool QJL = false>
 __global__ __launch_bounds__(kBlock) void append_kernel(Stream ks, Stream vs, const int8_t *__restrict__ signs,
                                                         int nvec, int n_new, int capacity, int start_pos) {
   __shared__ double mids[15];
   if (blockIdx.y == 0) {
-    encode<D, KB, T>(ks, signs, nvec, n_new, capacity, start_pos, mids);
+    if constexpr (QJL) {
+      __shared__ double cents[16];
+      __shared__ double resid[kResidual];
+      encode<D, KB, T, true>(ks, signs, nvec, n_new, capacity, start_pos, mids, cents, resid);
+      __syncthreads();
+      sketch<D>(ks, resid, nvec, n_new, capacity, start_pos);
+    } else {
+      encode<D, KB, T>(ks, signs, nvec, n_new, capacity, start_pos, mids);
+    }
   } else {
     encode<D, VB, T>(vs, signs, nvec, n_new, capacity, start_pos, mids);
   }
@@ -275,8 +356,21 @@ hipError_t launch3(const AppendArgs &a, hipStream_t stream) {
   const int nvec = a.batch * a.kv_heads * a.n_new;
   constexpr int VPB = kBlock / (D / 8);
   dim3 grid((nvec + VPB - 1) / VPB, 2);
-  Stream ks{a.k, a.k_codes, a.k_norms, a.k_centroids, a.outlier_idx, a.outlier_codes, a.outlier_scales};
-  Stream vs{a.v, a.v_codes, a.v_norms, a.v_centroids, nullptr, nullptr, nullptr};
+  Stream ks{a.k, a.k_codes, a.k_norms, a.k_centroids, a.outlier_idx, a.outlier_codes, a.outlier_scales,
+            a.qjl_proj, a.qjl_signs, a.qjl_norms};
+  Stream vs{a.v, a.v_codes, a.v_norms, a.v_centroids, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if constexpr (KB != 8) {
+    if (a.qjl_proj) {
+      if (a.in_f16) {
+        hipLaunchKernelGGL((append_kernel<D, KB, VB, _Float16, true>), grid, dim3(kBlock), 0, stream, ks, vs, a.signs,
+                           nvec, a.n_new, a.capacity, a.start_pos);
+      } else {
+        hipLaunchKernelGGL((append_kernel<D, KB, VB, float, true>), grid, dim3(kBlock), 0, stream, ks, vs, a.signs,
+                           nvec, a.n_new, a.capacity, a.start_pos);
+      }
+      return hipGetLastError();
+    }
+  }
   if (a.in_f16) {
     hipLaunchKernelGGL((append_kernel<D, KB, VB, _Float16>), grid, dim3(kBlock), 0, stream, ks, vs, a.signs, nvec,
                        a.n_new, a.capacity, a.start_pos);

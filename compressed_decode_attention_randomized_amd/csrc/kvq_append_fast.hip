@@ -422,7 +422,7 @@ bool fast_append_supported(const AppendArgs &a) {
   // per-block code table
   const bool lm = a.k_format >= 2 && a.k_format <= 4 && a.v_format >= 2 && a.v_format <= 4;
   return lm && (a.head_dim == 64 || a.head_dim == 128 || a.head_dim == 256) && a.batch * a.kv_heads <= 65535 &&
-         a.n_new >= 64 && a.outlier_idx == nullptr;
+         a.n_new >= 64 && a.outlier_idx == nullptr && a.qjl_proj == nullptr;
 }
 
 hipError_t launch_append_fast(const AppendArgs &a, hipStream_t stream) {

@@ -21,11 +21,18 @@
 //      the rotated domain straight from their codes;
 //   4. the slot states are merged by xor-shuffles inside the wave and through
 //      LDS across the four waves; the split writes (m, l) and sum p v / l.
+// Key side streams (far tier): an outlier stream adds q[idx] . (code * scale)
+// to each score after the reduction; a QJL sketch adds
+// ||r|| sqrt(pi/2)/m sum_i (2 z_i - 1) (S q~)_i, with S q~ formed once per
+// work-group into LDS and each lane scoring its slice of the sketch bits
+// before the reduction.
 // Near-tier splits run the same loop on fp16 rows in the original domain.
 // Sources: "The Engineering Behind AdapTQ", "Engineering the Hot Path" (rotate
 // q once, score from codes through a table, no dequantize pass); "FoveatedKV",
 // "Making it fast" (fused split-K dispatch over both tiers, q pre-scaled,
-// online softmax with one exp per score, fp8 keys for the far tier).
+// online softmax with one exp per score, fp8 keys for the far tier);
+// VeloxQuant-MLX, "Stage 3: QJL Residual Correction" and "Outlier Two-Stream
+// Cache" (the two key side streams).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -56,7 +63,13 @@ struct Params {
   const int32_t *out_idx;              // key outlier stream ([B][Hkv][8] channels) or NULL
   const int8_t *out_codes;             // [B][Hkv][capacity][8]
   const float *out_scales;             // [B][Hkv][capacity]
+  const float *qjl_proj;               // QJL sketch: S^T [D][D] or NULL
+  const uint8_t *qjl_signs;            // [B][Hkv][capacity][D/8]
+  const uint16_t *qjl_norms;           // [B][Hkv][capacity] fp16
 };
+
+// Key side streams of the far tier.
+constexpr int kNoExtra = 0, kOutliers = 1, kQjl = 2;
 
 // Score gate and spike flags of the far tier for one block of tokens, the G
 // heads of one KV head (log2 score units, as the kernel keeps them).
@@ -183,10 +196,15 @@ __device__ inline float2_t pair_entry(const uint8_t *tab, uint32_t f, uint32_t s
 // Far tier: packed Lloyd-Max (KB in 2..4) or fp8 (KB = 8) keys, Lloyd-Max values.
 // fp8 keys decode in hardware (v_cvt_pk_f32_fp8: OCP E4M3FN, exact in fp32),
 // 2- and 3-bit codes through pair tables, 4-bit codes one table read each.
-// OUT: the keys carry an outlier stream; every score gains
+// X = kOutliers: the keys carry an outlier stream; every score gains
 // q[idx] . (code * scale) / sqrt(d) (qo holds q[idx] pre-scaled).
-template <int D, int KB, int VB, int G, int DPL, bool OUT = false>
+// X = kQjl: the keys carry a QJL sketch; the lane's partial score becomes
+// nk * (its codec part) + rho * sum_e (2 z_e - 1) p_e over its DPL sketch
+// bits, rho = ||r||_16 sqrt(pi/2)/D and p = S q~ pre-scaled (pq holds 2 p,
+// psum the slice's sum of p), so the reduced partial is the whole score.
+template <int D, int KB, int VB, int G, int DPL, int X = kNoExtra>
 struct FarTier {
+  static constexpr bool OUT = X == kOutliers, QJL = X == kQjl;
   static constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
   static constexpr int KNB = DPL * KB / 8, VNB = DPL * VB / 8;
   static constexpr bool kKeyPairs = KB == 2 || KB == 3, kValPairs = VB == 2 || VB == 3;
@@ -204,6 +222,12 @@ struct FarTier {
   float qo[G][kOutlierCount];
   uint2 oc;
   float osc;
+  // QJL sketch (QJL only)
+  const uint8_t *zs0;
+  const uint16_t *zn0;
+  float pq[QJL ? G : 1][QJL ? DPL : 1], psum[QJL ? G : 1];
+  uint32_t zw;
+  float rho;
 
   __device__ void load(int t, int ds) {
     load_keys(t, ds);
@@ -215,6 +239,11 @@ struct FarTier {
     if constexpr (OUT) {
       oc = *reinterpret_cast<const uint2 *>(oc0 + (size_t)t * kOutlierCount);
       osc = os0[t];
+    }
+    if constexpr (QJL) {
+      const uint8_t *zr = zs0 + (size_t)t * (D / 8);
+      zw = (DPL == 32) ? reinterpret_cast<const uint32_t *>(zr)[ds] : reinterpret_cast<const uint16_t *>(zr)[ds];
+      rho = half_to_float(zn0[t]) * (1.2533141373155003f / (float)D);   // sqrt(pi/2) / m, m = D
     }
   }
   // the outlier stream's part of head h's score (log2 units)
@@ -262,8 +291,21 @@ struct FarTier {
         for (int h = 0; h < G; ++h) part[h] = fmaf(qr[h][e], c, part[h]);
       }
     }
+    if constexpr (QJL) {
+      float a[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) a[h] = -psum[h];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const float b = (float)((zw >> e) & 1u);
+#pragma unroll
+        for (int h = 0; h < G; ++h) a[h] = fmaf(pq[h][e], b, a[h]);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) part[h] = fmaf(rho, a[h], part[h] * nk);
+    }
   }
-  __device__ float key_scale() const { return nk; }
+  __device__ float key_scale() const { return QJL ? 1.f : nk; }
   __device__ void accumulate(const float (&p)[G], State<G, DPL> &st) const {
     float w[G];
 #pragma unroll
@@ -443,9 +485,10 @@ __device__ void token_loop_gated(const Tier &proto, const float (&qr)[G][DPL], S
 
 // NEAR: the launch has near-tier splits (without them the kernel carries no
 // registers for the near path).
-// GATED: score gate and spike flags; OUT: key outlier stream.
-template <int D, int KB, int VB, int G, bool NEAR, bool GATED, bool OUT = false>
+// GATED: score gate and spike flags; X: key side stream (none, outliers, QJL).
+template <int D, int KB, int VB, int G, bool NEAR, bool GATED, int X = kNoExtra>
 __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
+  constexpr bool OUT = X == kOutliers, QJL = X == kQjl;
   // G = 1: 32 coordinates per lane, except where near-tier fp16 rows would
   // double the pipelined registers; loads pipelined
   constexpr int DPL = (G == 1 && !NEAR) ? 32 : 16;
@@ -460,6 +503,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
   __shared__ __attribute__((aligned(16))) uint8_t pairtab[(kPairK + kPairV) > 0 ? kPairK + kPairV : 16];
   __shared__ float red_ml[kWaves][G][2];
   __shared__ float red_acc[kWaves][G][D];
+  __shared__ float ps[QJL ? G : 1][QJL ? D : 1];
 
   const int tid = threadIdx.x;
   const int split = blockIdx.x;
@@ -509,9 +553,35 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     }
   }
 
+  const float prescale = near ? kLog2e / sqrtf((float)D) : kLog2e / (float)D;
+  if constexpr (QJL) {
+    if (!near) {
+      // p = S (q~ pre-scaled) per head: thread (i, h0) forms row i for heads
+      // h0, h0 + kBlock/D, ...; the projection column is read coalesced and
+      // the query element is an LDS broadcast
+      constexpr int HS = kBlock / D, HP = (G + HS - 1) / HS;
+      const int i = tid % D, h0 = tid / D;
+      float acc[HP];
+#pragma unroll
+      for (int k = 0; k < HP; ++k) acc[k] = 0.f;
+#pragma unroll 4
+      for (int j = 0; j < D; ++j) {
+        const float sv = P.qjl_proj[(size_t)j * D + i];
+#pragma unroll
+        for (int k = 0; k < HP; ++k) {
+          if (h0 + k * HS < G) acc[k] = fmaf(sv, qs[h0 + k * HS][j], acc[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < HP; ++k) {
+        if (h0 + k * HS < G) ps[h0 + k * HS][i] = acc[k] * prescale;
+      }
+      __syncthreads();
+    }
+  }
+
   const int lane = tid & 63, wave = tid >> 6;
   const int ds = lane % LPT;
-  const float prescale = near ? kLog2e / sqrtf((float)D) : kLog2e / (float)D;
   float qr[G][DPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -535,7 +605,22 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     const int fs = split - P.num_near_splits;
     const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + 31) / 32 * 32;
     const int t0 = min(P.seq_len, fs * chunk), t1 = min(P.seq_len, t0 + chunk);
-    FarTier<D, KB, VB, G, DPL, OUT> tier;
+    FarTier<D, KB, VB, G, DPL, X> tier;
+    if constexpr (QJL) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+          const float v = ps[h][ds * DPL + e];
+          tier.pq[h][e] = 2.f * v;
+          sum += v;
+        }
+        tier.psum[h] = sum;
+      }
+      tier.zs0 = P.qjl_signs + (size_t)bh * P.capacity * (D / 8);
+      tier.zn0 = P.qjl_norms + (size_t)bh * P.capacity;
+    }
     if constexpr (OUT) {
       // the query at the outlier channels (original domain), scaled to log2 units of s
       const float sc = kLog2e / sqrtf((float)D);
@@ -622,13 +707,21 @@ hipError_t go(const AttendArgs &a, hipStream_t stream) {
   Params P{a.q, a.q_f16, a.kv_heads, a.q_heads, a.capacity, a.seq_len, a.num_splits, a.num_near_splits,
            a.near_len, a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids, a.v_centroids,
            a.near_k, a.near_v, a.part_o, a.part_ml, a.gate_ref, a.spike_ref, a.spike_bits, (a.seq_len + 31) / 32,
-           a.outlier_idx, a.outlier_codes, a.outlier_scales};
+           a.outlier_idx, a.outlier_codes, a.outlier_scales, a.qjl_proj, a.qjl_signs, a.qjl_norms};
   dim3 grid(a.near_only ? a.num_near_splits : a.num_near_splits + a.num_splits, a.batch * a.kv_heads);
   const bool near = a.num_near_splits > 0, gated = a.gated != 0;
   if constexpr (KB != 8) {
+    if (a.qjl_proj) {
+      if (near) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true, false, kQjl>), grid, dim3(kBlock), 0, stream, P);
+      else hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false, false, kQjl>), grid, dim3(kBlock), 0, stream, P);
+      return hipGetLastError();
+    }
     if (a.outlier_idx) {
-      if (near) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true, false, true>), grid, dim3(kBlock), 0, stream, P);
-      else hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false, false, true>), grid, dim3(kBlock), 0, stream, P);
+      if (near) {
+        hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true, false, kOutliers>), grid, dim3(kBlock), 0, stream, P);
+      } else {
+        hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false, false, kOutliers>), grid, dim3(kBlock), 0, stream, P);
+      }
       return hipGetLastError();
     }
   }
@@ -643,7 +736,7 @@ template <int D, int KB, int VB>
 hipError_t by_group(const AttendArgs &a, hipStream_t stream, bool *ok) {
   const int G = a.q_heads / a.kv_heads;
   if (G == 1) return go<D, KB, VB, 1>(a, stream);
-  if constexpr (KB != 3 && VB != 3) {
+  if constexpr (VB != 3) {
     if (G == 2) return go<D, KB, VB, 2>(a, stream);
     if (G == 4) return go<D, KB, VB, 4>(a, stream);
   }
@@ -657,6 +750,7 @@ hipError_t by_format(const AttendArgs &a, hipStream_t stream, bool *ok) {
   if (kf == 2 && vf == 2) return by_group<D, 2, 2>(a, stream, ok);
   if (kf == 3 && vf == 3) return by_group<D, 3, 3>(a, stream, ok);
   if (kf == 4 && vf == 4) return by_group<D, 4, 4>(a, stream, ok);
+  if (kf == 3 && vf == 4) return by_group<D, 3, 4>(a, stream, ok);
   if (kf == 8 && vf == 4) return by_group<D, 8, 4>(a, stream, ok);
   *ok = false;
   return hipSuccess;
@@ -686,7 +780,7 @@ AttendArgs far_part(const AttendArgs &a) {
 }  // namespace
 
 const char *attend_kernel_name(const AttendArgs &a) {
-  if (a.outlier_idx) return "attend_kernel";
+  if (a.outlier_idx || a.qjl_proj) return "attend_kernel";
   if (a.num_near_splits > 0) {
     const AttendArgs f = far_part(a);
     if (pair_attend_supported(f)) return "attend_pair_kernel+attend_kernel";
@@ -705,8 +799,8 @@ hipError_t launch_attend_gated(const AttendArgs &a, hipStream_t stream, bool *su
 }
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported) {
-  // The key outlier stream is added to the scores by the VALU kernel only.
-  if (a.outlier_idx) return launch_valu(a, stream, supported);
+  // Key side streams (outliers, QJL sketch) are scored by the VALU kernel only.
+  if (a.outlier_idx || a.qjl_proj) return launch_valu(a, stream, supported);
   // A near tier (fp16 rows, original domain) beside 4-bit or 2-bit far codes
   // that a pair-table kernel covers: the near splits run on the VALU kernel
   // and the far splits on the pair-table kernel, two launches on the stream

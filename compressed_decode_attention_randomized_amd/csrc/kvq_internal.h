@@ -30,6 +30,11 @@ struct AppendArgs {
   const int32_t *outlier_idx = nullptr;
   int8_t *outlier_codes = nullptr;
   float *outlier_scales = nullptr;
+  // QJL residual sketch of the keys (NULL proj: off; m = head_dim): S^T
+  // [d][m] float32, sign bits [B][Hkv][capacity][m/8], fp16 norms [B][Hkv][capacity]
+  const float *qjl_proj = nullptr;
+  uint8_t *qjl_signs = nullptr;
+  uint16_t *qjl_norms = nullptr;
 };
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream, bool *supported);
 // Bulk-throughput variant (Lloyd-Max keys and values, head_dim 64/128/256).
@@ -57,6 +62,10 @@ struct AttendArgs {
   const int32_t *outlier_idx = nullptr;
   const int8_t *outlier_codes = nullptr;
   const float *outlier_scales = nullptr;
+  // QJL residual sketch of the keys (NULL proj: off)
+  const float *qjl_proj = nullptr;
+  const uint8_t *qjl_signs = nullptr;
+  const uint16_t *qjl_norms = nullptr;
 };
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported);
 // Score-gated attention with spike flags (a.gate_ref / a.spike_ref / a.spike_bits):

@@ -90,6 +90,20 @@ typedef enum { KVQ_LM2 = 2, KVQ_LM3 = 3, KVQ_LM4 = 4, KVQ_FP8_E4M3 = 8 } kvq_for
  *   per-token scale RN_fp32(max |x_o| / 127) (code = nearest integer of
  *   x_o / scale, ties to even, zero scale gives zero codes); attention adds
  *   q[idx] . (code * scale) / sqrt(d) to every far-tier score.
+ *   QJL residual sketch of the keys ("Stage 3: QJL Residual Correction",
+ *   "Memory Layout"), Lloyd-Max keys only, not together with the outlier
+ *   stream; qjl_dim 0 (off) or head_dim (m sketch rows, m = head_dim):
+ *     qjl_proj   [head_dim][m] float32, the projection S transposed:
+ *                element (j, i) is S[i][j]; caller-drawn (Gaussian entries
+ *                make the estimate below unbiased), read-only
+ *     qjl_signs  [batch][kv_heads][capacity][m/8] bytes: bit i (LSB-first
+ *                stream) is 1 iff S_i . r >= 0, r = R k - n * c[code] the key
+ *                codec's rotated-domain residual (float64 on the device)
+ *     qjl_norms  [batch][kv_heads][capacity] fp16 bits of ||r||
+ *   With the sketch on, attention adds
+ *   ||r||_16 sqrt(pi/2)/m sum_i (2 z_i - 1) (S_i . R q) / sqrt(d) to every
+ *   far-tier score, an estimate of the query's product with the residual
+ *   that is unbiased over Gaussian S.
  * Code, norm and sign buffers must be 16-byte aligned and capacity a multiple of 16. */
 typedef struct kvq_cache {
   int32_t batch;
@@ -112,6 +126,10 @@ typedef struct kvq_cache {
   const int32_t *outlier_idx;
   int8_t *outlier_codes;
   float *outlier_scales;
+  int32_t qjl_dim;           /* 0 or head_dim */
+  const float *qjl_proj;
+  uint8_t *qjl_signs;
+  uint16_t *qjl_norms;
 } kvq_cache;
 
 /* Bytes of one packed row ("The Bit-Packing Problem"): head_dim*bits/8 for
@@ -192,7 +210,8 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q
  *               the caller before the call (bits are or-ed in); required
  *               exactly when spike_ref is given.
  * At least one of gate_ref and spike_ref must be given.  All three are
- * caller-owned and 4-byte aligned.  Served by the VALU kernel for every
+ * caller-owned and 4-byte aligned.  Caches with an outlier stream or a QJL
+ * sketch are not served (KVQ_EUNSUPPORTED).  Served by the VALU kernel for every
  * format (query groups G = 1, 2, 4; 3-bit codes at G = 1).  Errors as
  * kvq_decode_attention, and KVQ_EINVAL for a missing or unpaired reference. */
 kvq_status kvq_decode_attention_gated(const kvq_cache *cache, const void *q, int32_t q_dtype,

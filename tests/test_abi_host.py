@@ -58,7 +58,7 @@ def _fake_cache(**over):
     base = dict(batch=2, kv_heads=2, head_dim=128, capacity=64, k_format=4, v_format=4,
                 k_codes=0x1000, k_norms=0x2000, v_codes=0x3000, v_norms=0x4000, signs=0x5000,
                 k_centroids=0x6000, v_centroids=0x7000, near_k=0, near_v=0, near_len=0, outlier_count=0,
-                outlier_idx=0, outlier_codes=0, outlier_scales=0)
+                outlier_idx=0, outlier_codes=0, outlier_scales=0, qjl_dim=0, qjl_proj=0, qjl_signs=0, qjl_norms=0)
     base.update(over)
     return kvq.CacheStruct(**base)
 
@@ -116,6 +116,14 @@ def test_append_validation():
                                outlier_scales=0xE004)) == kvq.KVQ_EINVAL                 # misaligned scales
     assert _append(_fake_cache(outlier_count=8, k_format=8, k_norms=0, outlier_idx=0xC000,
                                outlier_codes=0xD000, outlier_scales=0xE000)) == kvq.KVQ_EUNSUPPORTED
+    qjl = dict(qjl_dim=128, qjl_proj=0xC000, qjl_signs=0xD000, qjl_norms=0xE000)
+    assert _append(_fake_cache(**{**qjl, "qjl_dim": 64})) == kvq.KVQ_EUNSUPPORTED        # m = head_dim only
+    assert _append(_fake_cache(**{**qjl, "qjl_signs": 0})) == kvq.KVQ_EINVAL              # buffers missing
+    assert _append(_fake_cache(**{**qjl, "qjl_norms": 0xE002})) == kvq.KVQ_EINVAL         # misaligned norms
+    assert _append(_fake_cache(**qjl, k_format=8, k_norms=0)) == kvq.KVQ_EUNSUPPORTED     # Lloyd-Max keys only
+    assert _append(_fake_cache(**qjl, outlier_count=8, outlier_idx=0xC000, outlier_codes=0xD000,
+                               outlier_scales=0xE000)) == kvq.KVQ_EUNSUPPORTED          # one side stream at a time
+    assert _gated(_fake_cache(**qjl)) == kvq.KVQ_EUNSUPPORTED
     assert _append(_fake_cache(), n=0) == kvq.KVQ_OK                     # nothing to do, no launch
     assert "capacity" in kvq.load().kvq_last_error().decode() or True
 
@@ -162,6 +170,9 @@ def test_attention_kernel_choice():
     assert name(near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_pair_kernel+attend_kernel"
     assert name(head_dim=256, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_wide_kernel+attend_kernel"
     assert name(k_format=3, v_format=3, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_kernel"
+    qjl = dict(qjl_dim=128, qjl_proj=0xC000, qjl_signs=0xD000, qjl_norms=0xE000)
+    assert name(**qjl) == "attend_kernel"                                 # the QJL sketch: VALU kernel only
+    assert name(k_format=3, v_format=4, hq=32) == "attend_kernel"         # 3-bit keys beside 4-bit values
     assert name(hq=3) is None and name(head_dim=96) is None
 
 

@@ -415,6 +415,78 @@ def test_outlier_two_stream(dev, d, bits, hq, kv):
     assert np.linalg.norm(out - exact) < np.linalg.norm(plain - exact)
 
 
+def _check_sketch(name, cache, x, kb, d, S, T):
+    """QJL sketch bits and residual norms of the GPU cache against the
+    oracle, bit for bit outside their boundary windows, on every row whose
+    codes agree with the oracle's (a code inside the decision window changes
+    the residual)."""
+    enc = O.qjl_encode(x, _signs(d), kb, S)
+    codes = O.unpack(cache.k_codes[:, :, :T].cpu().numpy(), kb, d)
+    same = (codes == enc["codes"]).all(axis=-1)
+    assert same.mean() > 0.99, f"{name}: rows with differing codes {1 - same.mean():.2e}"
+    z = O.unpack(cache.qjl_signs[:, :, :T].cpu().numpy(), 1, d)
+    rn = cache.qjl_norms[:, :, :T].cpu().numpy().view(np.uint16)
+    bad_z = (z != enc["sketch_bits"]) & same[..., None]
+    assert not (bad_z & ~enc["sketch_window"]).any(), f"{name}: {int(bad_z.sum())} sketch bits differ"
+    bad_n = (rn != enc["rnorm"]) & same
+    assert not (bad_n & ~enc["rnorm_window"]).any(), f"{name}: {int(bad_n.sum())} residual norms differ"
+    return z, rn
+
+
+@pytest.mark.parametrize("d,kb,vb,hq,kv,dtype,near", [(128, 3, 4, 32, 8, "f16", False),
+                                                      (128, 4, 4, 4, 4, "f16", False),
+                                                      (256, 2, 2, 8, 4, "f16", False),
+                                                      (64, 3, 3, 4, 4, "f32", False),
+                                                      (128, 4, 4, 32, 8, "f16", True)])
+def test_qjl_residual_sketch(dev, d, kb, vb, hq, kv, dtype, near):
+    """QJL residual sketch: appended keys carry the oracle's codes, sketch
+    bits and residual norms; attention matches the oracle's corrected scores
+    (with a near tier: the fp16 decode buffer in the same launch)."""
+    base = W.WORKLOADS["decode_buffer" if near else "llama7b_layer"]
+    wl = base.scaled(batch=2, q_heads=hq, kv_heads=kv, head_dim=d, seq_len=600, splits=3, dtype=dtype,
+                     k_bits=kb, v_bits=vb, near_fraction=(64 / 600 if near else 0.0), near_splits=2)
+    inp = W.generate(wl)
+    S = W.qjl_projection(d)
+    if near:
+        kn, vn = inp.tier("near")
+        kf, vf = inp.tier("far")
+    else:
+        kn = vn = None
+        kf, vf = inp.k, inp.v
+    T = kf.shape[2]
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, d, T, _fmt(kb), _fmt(vb), seed=W.SIGN_SEED, device=dev,
+                                 near_k=None if kn is None else _t(kn, dev),
+                                 near_v=None if vn is None else _t(vn, dev),
+                                 qjl_proj_t=_t(np.ascontiguousarray(S.T), dev))
+    assert cache.attention_kernel(wl.q_heads, 2 if near else 0) == "attend_kernel"
+    cache.append(_t(kf, dev), _t(vf, dev), start_pos=0)
+    SN = 2 if near else 0
+    out = cache.decode(_t(inp.q, dev), T, wl.splits, SN).cpu().numpy()
+
+    kp = cache.k_codes[:, :, :T].cpu().numpy()
+    kn16 = cache.k_norms[:, :, :T].cpu().numpy()
+    check_codes("QJL K", kp, kn16, kf, kb, d)
+    vp = cache.v_codes[:, :, :T].cpu().numpy()
+    vn16 = cache.v_norms[:, :, :T].cpu().numpy()
+    check_codes("QJL V", vp, vn16, vf, vb, d)
+    z, rn = _check_sketch("QJL", cache, kf, kb, d, S, T)
+
+    s = _signs(d)
+    k_rot = _dequant_gpu_cache(kp, kn16, kb, d)
+    v_rot = _dequant_gpu_cache(vp, vn16, vb, d)
+    q64 = inp.q.astype(np.float64)
+    if near:
+        eff = O.qjl_effective_keys(k_rot, rn, z, S)
+        ref = O.two_tier_attention(q64, kn.astype(np.float64), vn.astype(np.float64), eff, v_rot, s)
+    else:
+        ref = O.qjl_attention(q64, k_rot, v_rot, rn, z, S, s)
+    _rows_close("QJL attention", out, ref)
+    # the sketch term is visible: attention without it is further off
+    plain = O.attention(q64, k_rot, v_rot, s) if not near else None
+    if plain is not None:
+        assert np.abs(plain - ref).max() > 10 * ATOL
+
+
 def test_head_dim_64(dev):
     wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, head_dim=64, seq_len=200, splits=3)
     run_case(dev, wl)

@@ -39,6 +39,9 @@ Recipe (all draws from numpy PCG64, ``default_rng(1000 + index)``):
      is the floor(0.1*T) tokens with the highest score (ties to the lower
      index), in ascending token order; the far tier is the rest, in order.
      decode_buffer draws no score: its near tier is the last 256 positions.
+  7. QJL projection (keys with a residual sketch): its own generator,
+     ``default_rng(QJL_SEED + d)``, an [m, d] float32 N(0,1) matrix, m = d;
+     the library takes it transposed ([d, m]).
 """
 from __future__ import annotations
 
@@ -48,6 +51,7 @@ from typing import Optional
 import numpy as np
 
 SIGN_SEED = 42
+QJL_SEED = 4242
 
 
 @dataclasses.dataclass(frozen=True)
@@ -185,3 +189,8 @@ def new_token(wl: Workload, step: int = 0):
     v = rng.standard_normal(shape, dtype=np.float32)
     dt = _np_dtype(wl.dtype)
     return k.astype(dt), v.astype(dt)
+
+
+def qjl_projection(d: int) -> np.ndarray:
+    """The Gaussian projection S [m, d] (m = d) of the QJL residual sketch."""
+    return np.random.default_rng(QJL_SEED + d).standard_normal((d, d), dtype=np.float32)
