@@ -21,6 +21,7 @@ workload, on this host's cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -38,9 +39,10 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "packed-KV decode-attention HBM GB/s (% of peak) + quantize-append tokens/s"
 
 
-def cache_bytes(wl: W.Workload, outliers: int = 0) -> dict:
+def cache_bytes(wl: W.Workload, outliers: int = 0, qjl: bool = False) -> dict:
     """Algorithmic bytes of the decode read and of one appended token (a key
-    outlier stream adds its int8 codes and fp32 scale per token)."""
+    outlier stream adds its int8 codes and fp32 scale per token, a QJL sketch
+    its d/8 sign bytes and fp16 residual norm)."""
     d = wl.head_dim
     kb = wl.k_bits
     krow = d * kb // 8
@@ -48,7 +50,7 @@ def cache_bytes(wl: W.Workload, outliers: int = 0) -> dict:
     pairs = wl.batch * wl.kv_heads
     far = wl.far_len
     knorm = 0 if kb == 8 else 2
-    per_tok = krow + knorm + vrow + 2 + (outliers + 4 if outliers else 0)
+    per_tok = krow + knorm + vrow + 2 + (outliers + 4 if outliers else 0) + (d // 8 + 2 if qjl else 0)
     near = wl.near_len * 2 * d * 2
     qb = wl.batch * wl.q_heads * d * (4 if wl.dtype == "f32" else 2)
     ob = wl.batch * wl.q_heads * d * 4
@@ -72,6 +74,10 @@ def parse(argv=None):
                          "= the query's own log-sum-exp from an ungated pass, spike threshold 4 below it")
     ap.add_argument("--outliers", type=int, default=0, choices=(0, 8),
                     help="key outlier stream with this many channels, calibrated on the first 256 tokens")
+    ap.add_argument("--qjl", action="store_true",
+                    help="QJL residual sketch on the keys (m = head_dim rows of a seeded Gaussian projection)")
+    ap.add_argument("--k-bits", type=int, default=None, choices=(2, 3, 4),
+                    help="override the key code bits only (e.g. 3 with --qjl: 3-bit codes plus the 1-bit sketch)")
     ap.add_argument("--query-scale", type=float, default=1.0,
                     help="multiply the decode query (a larger scale gives a more peaked softmax)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
@@ -239,10 +245,15 @@ def main(argv=None) -> int:
     wl = W.WORKLOADS[args.workload]
     if args.bits:
         wl = wl.with_bits(args.bits)
+    if args.k_bits:
+        wl = dataclasses.replace(wl, k_bits=args.k_bits, name=f"{wl.name.split('@')[0]}@k{args.k_bits}")
     if args.splits:
         wl = wl.scaled(splits=args.splits)
+    if args.qjl and wl.k_bits == 8:
+        print("--qjl needs Lloyd-Max keys", file=sys.stderr)
+        return 2
     dev = torch.device("cuda")
-    by = cache_bytes(wl, args.outliers)
+    by = cache_bytes(wl, args.outliers, args.qjl)
     print(f"# workload {wl.name}: cache {by['cache'] / 1e6:.1f} MB", file=sys.stderr, flush=True)
 
     inp = W.generate(wl)
@@ -262,12 +273,16 @@ def main(argv=None) -> int:
     kn_dev = None if kn is None else torch.from_numpy(np.ascontiguousarray(kn)).to(dev)
     vn_dev = None if vn is None else torch.from_numpy(np.ascontiguousarray(vn)).to(dev)
     R = max(1, math.ceil((1 << 30) / by["cache"]))
+    proj_t = None
+    if args.qjl:
+        proj_t = torch.from_numpy(np.ascontiguousarray(W.qjl_projection(wl.head_dim).T)).to(dev)
     caches = []
     for r in range(R):
         c = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, T, fmt[wl.k_bits], fmt[wl.v_bits],
                                  seed=W.SIGN_SEED, device=dev,
                                  near_k=None if kn_dev is None else kn_dev.clone(),
-                                 near_v=None if vn_dev is None else vn_dev.clone(), outliers=args.outliers)
+                                 near_v=None if vn_dev is None else vn_dev.clone(), outliers=args.outliers,
+                                 qjl_proj_t=proj_t)
         if args.outliers:
             c.calibrate(k_dev[:, :, :min(256, T)].contiguous())
         caches.append(c)
@@ -378,7 +393,7 @@ def main(argv=None) -> int:
                    "head_dim": wl.head_dim, "seq_len": wl.seq_len, "k_bits": wl.k_bits, "v_bits": wl.v_bits,
                    "splits": S, "near_splits": near_splits, "layer_replicas": R, "launch": "hip_graph",
                    "gated": bool(args.gate), "query_scale": args.query_scale, "outliers": args.outliers,
-                   "step_bytes": step_bytes},
+                   "qjl": bool(args.qjl), "step_bytes": step_bytes},
         "pct_of_hbm_peak": round(100 * step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
         "append_tokens_per_s": round(append_tok_s, 1),
         "append_GBps": round(append_bytes / (append_ms / 1e3) / 1e9, 2),

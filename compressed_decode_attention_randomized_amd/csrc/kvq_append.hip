@@ -312,7 +312,7 @@ __device__ void sketch(const Stream &st, const double *resid, int nvec, int n_ne
 #pragma unroll
   for (int k = 0; k < kPer; ++k) acc[k] = 0.0;
   const float *col = st.qjl_proj + i;
-#pragma unroll 4
+#pragma unroll 16
   for (int j = 0; j < D; ++j) {
     const double s = (double)col[(size_t)j * D];
     const double *rv = resid + j * VPB + g * kPer;

@@ -490,9 +490,11 @@ template <int D, int KB, int VB, int G, bool NEAR, bool GATED, int X = kNoExtra>
 __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
   constexpr bool OUT = X == kOutliers, QJL = X == kQjl;
   // G = 1: 32 coordinates per lane, except where near-tier fp16 rows would
-  // double the pipelined registers; loads pipelined
+  // double the pipelined registers; loads pipelined at every G (the next
+  // block's rows cost a few registers beside the G x DPL query and
+  // accumulator arrays, and halve the memory round trips a wave waits on)
   constexpr int DPL = (G == 1 && !NEAR) ? 32 : 16;
-  constexpr bool kPipe = (G == 1);
+  constexpr bool kPipe = true;
   constexpr int LPT = D / DPL;
   static_assert(LPT >= 1 && LPT <= 64, "lane mapping");
 
@@ -564,7 +566,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
       float acc[HP];
 #pragma unroll
       for (int k = 0; k < HP; ++k) acc[k] = 0.f;
-#pragma unroll 4
+#pragma unroll 16
       for (int j = 0; j < D; ++j) {
         const float sv = P.qjl_proj[(size_t)j * D + i];
 #pragma unroll
