@@ -545,6 +545,40 @@ def test_incremental_append_equals_bulk(dev):
         assert torch.equal(getattr(bulk, name), getattr(inc, name)), name
 
 
+@pytest.mark.parametrize("d,bits,hkv,G,kernel", [(128, 4, 5, 2, "attend_pair_kernel"), (64, 3, 3, 1, "attend_kernel")])
+def test_largest_attention_grid(dev, d, bits, hkv, G, kernel):
+    """batch * kv_heads = 65535, the largest the attention calls accept (one
+    grid dimension), with a ragged 20-token context: sampled rows' codes and
+    sampled (b, KV head) attention, the last of the grid included, against
+    the oracle; one more (b, KV head) is refused on the host."""
+    B = 65535 // hkv
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=B, q_heads=hkv * G, kv_heads=hkv, head_dim=d, seq_len=20,
+                                             splits=1).with_bits(bits)
+    inp = W.generate(wl)
+    cache = kvq.KVCache.allocate(B, hkv, d, 20, _fmt(bits), _fmt(bits), seed=W.SIGN_SEED, device=dev)
+    assert cache.attention_kernel(wl.q_heads) == kernel
+    cache.append(_t(inp.k, dev), _t(inp.v, dev), 0)
+    out = cache.decode(_t(inp.q, dev), 20, 1)
+    torch.cuda.synchronize()
+    s = _signs(d)
+    for b, hk in [(0, 0), (B // 2, hkv // 2), (B - 1, hkv - 1)]:
+        kp = cache.k_codes[b, hk, :20].cpu().numpy()
+        vp = cache.v_codes[b, hk, :20].cpu().numpy()
+        kn16 = cache.k_norms[b, hk, :20].cpu().numpy()
+        vn16 = cache.v_norms[b, hk, :20].cpu().numpy()
+        check_codes(f"grid K b{b}", kp, kn16, inp.k[b, hk], bits, d)
+        check_codes(f"grid V b{b}", vp, vn16, inp.v[b, hk], bits, d)
+        k_rot = _dequant_gpu_cache(kp[None, None], kn16[None, None], bits, d)
+        v_rot = _dequant_gpu_cache(vp[None, None], vn16[None, None], bits, d)
+        ref = O.attention(inp.q[b:b + 1, hk * G:(hk + 1) * G].astype(np.float64), k_rot, v_rot, s)
+        _rows_close(f"grid b{b} hkv{hk}", out[b:b + 1, hk * G:(hk + 1) * G].cpu().numpy(), ref)
+    big = kvq.KVCache.allocate(B + 1, hkv, d, 16, _fmt(bits), _fmt(bits), seed=W.SIGN_SEED, device=dev) \
+        if (B + 1) * hkv > 65535 else None
+    if big is not None:
+        with pytest.raises(kvq.KVQError):
+            big.decode(_t(inp.q[:1].repeat(B + 1, axis=0), dev), 16, 1)
+
+
 def test_empty_context_gives_zero(dev):
     wl = W.WORKLOADS["llama7b_layer"].scaled(batch=1, seq_len=16)
     cache = kvq.KVCache.allocate(1, 8, 128, 16, seed=W.SIGN_SEED, device=dev)
