@@ -371,6 +371,20 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     att_ms = [a.elapsed_time(b) for a, b in evs]
 
+    # ---- the one-token decode-step append alone: n_att back-to-back appends
+    # replayed from a HIP graph (a Python launch would outlast the kernel) ----
+    g_app = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_app):
+        for i in range(n_att):
+            caches[i % R].append(k_new, v_new, T - 1)
+    g_app.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g_app.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    append_step_us = e0.elapsed_time(e1) / n_att * 1e3
+
     att_bytes = by["cache"] + by["q"] + by["out"]
     step_bytes = att_bytes + by["append_token"]
     achieved = att_bytes / (att_avg / 1e3) / 1e9
@@ -397,6 +411,7 @@ def main(argv=None) -> int:
         "pct_of_hbm_peak": round(100 * step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
         "append_tokens_per_s": round(append_tok_s, 1),
         "append_GBps": round(append_bytes / (append_ms / 1e3) / 1e9, 2),
+        "append_step_us": round(append_step_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

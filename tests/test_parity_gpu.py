@@ -545,6 +545,28 @@ def test_incremental_append_equals_bulk(dev):
         assert torch.equal(getattr(bulk, name), getattr(inc, name)), name
 
 
+@pytest.mark.parametrize("d,bits", [(64, 2), (128, 3), (256, 4)])
+def test_qjl_incremental_append_equals_bulk(dev, d, bits):
+    """With a QJL sketch, appends of 1, 63, 86 and 50 tokens at their
+    positions write the same codes, norms, sketch bits and residual norms as
+    one bulk append (work-groups cut at other vector boundaries, partly
+    filled ones included)."""
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=2, q_heads=6, kv_heads=3, head_dim=d, seq_len=200)
+    inp = W.generate(wl)
+    T = wl.seq_len
+    pt = _t(np.ascontiguousarray(W.qjl_projection(d).T), dev)
+    mk = lambda: kvq.KVCache.allocate(wl.batch, wl.kv_heads, d, T, _fmt(bits), _fmt(bits), seed=W.SIGN_SEED,
+                                      device=dev, qjl_proj_t=pt)
+    bulk, inc = mk(), mk()
+    bulk.append(_t(inp.k, dev), _t(inp.v, dev), 0)
+    for a, b in ((0, 1), (1, 64), (64, 150), (150, 200)):
+        inc.append(_t(inp.k[:, :, a:b], dev), _t(inp.v[:, :, a:b], dev), a)
+    torch.cuda.synchronize()
+    for name in ("k_codes", "v_codes", "k_norms", "v_norms", "qjl_signs", "qjl_norms"):
+        assert torch.equal(getattr(bulk, name), getattr(inc, name)), name
+    _check_sketch("QJL bulk", bulk, inp.k, bits, d, W.qjl_projection(d), T)
+
+
 @pytest.mark.parametrize("d,bits,hkv,G,kernel", [(128, 4, 5, 2, "attend_pair_kernel"), (64, 3, 3, 1, "attend_kernel")])
 def test_largest_attention_grid(dev, d, bits, hkv, G, kernel):
     """batch * kv_heads = 65535, the largest the attention calls accept (one
