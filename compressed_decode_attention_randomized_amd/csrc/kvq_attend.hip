@@ -242,7 +242,8 @@ struct FarTier {
     }
     if constexpr (QJL) {
       const uint8_t *zr = zs0 + (size_t)t * (D / 8);
-      zw = (DPL == 32) ? reinterpret_cast<const uint32_t *>(zr)[ds] : reinterpret_cast<const uint16_t *>(zr)[ds];
+      zw = (DPL == 32) ? reinterpret_cast<const uint32_t *>(zr)[ds]
+                       : (DPL == 16) ? (uint32_t)reinterpret_cast<const uint16_t *>(zr)[ds] : (uint32_t)zr[ds];
       rho = half_to_float(zn0[t]) * (1.2533141373155003f / (float)D);   // sqrt(pi/2) / m, m = D
     }
   }
@@ -490,10 +491,15 @@ template <int D, int KB, int VB, int G, bool NEAR, bool GATED, int X = kNoExtra>
 __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
   constexpr bool OUT = X == kOutliers, QJL = X == kQjl;
   // G = 1: 32 coordinates per lane, except where near-tier fp16 rows would
-  // double the pipelined registers; loads pipelined at every G (the next
-  // block's rows cost a few registers beside the G x DPL query and
-  // accumulator arrays, and halve the memory round trips a wave waits on)
-  constexpr int DPL = (G == 1 && !NEAR) ? 32 : 16;
+  // double the pipelined registers; G >= 4 with a near tier (where the far
+  // codes allow whole-word slices): 8, so the near rows' fp16 slices and the
+  // G x DPL arrays leave room for three or four waves per SIMD (the
+  // decode-buffer launch: 27.5 -> 25.5 us; on far-only launches the extra
+  // reduction round and the softmax repeated over twice the lanes cost more
+  // than the occupancy gains).  Loads pipelined at every G (the next block's
+  // rows cost a few registers beside the G x DPL query and accumulator
+  // arrays, and halve the memory round trips a wave waits on).
+  constexpr int DPL = (G == 1 && !NEAR) ? 32 : ((NEAR && G >= 4 && KB != 3 && VB != 3) ? 8 : 16);
   constexpr bool kPipe = true;
   constexpr int LPT = D / DPL;
   static_assert(LPT >= 1 && LPT <= 64, "lane mapping");
