@@ -136,18 +136,26 @@ struct State {
     }
   }
   // Adds one token with scores s[h] (already -inf if the token is absent);
-  // returns the weights p[h] for the value accumulation.
+  // returns the weights p[h] for the value accumulation.  For G >= 2 the
+  // exponentials are the hardware's v_exp_f32 (weights are at most 1; one
+  // that would be below 2^-126 becomes 0, which no fp32 sum of weights
+  // would notice): 3-6% on those launches; the G = 1 launches measured
+  // slower with it (two_tier 171.9 -> 184.4 us) and keep exp2f.
+  __device__ static float exp2w(float x) {
+    if constexpr (G >= 2) return __builtin_amdgcn_exp2f(x);
+    else return exp2f(x);
+  }
   __device__ void add_scores(const float (&s)[G], float (&p)[G]) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if (s[h] > m[h]) {
-        const float alpha = exp2f(m[h] - s[h]);
+        const float alpha = exp2w(m[h] - s[h]);
         l[h] *= alpha;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha;
         m[h] = s[h];
       }
-      p[h] = (s[h] == -INFINITY) ? 0.f : exp2f(s[h] - m[h]);
+      p[h] = (s[h] == -INFINITY) ? 0.f : exp2w(s[h] - m[h]);
       l[h] += p[h];
     }
   }
@@ -170,6 +178,29 @@ struct State {
     }
   }
 };
+
+// Sum of x over the LPT consecutive lanes that share a token (LPT a power of
+// two), in every one of them.  Groups of up to 16 lanes reduce with DPP
+// moves folded into the adds: quad permutations [1,0,3,2] and [2,3,0,1],
+// then the row half-mirror (lane i with 7 - i) and the row mirror (i with
+// 15 - i), which after the earlier stages pair lanes holding the two halves'
+// sums; wider groups finish with shuffles.  Each stage adds the same two
+// values in either order, so all lanes of a group end with the same bits.
+template <int CTRL>
+__device__ inline float add_dpp(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+template <int LPT>
+__device__ inline float lane_sum(float x) {
+  if constexpr (LPT >= 2) x = add_dpp<0xB1>(x);
+  if constexpr (LPT >= 4) x = add_dpp<0x4E>(x);
+  if constexpr (LPT >= 8) x = add_dpp<0x141>(x);
+  if constexpr (LPT >= 16) x = add_dpp<0x140>(x);
+  if constexpr (LPT >= 32) x += __shfl_xor(x, 16);
+  if constexpr (LPT >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
 
 // Codes 2p and 2p+1 (one 2B-bit field) of an LSB-first bit stream.
 template <int B>
@@ -391,10 +422,7 @@ __device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G
     float part[G];
     cur.score(qr, part);
 #pragma unroll
-    for (int m = 1; m < LPT; m <<= 1) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) part[h] += __shfl_xor(part[h], m);
-    }
+    for (int h = 0; h < G; ++h) part[h] = lane_sum<LPT>(part[h]);
     float s[G], p[G];
     const float ks = cur.key_scale();
 #pragma unroll
@@ -432,10 +460,7 @@ __device__ void token_loop_gated(const Tier &proto, const float (&qr)[G][DPL], S
     float part[G];
     X.score(qr, part);
 #pragma unroll
-    for (int m = 1; m < LPT; m <<= 1) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) part[h] += __shfl_xor(part[h], m);
-    }
+    for (int h = 0; h < G; ++h) part[h] = lane_sum<LPT>(part[h]);
     const bool valid = t < t1;
     float s[G];
     const float ks = X.key_scale();
@@ -564,25 +589,54 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
   const float prescale = near ? kLog2e / sqrtf((float)D) : kLog2e / (float)D;
   if constexpr (QJL) {
     if (!near) {
-      // p = S (q~ pre-scaled) per head: thread (i, h0) forms row i for heads
-      // h0, h0 + kBlock/D, ...; the projection column is read coalesced and
-      // the query element is an LDS broadcast
-      constexpr int HS = kBlock / D, HP = (G + HS - 1) / HS;
-      const int i = tid % D, h0 = tid / D;
-      float acc[HP];
+      // p = S (q~ pre-scaled) per head.  Thread t takes the four columns
+      // 4c..4c+3 of S^T (c = t % (D/4), one 16-byte load per row) over its
+      // range of rows (t / (D/4)), sixteen loads in flight; the ranges of a
+      // wave are summed by shuffles, the four waves' sums through red_acc
+      // (unused until the epilogue), in a fixed order.
+      constexpr int CG = D / 4, R = kBlock / CG, JR = D / R, JC = JR < 16 ? JR : 16;
+      const int c = tid % CG, r = tid / CG;
+      float acc[G][4];
 #pragma unroll
-      for (int k = 0; k < HP; ++k) acc[k] = 0.f;
-#pragma unroll 16
-      for (int j = 0; j < D; ++j) {
-        const float sv = P.qjl_proj[(size_t)j * D + i];
+      for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.f;
+      const float4 *col = reinterpret_cast<const float4 *>(P.qjl_proj) + c;
+      for (int j0 = r * JR; j0 < (r + 1) * JR; j0 += JC) {
+        float4 sv[JC];
 #pragma unroll
-        for (int k = 0; k < HP; ++k) {
-          if (h0 + k * HS < G) acc[k] = fmaf(sv, qs[h0 + k * HS][j], acc[k]);
+        for (int u = 0; u < JC; ++u) sv[u] = col[(size_t)(j0 + u) * CG];
+#pragma unroll
+        for (int u = 0; u < JC; ++u) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float qv = qs[h][j0 + u];
+            acc[h][0] = fmaf(sv[u].x, qv, acc[h][0]);
+            acc[h][1] = fmaf(sv[u].y, qv, acc[h][1]);
+            acc[h][2] = fmaf(sv[u].z, qv, acc[h][2]);
+            acc[h][3] = fmaf(sv[u].w, qv, acc[h][3]);
+          }
         }
       }
+      const int lane0 = tid & 63, wave0 = tid >> 6;
 #pragma unroll
-      for (int k = 0; k < HP; ++k) {
-        if (h0 + k * HS < G) ps[h0 + k * HS][i] = acc[k] * prescale;
+      for (int m = CG; m < 64; m <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[h][e] += __shfl_xor(acc[h][e], m);
+        }
+      }
+      if (lane0 < CG) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          *reinterpret_cast<float4 *>(&red_acc[wave0][h][4 * c]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      }
+      __syncthreads();
+      for (int o = tid; o < G * D; o += kBlock) {
+        const int h = o / D, i = o - (o / D) * D;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v += red_acc[w][h][i];
+        ps[h][i] = v * prescale;
       }
       __syncthreads();
     }
