@@ -20,9 +20,14 @@ def dev():
     return torch.device("cuda")
 
 
-@pytest.mark.parametrize("name", ["llama7b_layer", "two_tier", "decode_buffer"])
-def test_decode_step_graph_replays_match_eager(dev, name):
+@pytest.mark.parametrize("name,side", [("llama7b_layer", None), ("two_tier", None), ("decode_buffer", None),
+                                       ("llama7b_layer", "qjl"), ("llama7b_layer", "outliers")])
+def test_decode_step_graph_replays_match_eager(dev, name, side):
+    """side: a key side stream (the QJL sketch over 3-bit keys, or the
+    outlier stream calibrated on the first 128 tokens)."""
     wl = W.WORKLOADS[name].scaled(batch=1, seq_len=700, splits=8)
+    if side == "qjl":
+        wl = wl.scaled(k_bits=3)
     inp = W.generate(wl)
     if wl.near_fraction:
         kn, vn = inp.tier("near")
@@ -34,8 +39,12 @@ def test_decode_step_graph_replays_match_eager(dev, name):
         kf, vf, near_splits, near_k, near_v = inp.k, inp.v, 0, None, None
     T = kf.shape[2]
     fmt = {2: kvq.KVQ_LM2, 3: kvq.KVQ_LM3, 4: kvq.KVQ_LM4, 8: kvq.KVQ_FP8_E4M3}
+    proj = torch.from_numpy(np.ascontiguousarray(W.qjl_projection(wl.head_dim).T)).to(dev) if side == "qjl" else None
     cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, T, fmt[wl.k_bits], fmt[wl.v_bits],
-                                 seed=W.SIGN_SEED, device=dev, near_k=near_k, near_v=near_v)
+                                 seed=W.SIGN_SEED, device=dev, near_k=near_k, near_v=near_v,
+                                 outliers=8 if side == "outliers" else 0, qjl_proj_t=proj)
+    if side == "outliers":
+        cache.calibrate(torch.from_numpy(np.ascontiguousarray(kf[:, :, :128])).to(dev))
     cache.append(torch.from_numpy(np.ascontiguousarray(kf)).to(dev),
                  torch.from_numpy(np.ascontiguousarray(vf)).to(dev), 0)
     knew, vnew = (torch.from_numpy(a).to(dev) for a in W.new_token(wl))
