@@ -229,7 +229,7 @@ def cpu_baseline(wl: W.Workload, inp: W.Inputs, seconds: float = 12.0) -> dict:
 def main(argv=None) -> int:
     args = parse(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: libkvq has no multi-GPU path "
               f"(requested --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
         return 2
     import torch
