@@ -228,7 +228,11 @@ __device__ inline float2_t pair_entry(const uint8_t *tab, uint32_t f, uint32_t s
 // fp8 keys decode in hardware (v_cvt_pk_f32_fp8: OCP E4M3FN, exact in fp32),
 // 2- and 3-bit codes through pair tables, 4-bit codes one table read each.
 // X = kOutliers: the keys carry an outlier stream; every score gains
-// q[idx] . (code * scale) / sqrt(d) (qo holds q[idx] pre-scaled).
+// q[idx] . (code * scale) / sqrt(d).  The channels are shared out over the
+// token's lanes (channel k on lane k % LPT; qo holds q[idx[k]] pre-scaled
+// for the lane's channels, osel their bit offsets in the 8 code bytes), and
+// each lane folds scale * sum q . code into its partial before the
+// reduction, so the key scale is applied in the lane (key_scale() = 1).
 // X = kQjl: the keys carry a QJL sketch; the lane's partial score becomes
 // nk * (its codec part) + rho * sum_e (2 z_e - 1) p_e over its DPL sketch
 // bits, rho = ||r||_16 sqrt(pi/2)/D and p = S q~ pre-scaled (pq holds 2 p,
@@ -236,6 +240,7 @@ __device__ inline float2_t pair_entry(const uint8_t *tab, uint32_t f, uint32_t s
 template <int D, int KB, int VB, int G, int DPL, int X = kNoExtra>
 struct FarTier {
   static constexpr bool OUT = X == kOutliers, QJL = X == kQjl;
+  static constexpr int kLPT = D / DPL, kOPL = (kOutlierCount + kLPT - 1) / kLPT;   // outlier channels per lane
   static constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
   static constexpr int KNB = DPL * KB / 8, VNB = DPL * VB / 8;
   static constexpr bool kKeyPairs = KB == 2 || KB == 3, kValPairs = VB == 2 || VB == 3;
@@ -250,7 +255,8 @@ struct FarTier {
   // outlier stream (OUT only)
   const int8_t *oc0;
   const float *os0;
-  float qo[G][kOutlierCount];
+  float qo[G][OUT ? kOPL : 1];
+  uint32_t osel[OUT ? kOPL : 1];
   uint2 oc;
   float osc;
   // QJL sketch (QJL only)
@@ -278,21 +284,9 @@ struct FarTier {
       rho = half_to_float(zn0[t]) * (1.2533141373155003f / (float)D);   // sqrt(pi/2) / m, m = D
     }
   }
-  // the outlier stream's part of head h's score (log2 units)
-  __device__ float extra(int h) const {
-    if constexpr (OUT) {
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < kOutlierCount; ++k) {
-        const uint32_t w = (k < 4) ? oc.x : oc.y;
-        const float c = (float)(int8_t)((w >> (8 * (k & 3))) & 0xFFu);
-        acc = fmaf(qo[h][k], c, acc);
-      }
-      return acc * osc;
-    } else {
-      return 0.f;
-    }
-  }
+  // a part of the score added after the cross-lane reduction (none: the
+  // side streams fold theirs into the lane partials)
+  __device__ float extra(int) const { return 0.f; }
   __device__ void load_values(int t, int ds) {
     load_slice<VNB>(vrow0 + (size_t)t * VROW + ds * VNB, vw);
     nv = half_to_float(vn0[t]);
@@ -336,8 +330,23 @@ struct FarTier {
 #pragma unroll
       for (int h = 0; h < G; ++h) part[h] = fmaf(rho, a[h], part[h] * nk);
     }
+    if constexpr (OUT) {
+      float c[kOPL];
+#pragma unroll
+      for (int u = 0; u < kOPL; ++u) {
+        const uint32_t w = (osel[u] < 32u) ? oc.x : oc.y;
+        c[u] = (float)(int8_t)((w >> (osel[u] & 31u)) & 0xFFu);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int u = 0; u < kOPL; ++u) a = fmaf(qo[h][u], c[u], a);
+        part[h] = fmaf(osc, a, part[h] * nk);
+      }
+    }
   }
-  __device__ float key_scale() const { return QJL ? 1.f : nk; }
+  __device__ float key_scale() const { return (QJL || OUT) ? 1.f : nk; }
   __device__ void accumulate(const float (&p)[G], State<G, DPL> &st) const {
     float w[G];
 #pragma unroll
@@ -685,17 +694,23 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     }
     if constexpr (OUT) {
       // the query at the outlier channels (original domain), scaled to log2 units of s
+      // the lane's channels k = ds + LPT u (< 8); others get q = 0
       const float sc = kLog2e / sqrtf((float)D);
       const int32_t *oi = P.out_idx + (size_t)bh * kOutlierCount;
+      constexpr int kOPL = decltype(tier)::kOPL;
+      const int ods = (tid & 63) % LPT;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const size_t qrow = ((size_t)b * P.q_heads + hkv * G + h) * D;
+      for (int u = 0; u < kOPL; ++u) {
+        const int k = ods + LPT * u;
+        const bool has = k < kOutlierCount;
+        const int c = has ? oi[k] : 0;
+        tier.osel[u] = has ? (uint32_t)(8 * k) : 0u;
 #pragma unroll
-        for (int k = 0; k < kOutlierCount; ++k) {
-          const int c = oi[k];
+        for (int h = 0; h < G; ++h) {
+          const size_t qrow = ((size_t)b * P.q_heads + hkv * G + h) * D;
           const float v = P.q_f16 ? half_to_float(static_cast<const uint16_t *>(P.q)[qrow + c])
                                   : static_cast<const float *>(P.q)[qrow + c];
-          tier.qo[h][k] = v * sc;
+          tier.qo[h][u] = has ? v * sc : 0.f;
         }
       }
       tier.oc0 = P.out_codes + (size_t)bh * P.capacity * kOutlierCount;
