@@ -284,9 +284,6 @@ struct FarTier {
       rho = half_to_float(zn0[t]) * (1.2533141373155003f / (float)D);   // sqrt(pi/2) / m, m = D
     }
   }
-  // a part of the score added after the cross-lane reduction (none: the
-  // side streams fold theirs into the lane partials)
-  __device__ float extra(int) const { return 0.f; }
   __device__ void load_values(int t, int ds) {
     load_slice<VNB>(vrow0 + (size_t)t * VROW + ds * VNB, vw);
     nv = half_to_float(vn0[t]);
@@ -396,7 +393,6 @@ struct NearTier {
     }
   }
   __device__ float key_scale() const { return 1.f; }
-  __device__ float extra(int) const { return 0.f; }
   __device__ void accumulate(const float (&p)[G], State<G, DPL> &st) const {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
@@ -435,7 +431,7 @@ __device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G
     float s[G], p[G];
     const float ks = cur.key_scale();
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = valid ? fmaf(part[h], ks, cur.extra(h)) : -INFINITY;
+    for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
     st.add_scores(s, p);
     cur.accumulate(p, st);
     if constexpr (PIPE) cur = nxt;
@@ -474,7 +470,7 @@ __device__ void token_loop_gated(const Tier &proto, const float (&qr)[G][DPL], S
     float s[G];
     const float ks = X.key_scale();
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = valid ? fmaf(part[h], ks, X.extra(h)) : -INFINITY;
+    for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
     if (vy) Y.accumulate(py, st);
     if (fg.bits) {
       const int tw = t - ts;                       // the wave's first token of the block
