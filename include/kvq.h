@@ -103,7 +103,9 @@ typedef enum { KVQ_LM2 = 2, KVQ_LM3 = 3, KVQ_LM4 = 4, KVQ_FP8_E4M3 = 8 } kvq_for
  *   With the sketch on, attention adds
  *   ||r||_16 sqrt(pi/2)/m sum_i (2 z_i - 1) (S_i . R q) / sqrt(d) to every
  *   far-tier score, an estimate of the query's product with the residual
- *   that is unbiased over Gaussian S.
+ *   that is unbiased over Gaussian S.  A key whose fp16 norm overflows
+ *   (||k|| >= 65520) has no defined residual; its sketch bits and residual
+ *   norm are unspecified.
  * Code, norm and sign buffers must be 16-byte aligned and capacity a multiple of 16. */
 typedef struct kvq_cache {
   int32_t batch;
