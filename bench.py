@@ -213,10 +213,20 @@ def cpu_baseline(wl: W.Workload, inp: W.Inputs, seconds: float = 12.0) -> dict:
             break
     pair_bytes = by["cache"] / (wl.batch * wl.kv_heads)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    cpu_model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu_model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": round(n_pairs * pair_bytes / t_att / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
+        "cpu_model": cpu_model,
+        "host_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"{n_pairs} of {wl.batch * wl.kv_heads} (batch, kv-head) pairs of {wl.name}: "
                   f"oracle dequantize+attention over {wl.seq_len} tokens x {G} query heads each "
