@@ -670,3 +670,58 @@ def test_full_size_sampled(dev, name):
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_full_size_bitwidth_sweep_sampled(dev, bits):
     _full_size(dev, "bitwidth_sweep", bits=bits, sample_heads=1)
+
+
+@pytest.mark.parametrize("side", ["qjl", "outliers"])
+def test_full_size_side_streams(dev, side):
+    """llama7b_layer at full size in the launch configuration the benchmark
+    times for the key side streams (8 splits; the QJL sketch over 3-bit keys,
+    or the outlier stream calibrated on the first 256 tokens): sampled token
+    rows bit for bit, and the attention of two sampled (b, KV head) pairs,
+    against the oracle."""
+    wl = W.WORKLOADS["llama7b_layer"].scaled(splits=8)
+    if side == "qjl":
+        wl = wl.scaled(k_bits=3)
+    inp = W.generate(wl)
+    d, T, G = wl.head_dim, wl.seq_len, wl.group
+    s = _signs(d)
+    S = W.qjl_projection(d)
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, d, T, _fmt(wl.k_bits), _fmt(wl.v_bits), seed=W.SIGN_SEED,
+                                 device=dev, outliers=8 if side == "outliers" else 0,
+                                 qjl_proj_t=_t(np.ascontiguousarray(S.T), dev) if side == "qjl" else None)
+    k = inp.k
+    if side == "outliers":
+        cache.calibrate(_t(inp.k[:, :, :256], dev))
+        idx = O.calibrate_outliers(inp.k[:, :, :256])
+        assert np.array_equal(cache.outlier_idx.cpu().numpy(), idx)
+        k, ko = O.split_outliers(inp.k, idx)
+    cache.append(_t(inp.k, dev), _t(inp.v, dev), 0)
+    out = cache.decode(_t(inp.q, dev), T, wl.splits).cpu().numpy()
+    rng = np.random.default_rng(1)
+    for _ in range(2):
+        b, hk = int(rng.integers(wl.batch)), int(rng.integers(wl.kv_heads))
+        kp = cache.k_codes[b, hk].cpu().numpy()
+        kn16 = cache.k_norms[b, hk].cpu().numpy()
+        vp = cache.v_codes[b, hk].cpu().numpy()
+        vn16 = cache.v_norms[b, hk].cpu().numpy()
+        check_codes(f"full {side} K b{b}", kp, kn16, k[b, hk], wl.k_bits, d)
+        check_codes(f"full {side} V b{b}", vp, vn16, inp.v[b, hk], wl.v_bits, d)
+        k_rot = _dequant_gpu_cache(kp, kn16, wl.k_bits, d)[None, None]
+        v_rot = _dequant_gpu_cache(vp, vn16, wl.v_bits, d)[None, None]
+        q = inp.q[b:b + 1, hk * G:(hk + 1) * G].astype(np.float64)
+        if side == "qjl":
+            z = O.unpack(cache.qjl_signs[b, hk].cpu().numpy(), 1, d)
+            rn = cache.qjl_norms[b, hk].cpu().numpy().view(np.uint16)
+            enc = O.qjl_encode(k[b, hk], s, wl.k_bits, S)
+            same = (O.unpack(kp, wl.k_bits, d) == enc["codes"]).all(axis=-1)
+            assert not ((z != enc["sketch_bits"]) & same[:, None] & ~enc["sketch_window"]).any()
+            assert not ((rn != enc["rnorm"]) & same & ~enc["rnorm_window"]).any()
+            ref = O.qjl_attention(q, k_rot, v_rot, rn[None, None], z[None, None], S, s)
+        else:
+            oc = cache.outlier_codes[b, hk].cpu().numpy()
+            osc = cache.outlier_scales[b, hk].cpu().numpy()
+            oc_ref, os_ref = O.quantize_outliers(ko[b, hk])
+            assert np.array_equal(oc, oc_ref) and np.array_equal(osc, os_ref)
+            ref = O.two_stream_attention(q, k_rot, v_rot, idx[b:b + 1, hk:hk + 1], oc[None, None],
+                                         osc[None, None], s)
+        _rows_close(f"full {side} b{b} hkv{hk}", out[b:b + 1, hk * G:(hk + 1) * G], ref)
