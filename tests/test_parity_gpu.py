@@ -725,3 +725,48 @@ def test_full_size_side_streams(dev, side):
             ref = O.two_stream_attention(q, k_rot, v_rot, idx[b:b + 1, hk:hk + 1], oc[None, None],
                                          osc[None, None], s)
         _rows_close(f"full {side} b{b} hkv{hk}", out[b:b + 1, hk * G:(hk + 1) * G], ref)
+
+
+def test_full_size_gate(dev):
+    """two_tier at full size with the score gate and spike flags as the
+    benchmark's --gate runs them (references from the query's own
+    log-sum-exp, flags 4 below it), on a peaked query (x 8): the attention
+    of sampled (b, head) pairs against the gated oracle, their flag words bit
+    for bit except within 1e-3 of the threshold, and a gate that drops most
+    far values."""
+    wl = W.WORKLOADS["two_tier"]
+    inp = W.generate(wl)
+    kn, vn = inp.tier("near")
+    kf, vf = inp.tier("far")
+    SN, T, d = wl.near_split_count, kf.shape[2], wl.head_dim
+    q = _t((inp.q.astype(np.float32) * 8.0).astype(inp.q.dtype), dev)
+    q64 = q.cpu().numpy().astype(np.float64)
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, d, T, _fmt(wl.k_bits), _fmt(wl.v_bits), seed=W.SIGN_SEED,
+                                 device=dev, near_k=_t(kn, dev), near_v=_t(vn, dev))
+    cache.append(_t(kf, dev), _t(vf, dev), 0)
+    lse = torch.empty((wl.batch, wl.q_heads), dtype=torch.float32, device=dev)
+    cache.decode(q, T, wl.splits, SN, lse=lse)
+    spike = lse - 4.0
+    words = torch.zeros((wl.batch, wl.q_heads, (T + 31) // 32), dtype=torch.int32, device=dev)
+    po, pml = cache.attend(q, T, wl.splits, SN, gate_ref=lse, spike_ref=spike, spike_bits=words)
+    out = cache.merge(po, pml, wl.splits, SN).cpu().numpy()
+    gate64 = lse.cpu().numpy().astype(np.float64)
+    spike64 = spike.cpu().numpy().astype(np.float64)
+    all_words = words.cpu().numpy().view(np.uint32)
+    s = _signs(d)
+    rng = np.random.default_rng(2)
+    for _ in range(2):
+        b, h = int(rng.integers(wl.batch)), int(rng.integers(wl.kv_heads))
+        k_rot = _dequant_gpu_cache(cache.k_codes[b, h, :T].cpu().numpy(), None, 8, d)[None, None]
+        v_rot = _dequant_gpu_cache(cache.v_codes[b, h, :T].cpu().numpy(), cache.v_norms[b, h, :T].cpu().numpy(),
+                                   wl.v_bits, d)[None, None]
+        qq = q64[b:b + 1, h:h + 1]
+        knb, vnb = kn[b:b + 1, h:h + 1].astype(np.float64), vn[b:b + 1, h:h + 1].astype(np.float64)
+        ref = O.gated_two_tier_attention(qq, knb, vnb, k_rot, v_rot, s, gate64[b:b + 1, h:h + 1])
+        _rows_close(f"full gate b{b} h{h}", out[b:b + 1, h:h + 1], ref)
+        sf = O.far_scores(qq, k_rot, s)
+        assert (sf < gate64[b, h] - O.GATE_LOG).mean() > 0.5
+        want = O.spike_flags(qq, k_rot, s, spike64[b:b + 1, h:h + 1])[0, 0]
+        got = ((all_words[b, h][:, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(-1)[:T].astype(bool)
+        near_thr = np.abs(sf[0, 0] - spike64[b, h]) <= 1e-3
+        assert not ((got != want) & ~near_thr).any() and got.any()
