@@ -132,7 +132,10 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use float16 or float32")
 
 
-def _need(t, name: str, shape):
+def _need(t, name: str, shape, dtype=None):
+    """t must be a contiguous device tensor of this shape (and dtype, if given):
+    the kernels index these buffers by the shape alone, so a wrong shape or
+    element size would make them read or write past the allocation."""
     import torch
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
@@ -140,6 +143,8 @@ def _need(t, name: str, shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
 @dataclass
@@ -211,8 +216,9 @@ class KVCache:
     def struct(self) -> CacheStruct:
         p = lambda t: 0 if t is None else t.data_ptr()
         if self.near_k is not None:
-            _need(self.near_k, "near_k", (self.batch, self.kv_heads, self.near_len, self.head_dim))
-            _need(self.near_v, "near_v", (self.batch, self.kv_heads, self.near_len, self.head_dim))
+            import torch
+            _need(self.near_k, "near_k", (self.batch, self.kv_heads, self.near_len, self.head_dim), torch.float16)
+            _need(self.near_v, "near_v", (self.batch, self.kv_heads, self.near_len, self.head_dim), torch.float16)
         return CacheStruct(self.batch, self.kv_heads, self.head_dim, self.capacity, self.k_format,
                            self.v_format, p(self.k_codes), p(self.k_norms), p(self.v_codes), p(self.v_norms),
                            p(self.signs), p(self.k_centroids), p(self.v_centroids), p(self.near_k),
@@ -264,16 +270,16 @@ class KVCache:
         _need(q, "q", (self.batch, q_heads, self.head_dim))
         if part_o is None:
             part_o, part_ml = self.partial_buffers(q_heads, num_splits, num_near_splits)
+        import torch
         S = num_splits + num_near_splits
-        _need(part_o, "part_o", (self.batch, q_heads, S, self.head_dim))
-        _need(part_ml, "part_ml", (self.batch, q_heads, S, 2))
+        _need(part_o, "part_o", (self.batch, q_heads, S, self.head_dim), torch.float32)
+        _need(part_ml, "part_ml", (self.batch, q_heads, S, 2), torch.float32)
         cs = self.struct()
         if gate_ref is None and spike_ref is None:
             _check(load().kvq_decode_attention(ctypes.byref(cs), q.data_ptr(), _dtype_code(q), q_heads, seq_len,
                                                num_splits, num_near_splits, part_o.data_ptr(), part_ml.data_ptr(),
                                                _stream_handle(q.device)), "kvq_decode_attention")
             return part_o, part_ml
-        import torch
         for name, ref in (("gate_ref", gate_ref), ("spike_ref", spike_ref)):
             if ref is not None:
                 _need(ref, name, (self.batch, q_heads))
@@ -294,11 +300,16 @@ class KVCache:
     def merge(self, part_o, part_ml, num_splits: int, num_near_splits: int = 0, out=None, lse=None):
         import torch
         B, Hq, S, d = part_o.shape
+        if B != self.batch or d != self.head_dim or S != num_splits + num_near_splits:
+            raise ValueError(f"part_o has shape {tuple(part_o.shape)}, expected "
+                             f"({self.batch}, Hq, {num_splits + num_near_splits}, {self.head_dim})")
+        _need(part_o, "part_o", (B, Hq, S, d), torch.float32)
+        _need(part_ml, "part_ml", (B, Hq, S, 2), torch.float32)
         if out is None:
             out = torch.empty((B, Hq, d), dtype=torch.float32, device=part_o.device)
-        _need(out, "out", (B, Hq, d))
+        _need(out, "out", (B, Hq, d), torch.float32)
         if lse is not None:
-            _need(lse, "lse", (B, Hq))
+            _need(lse, "lse", (B, Hq), torch.float32)
         cs = self.struct()
         _check(load().kvq_merge(ctypes.byref(cs), part_o.data_ptr(), part_ml.data_ptr(), Hq, num_splits,
                                 num_near_splits, out.data_ptr(), 0 if lse is None else lse.data_ptr(),

@@ -215,7 +215,11 @@ const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads,
                     cache->near_k, cache->near_v, nullptr, nullptr};
   if (cache->outlier_count) a.outlier_idx = cache->outlier_idx;
   if (cache->qjl_dim) a.qjl_proj = cache->qjl_proj;
-  return kvq::attend_kernel_name(a);
+  const char *name = kvq::attend_kernel_name(a);
+  if (!name)
+    kvq::fail(KVQ_EUNSUPPORTED, "kvq_decode_attention_kernel: group %d with formats (%d,%d) at head_dim %d not built",
+              q_heads / cache->kv_heads, cache->k_format, cache->v_format, cache->head_dim);
+  return name;
 }
 
 kvq_status kvq_merge(const kvq_cache *cache, const float *part_o, const float *part_ml, int32_t q_heads,

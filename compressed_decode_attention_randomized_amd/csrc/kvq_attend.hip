@@ -21,11 +21,12 @@
 //      the rotated domain straight from their codes;
 //   4. the slot states are merged by xor-shuffles inside the wave and through
 //      LDS across the four waves; the split writes (m, l) and sum p v / l.
-// Key side streams (far tier): an outlier stream adds q[idx] . (code * scale)
-// to each score after the reduction; a QJL sketch adds
-// ||r|| sqrt(pi/2)/m sum_i (2 z_i - 1) (S q~)_i, with S q~ formed once per
-// work-group into LDS and each lane scoring its slice of the sketch bits
-// before the reduction.
+// Key side streams (far tier), both folded into each lane's partial score
+// before the cross-lane reduction: an outlier stream adds
+// q[idx] . (code * scale), its 8 channels shared out over the lanes of a
+// token; a QJL sketch adds ||r|| sqrt(pi/2)/m sum_i (2 z_i - 1) (S q~)_i,
+// with S q~ formed once per work-group into LDS and each lane scoring its
+// slice of the sketch bits.
 // Near-tier splits run the same loop on fp16 rows in the original domain.
 // Sources: "The Engineering Behind AdapTQ", "Engineering the Hot Path" (rotate
 // q once, score from codes through a table, no dequantize pass); "FoveatedKV",
@@ -805,6 +806,20 @@ hipError_t go(const AttendArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Query groups the VALU kernel is instantiated for: 1, 2 and 4 (3-bit
+// values: 1 only).
+bool valu_group_built(int G, int v_format) { return G == 1 || (v_format != 3 && (G == 2 || G == 4)); }
+
+bool valu_formats_built(int kf, int vf) {
+  return (kf == 2 && vf == 2) || (kf == 3 && vf == 3) || (kf == 4 && vf == 4) || (kf == 3 && vf == 4) ||
+         (kf == 8 && vf == 4);
+}
+
+bool valu_attend_supported(const AttendArgs &a) {
+  return (a.head_dim == 64 || a.head_dim == 128 || a.head_dim == 256) && a.q_heads % a.kv_heads == 0 &&
+         valu_group_built(a.q_heads / a.kv_heads, a.v_format) && valu_formats_built(a.k_format, a.v_format);
+}
+
 template <int D, int KB, int VB>
 hipError_t by_group(const AttendArgs &a, hipStream_t stream, bool *ok) {
   const int G = a.q_heads / a.kv_heads;
@@ -853,16 +868,18 @@ AttendArgs far_part(const AttendArgs &a) {
 }  // namespace
 
 const char *attend_kernel_name(const AttendArgs &a) {
-  if (a.outlier_idx || a.qjl_proj) return "attend_kernel";
+  // NULL where launch_attend would return KVQ_EUNSUPPORTED
+  const char *valu = valu_attend_supported(a) ? "attend_kernel" : nullptr;
+  if (a.outlier_idx || a.qjl_proj) return valu;
   if (a.num_near_splits > 0) {
     const AttendArgs f = far_part(a);
-    if (pair_attend_supported(f)) return "attend_pair_kernel+attend_kernel";
-    if (wide_attend_supported(f)) return "attend_wide_kernel+attend_kernel";
+    if (pair_attend_supported(f)) return valu ? "attend_pair_kernel+attend_kernel" : nullptr;
+    if (wide_attend_supported(f)) return valu ? "attend_wide_kernel+attend_kernel" : nullptr;
   }
   if (pair_attend_supported(a)) return "attend_pair_kernel";
   if (wide_attend_supported(a)) return "attend_wide_kernel";
   if (mfma_attend_supported(a)) return "attend_mfma_kernel";
-  return "attend_kernel";
+  return valu;
 }
 
 hipError_t launch_attend_gated(const AttendArgs &a, hipStream_t stream, bool *supported) {

@@ -239,7 +239,8 @@ kvq_status kvq_calibrate_outliers(const kvq_cache *cache, const void *keys, int3
 
 /* Name of the attention kernel kvq_decode_attention launches for this cache,
  * query-head count and near-split count (for profiles and reports): a static
- * string, or NULL if the cache description is invalid.  A cache with a near
+ * string, or NULL if the cache description is invalid or the call would
+ * return KVQ_EUNSUPPORTED (kvq_last_error then says why).  A cache with a near
  * tier whose far codes a pair-table kernel covers is served by two launches
  * on the stream (near splits, then far splits); the name is then
  * "<far kernel>+attend_kernel". */

@@ -119,3 +119,25 @@ def test_qjl_sign_of_zero_is_caught(monkeypatch):
         return np.where(dots == 0.0, 0, z).astype(np.uint8), w
     monkeypatch.setattr(O, "qjl_sketch_bits", bad)
     _fails(TQ.test_identity_projection_by_hand)
+
+
+def test_window_hundred_times_too_wide_is_caught(monkeypatch):
+    from tests import test_oracle_window as TW
+    monkeypatch.setattr(O, "WINDOW", 100 * O.WINDOW)
+    _fails(TW.test_lm_window_width_and_scale, 128, 4)
+    _fails(TW.test_fp8_window_width_and_scale, 128)
+
+
+def test_window_ten_times_too_narrow_is_caught(monkeypatch):
+    from tests import test_oracle_window as TW
+    monkeypatch.setattr(O, "WINDOW", O.WINDOW / 10)
+    _fails(TW.test_lm_window_width_and_scale, 64, 2)
+    _fails(TW.test_fp8_window_width_and_scale, 256)
+
+
+def test_window_on_the_unit_scale_is_caught(monkeypatch):
+    """A window measured on u = z / (sqrt(d) ||x||) (the N(0, 1/d) scale)
+    instead of the coordinate's sigma is sqrt(d) times too wide."""
+    from tests import test_oracle_window as TW
+    monkeypatch.setattr(O, "WINDOW", O.WINDOW * (128 ** 0.5))
+    _fails(TW.test_lm_window_width_and_scale, 128, 3)
