@@ -24,6 +24,7 @@ pytestmark = pytest.mark.gpu
 ATOL = 2e-3
 RTOL = 1e-3
 WINDOW_FRACTION = 1e-4
+WINDOW_REPORT = []          # one line per code check, printed in the session summary
 
 
 @pytest.fixture(scope="module")
@@ -63,6 +64,11 @@ def check_codes(name, gpu_packed, gpu_norms, x, bits, d):
     outside = bad & ~window
     assert not outside.any(), f"{name}: {int(outside.sum())} code mismatches outside the boundary window"
     frac = bad.sum() / bad.size
+    line = (f"{name}: {bad.size // d} rows x {d}: {int(bad.sum())} code mismatches, all inside the window "
+            f"({frac:.2e} of coordinates); {int(window.sum())} coordinates in the window")
+    print(line, flush=True)
+    if bad.size // d >= 4096:          # the full-size checks
+        WINDOW_REPORT.append(line)
     assert frac < WINDOW_FRACTION, f"{name}: windowed mismatches {frac:.2e}"
     return codes, norms_ok
 
@@ -245,6 +251,19 @@ def test_head_dim_256_unit_groups(dev, hq, bits):
     cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, wl.seq_len, _fmt(bits), _fmt(bits),
                                  seed=W.SIGN_SEED, device=dev)
     assert cache.attention_kernel(wl.q_heads) == "attend_wide_kernel"
+    run_case(dev, wl)
+
+
+@pytest.mark.parametrize("hq,kv,T,splits", [(2, 2, 1000, 4), (8, 2, 1000, 7), (16, 2, 300, 16), (64, 8, 77, 3)])
+def test_head_dim_128_two_bit(dev, hq, kv, T, splits):
+    """Head dimension 128 with 2-bit keys and values (the matrix-core kernel
+    with a 16-entry table), G = 1, 4, 8: ragged tails, and empty trailing
+    splits (300 tokens in chunks of 32 over 16 splits; 77 tokens over 3),
+    partial states checked split by split."""
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=2, q_heads=hq, kv_heads=kv, seq_len=T, splits=splits).with_bits(2)
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, 16, _fmt(2), _fmt(2), seed=W.SIGN_SEED,
+                                 device=dev)
+    assert cache.attention_kernel(wl.q_heads) == "attend_mfma_kernel"
     run_case(dev, wl)
 
 
@@ -615,7 +634,11 @@ def test_empty_context_gives_zero(dev):
 # full sizes, launch configuration of the benchmark, sampled checks
 # ---------------------------------------------------------------------------
 
-def _full_size(dev, name, bits=None, sample_heads=2):
+def _full_size(dev, name, bits=None, every_row=False, all_heads=False, sample_heads=2):
+    """The workload at full size in the benchmark's launch configuration.
+    Codes and norms: every row (every_row) or one whole (b, KV head) slab
+    plus 4096 random rows.  Attention: every (b, query head) row (all_heads)
+    or the G query heads of sampled (b, KV head) pairs."""
     wl = W.WORKLOADS[name]
     if bits:
         wl = wl.with_bits(bits)
@@ -637,16 +660,35 @@ def _full_size(dev, name, bits=None, sample_heads=2):
     rng = np.random.default_rng(0)
     s = _signs(d)
     G = wl.group
-    # sampled token rows: codes and norms against the oracle
-    bs = rng.integers(0, wl.batch, 64)
-    hs = rng.integers(0, wl.kv_heads, 64)
-    ts = rng.integers(0, T, 64)
-    ix = tuple(torch.from_numpy(a).to(dev) for a in (bs, hs, ts))
-    kp = cache.k_codes[ix].cpu().numpy()
-    vp = cache.v_codes[ix].cpu().numpy()
-    check_codes(f"{name} K sample", kp, cache.k_norms[ix].cpu().numpy(), kf[bs, hs, ts], wl.k_bits, d)
-    check_codes(f"{name} V sample", vp, cache.v_norms[ix].cpu().numpy(), vf[bs, hs, ts], wl.v_bits, d)
-    # sampled (b, kv head): attention of its G query heads against the oracle
+    print(f"{wl.name}: cache written and decoded; kernel {cache.attention_kernel(wl.q_heads, SN)}", flush=True)
+    if every_row:
+        for tag, gp, gn, x, nb in (("K", cache.k_codes, cache.k_norms, kf, wl.k_bits),
+                                   ("V", cache.v_codes, cache.v_norms, vf, wl.v_bits)):
+            check_codes(f"{wl.name} {tag} every row", gp[:, :, :T].cpu().numpy(), gn[:, :, :T].cpu().numpy(), x,
+                        nb, d)
+    else:
+        b0, h0 = int(rng.integers(wl.batch)), int(rng.integers(wl.kv_heads))
+        bs = rng.integers(0, wl.batch, 4096)
+        hs = rng.integers(0, wl.kv_heads, 4096)
+        ts = rng.integers(0, T, 4096)
+        ix = tuple(torch.from_numpy(a).to(dev) for a in (bs, hs, ts))
+        for tag, gp, gn, x, nb in (("K", cache.k_codes, cache.k_norms, kf, wl.k_bits),
+                                   ("V", cache.v_codes, cache.v_norms, vf, wl.v_bits)):
+            check_codes(f"{wl.name} {tag} slab b{b0} h{h0}", gp[b0, h0, :T].cpu().numpy(),
+                        gn[b0, h0, :T].cpu().numpy(), x[b0, h0], nb, d)
+            check_codes(f"{wl.name} {tag} 4096 random rows", gp[ix].cpu().numpy(), gn[ix].cpu().numpy(),
+                        x[bs, hs, ts], nb, d)
+    if all_heads:
+        k_rot = _dequant_gpu_cache(cache.k_codes[:, :, :T].cpu().numpy(), cache.k_norms[:, :, :T].cpu().numpy(),
+                                   wl.k_bits, d)
+        v_rot = _dequant_gpu_cache(cache.v_codes[:, :, :T].cpu().numpy(), cache.v_norms[:, :, :T].cpu().numpy(),
+                                   wl.v_bits, d)
+        q = inp.q.astype(np.float64)
+        ref = O.attention(q, k_rot, v_rot, s) if kn is None else \
+            O.two_tier_attention(q, kn.astype(np.float64), vn.astype(np.float64), k_rot, v_rot, s)
+        _rows_close(f"{wl.name} every (b, head)", out, ref)
+        print(f"{wl.name}: attention of all {wl.batch * wl.q_heads} (b, query head) rows within tolerance", flush=True)
+        return
     for _ in range(sample_heads):
         b, hk = int(rng.integers(wl.batch)), int(rng.integers(wl.kv_heads))
         kp = cache.k_codes[b, hk].cpu().numpy()[None, None]
@@ -662,7 +704,15 @@ def _full_size(dev, name, bits=None, sample_heads=2):
         _rows_close(f"{name} full b{b} hkv{hk}", out[b:b + 1, hk * G:(hk + 1) * G], ref)
 
 
-@pytest.mark.parametrize("name", ["single_head_fp32", "llama7b_layer", "long_context", "two_tier", "decode_buffer"])
+@pytest.mark.parametrize("name", ["single_head_fp32", "llama7b_layer", "long_context"])
+def test_full_size_every_row(dev, name):
+    """Configurations 1-3 at full size: every row's codes and norms against
+    the oracle (in-window mismatches counted and printed), and every
+    (b, query head) output row."""
+    _full_size(dev, name, every_row=True, all_heads=True)
+
+
+@pytest.mark.parametrize("name", ["two_tier", "decode_buffer"])
 def test_full_size_sampled(dev, name):
     _full_size(dev, name)
 

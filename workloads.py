@@ -194,3 +194,59 @@ def new_token(wl: Workload, step: int = 0):
 def qjl_projection(d: int) -> np.ndarray:
     """The Gaussian projection S [m, d] (m = d) of the QJL residual sketch."""
     return np.random.default_rng(QJL_SEED + d).standard_normal((d, d), dtype=np.float32)
+
+
+@dataclasses.dataclass
+class DeviceInputs:
+    """Device-resident draws of one workload (torch tensors): the same
+    shapes, dtypes, distributions and structure as `generate`, drawn from a
+    seeded torch generator on the device instead of numpy on the host, for
+    runs where host generation of the larger configurations would dominate
+    (the benchmark).  Not bit-identical to `generate`."""
+    wl: Workload
+    k: object                      # [B, Hkv, T, d] storage dtype
+    v: object
+    q: object                      # [B, Hq, d]
+    near_idx: object = None        # [B, Hkv, near_len] int64
+    far_idx: object = None         # [B, Hkv, far_len] int64
+
+    def tier(self, which: str):
+        import torch
+        idx = self.near_idx if which == "near" else self.far_idx
+        g = idx[..., None].expand(-1, -1, -1, self.wl.head_dim)
+        return torch.gather(self.k, 2, g).contiguous(), torch.gather(self.v, 2, g).contiguous()
+
+
+def generate_device(wl: Workload, device, seed_offset: int = 0) -> DeviceInputs:
+    """The module recipe, steps 1-6, with torch's generator on `device`
+    (seed 1000 + index + seed_offset)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(1000 + wl.index + seed_offset)
+    B, Hkv, T, d = wl.batch, wl.kv_heads, wl.seq_len, wl.head_dim
+    dt = {"f32": torch.float32, "f16": torch.float16}[wl.dtype]
+
+    k = torch.randn((B, Hkv, T, d), generator=g, device=device, dtype=torch.float32)
+    v = torch.randn((B, Hkv, T, d), generator=g, device=device, dtype=torch.float32)
+    if wl.outlier_channels:
+        for h in range(Hkv):
+            ch = torch.randperm(d, generator=g, device=device)[: wl.outlier_channels]
+            k[:, h, :, ch] *= wl.outlier_scale
+    if wl.lognormal_sigma:
+        sk = torch.exp(wl.lognormal_sigma * torch.randn((Hkv, d), generator=g, device=device))
+        sv = torch.exp(wl.lognormal_sigma * torch.randn((Hkv, d), generator=g, device=device))
+        k *= sk[None, :, None, :]
+        v *= sv[None, :, None, :]
+    k, v = k.to(dt), v.to(dt)
+    q = torch.randn((B, wl.q_heads, d), generator=g, device=device, dtype=torch.float32).to(dt)
+    out = DeviceInputs(wl, k, v, q)
+    if wl.near_fraction and wl.near_recent:
+        pos = torch.arange(T, device=device, dtype=torch.int64)
+        out.near_idx = pos[wl.far_len:].expand(B, Hkv, -1).contiguous()
+        out.far_idx = pos[:wl.far_len].expand(B, Hkv, -1).contiguous()
+    elif wl.near_fraction:
+        score = torch.rand((B, Hkv, T), generator=g, device=device, dtype=torch.float64)
+        order = torch.argsort(-score, dim=-1, stable=True)
+        out.near_idx = torch.sort(order[..., : wl.near_len], dim=-1).values
+        out.far_idx = torch.sort(order[..., wl.near_len:], dim=-1).values
+    return out
