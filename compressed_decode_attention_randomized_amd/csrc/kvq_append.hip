@@ -408,6 +408,7 @@ hipError_t launch1(const AppendArgs &a, hipStream_t stream, bool *ok) {
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream, bool *supported) {
   *supported = true;
+  if (bulk_append_supported(a)) return launch_append_bulk(a, stream);
   if (fast_append_supported(a)) return launch_append_fast(a, stream);
   switch (a.head_dim) {
     case 64: return launch1<64>(a, stream, supported);

@@ -40,6 +40,10 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t stream, bool *supporte
 // Bulk-throughput variant (Lloyd-Max keys and values, head_dim 64/128/256).
 bool fast_append_supported(const AppendArgs &a);
 hipError_t launch_append_fast(const AppendArgs &a, hipStream_t stream);
+// Bulk variant with one lane per vector (fp16 input, Lloyd-Max or fp8 keys,
+// Lloyd-Max values, head_dim 64/128/256, no key side streams).
+bool bulk_append_supported(const AppendArgs &a);
+hipError_t launch_append_bulk(const AppendArgs &a, hipStream_t stream);
 
 // Decode-attention launch (validated arguments).
 struct AttendArgs {

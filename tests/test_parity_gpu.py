@@ -550,6 +550,78 @@ def test_append_near_decision_midpoints(dev, d, bits):
                 x[:, :, ::-1].copy(), bits, d)
 
 
+def _fp16_near_decisions(d, bits, n, seed):
+    """fp16 vectors [n, d] each with one rotated coordinate as close to a
+    decision as fp16 allows: dense N(0,1) draws in which one input coordinate
+    x_k is solved for (rotated coordinate j on a Lloyd-Max decision midpoint,
+    or on an E4M3 rounding midpoint for bits == 8, or every third vector the
+    norm on an fp16 rounding midpoint), rounded to fp16, best of the d
+    choices of k.  Offsets of about 1e-7 .. 1e-4 on the coordinate's scale
+    result (test data only; the oracle decides every code exactly)."""
+    rng = np.random.default_rng(seed)
+    s = _signs(d).astype(np.float64)
+    H = O.hadamard(d).astype(np.float64)
+    x = rng.standard_normal((n, d)).astype(np.float16).astype(np.float64)
+    if bits == 8:
+        grid = O.e4m3_decode(np.arange(0x7F))
+        targets = 0.5 * (grid[40:72] + grid[41:73])             # rounding midpoints between 0.25 and 4
+    else:
+        _, mids = O.codebook(bits, d)
+        targets = mids * math.sqrt(d)                           # on the z / ||x|| scale
+    fp16_mids = np.array([0.5 * (float(np.float16(a)) + float(np.nextafter(np.float16(a), np.float16(np.inf))))
+                          for a in np.linspace(6.0, 16.0, 64)])
+    for r in range(n):
+        z = H @ (s * x[r])
+        S = float(x[r] @ x[r])
+        j = int(rng.integers(d))
+        cand = x[r].copy()
+        k = np.arange(d)
+        c = H[j] * s                                             # dz_j / dx_k
+        A, B = z[j] - c * cand, S - cand ** 2
+        if r % 3 == 2 and bits != 8:                             # norm on an fp16 midpoint
+            m = fp16_mids[int(rng.integers(len(fp16_mids)))]
+            v = np.sqrt(np.maximum(m * m - B, 0.0))
+            v16 = v.astype(np.float16).astype(np.float64)
+            err = np.abs(np.sqrt(B + v16 ** 2) - m)
+        elif bits == 8:                                          # y_j = z_j / sqrt(d) on an E4M3 midpoint
+            M = targets[int(rng.integers(len(targets)))] * rng.choice([-1.0, 1.0])
+            v = (M * math.sqrt(d) - A) / c
+            v16 = np.clip(v, -60000, 60000).astype(np.float16).astype(np.float64)
+            err = np.abs((A + c * v16) / math.sqrt(d) - M) / np.sqrt(B + v16 ** 2)
+        else:                                                    # z_j / ||x|| on a midpoint
+            M = targets[int(rng.integers(len(targets)))]
+            # (A + c v)^2 = M^2 (B + v^2), the root with the sign of M
+            qa, qb, qc = 1.0 - M * M, 2.0 * A * c, A * A - M * M * B
+            disc = np.sqrt(np.maximum(qb * qb - 4 * qa * qc, 0.0))
+            roots = np.stack([(-qb + disc) / (2 * qa), (-qb - disc) / (2 * qa)])
+            ok = np.sign(A + c * roots) == np.sign(M)
+            v = np.where(ok[0], roots[0], roots[1])
+            v16 = np.clip(v, -60000, 60000).astype(np.float16).astype(np.float64)
+            err = np.abs((A + c * v16) / np.sqrt(B + v16 ** 2) - M)
+        best = int(np.nanargmin(np.where(np.isfinite(err), err, np.inf)))
+        x[r, best] = v16[best]
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("d,bits", [(64, 2), (64, 4), (128, 3), (128, 4), (128, 8), (256, 2), (256, 4), (256, 8)])
+def test_append_fp16_near_decisions(dev, d, bits):
+    """fp16 input on the bulk path (one lane per vector) with rotated
+    coordinates, norms and fp8 values placed as near their decisions as fp16
+    allows (see _fp16_near_decisions) and a ragged last batch: codes and
+    norms equal the oracle outside the 1e-6 window."""
+    B, H, T = 1, 2, 300
+    x = _fp16_near_decisions(d, bits, B * H * T, seed=5 + d + bits).reshape(B, H, T, d)
+    v = _fp16_near_decisions(d, 4 if bits == 8 else bits, B * H * T, seed=9 + d + bits).reshape(B, H, T, d)
+    cache = kvq.KVCache.allocate(B, H, d, T, _fmt(bits), _fmt(4 if bits == 8 else bits), seed=W.SIGN_SEED,
+                                 device=dev)
+    cache.append(_t(x, dev), _t(v, dev), 0)
+    torch.cuda.synchronize()
+    check_codes(f"d{d} b{bits} fp16 K", cache.k_codes[:, :, :T].cpu().numpy(), cache.k_norms[:, :, :T].cpu().numpy(),
+                x, bits, d)
+    check_codes(f"d{d} b{bits} fp16 V", cache.v_codes[:, :, :T].cpu().numpy(), cache.v_norms[:, :, :T].cpu().numpy(),
+                v, 4 if bits == 8 else bits, d)
+
+
 def test_incremental_append_equals_bulk(dev):
     wl = W.WORKLOADS["llama7b_layer"].scaled(batch=2, q_heads=8, kv_heads=2, seq_len=200)
     inp = W.generate(wl)
