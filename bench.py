@@ -87,6 +87,7 @@ def parse(argv=None):
     ap.add_argument("--workload", default="two_tier", choices=sorted(W.WORKLOADS) + [t for t in TABLE if "@" in t])
     ap.add_argument("--bits", type=int, default=None, help="override code bits (bitwidth_sweep)")
     ap.add_argument("--splits", type=int, default=None)
+    ap.add_argument("--near-splits", type=int, default=None, help="near-tier splits (caches with a near tier)")
     ap.add_argument("--no-table", action="store_true", help="measure the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gate", action="store_true",
@@ -441,6 +442,8 @@ def main(argv=None) -> int:
         wl = dataclasses.replace(wl, k_bits=args.k_bits, name=f"{wl.name.split('@')[0]}@k{args.k_bits}")
     if args.splits:
         wl = wl.scaled(splits=args.splits)
+    if args.near_splits:
+        wl = wl.scaled(near_splits=args.near_splits)
     if args.qjl and wl.k_bits == 8:
         print("--qjl needs Lloyd-Max keys", file=sys.stderr)
         return 2

@@ -22,7 +22,7 @@ KVQ_LM2, KVQ_LM3, KVQ_LM4, KVQ_FP8_E4M3 = 2, 3, 4, 8
 
 EXPORTED = ("kvq_row_bytes", "kvq_lloyd_max", "kvq_make_signs", "kvq_quantize_append",
             "kvq_decode_attention", "kvq_decode_attention_gated", "kvq_decode_attention_kernel", "kvq_merge",
-            "kvq_calibrate_outliers",
+            "kvq_calibrate_outliers", "kvq_decode", "kvq_decode_workspace_bytes",
             "kvq_partials_floats",
             "kvq_status_string", "kvq_last_error")
 
@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvq_decode_attention_kernel": (ctypes.c_char_p, [CP, I32, I32]),
         "kvq_merge": (I32, [CP, P, P, I32, I32, I32, P, P, P]),
         "kvq_partials_floats": (SZ, [I32, I32, I32, I32]),
+        "kvq_decode": (I32, [CP, P, I32, I32, I32, I32, I32, P, SZ, P, P, P]),
+        "kvq_decode_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
         "kvq_status_string": (ctypes.c_char_p, [I32]),
         "kvq_last_error": (ctypes.c_char_p, []),
     }
@@ -327,3 +329,34 @@ class KVCache:
     def decode(self, q, seq_len: int, num_splits: int, num_near_splits: int = 0, lse=None):
         po, pml = self.attend(q, seq_len, num_splits, num_near_splits)
         return self.merge(po, pml, num_splits, num_near_splits, lse=lse)
+
+    def workspace(self, q_heads: int, num_splits: int, num_near_splits: int = 0):
+        """A device workspace for decode_ws (uint8, kvq_decode_workspace_bytes)."""
+        import torch
+        n = int(load().kvq_decode_workspace_bytes(self.batch, q_heads, num_splits, num_near_splits, self.head_dim))
+        if not n:
+            raise ValueError("invalid decode shape")
+        return torch.empty(n, dtype=torch.uint8, device=self.k_codes.device)
+
+    def decode_ws(self, q, seq_len: int, num_splits: int, num_near_splits: int = 0, workspace=None, out=None,
+                  lse=None):
+        """kvq_decode (split partials in `workspace`, from workspace() if None)."""
+        import torch
+        q_heads = int(q.shape[1])
+        _need(q, "q", (self.batch, q_heads, self.head_dim))
+        if out is None:
+            out = torch.empty((self.batch, q_heads, self.head_dim), dtype=torch.float32, device=q.device)
+        _need(out, "out", (self.batch, q_heads, self.head_dim), torch.float32)
+        if lse is not None:
+            _need(lse, "lse", (self.batch, q_heads), torch.float32)
+        cs = self.struct()
+        lp = 0 if lse is None else lse.data_ptr()
+        if workspace is None:
+            workspace = self.workspace(q_heads, num_splits, num_near_splits)
+        if not (workspace.is_cuda and workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous device tensor")
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(load().kvq_decode(ctypes.byref(cs), q.data_ptr(), _dtype_code(q), q_heads, seq_len, num_splits,
+                                 num_near_splits, workspace.data_ptr(), nbytes, out.data_ptr(), lp,
+                                 _stream_handle(q.device)), "kvq_decode")
+        return out

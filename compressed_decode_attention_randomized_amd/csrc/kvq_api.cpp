@@ -222,10 +222,83 @@ const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads,
   return name;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Byte layout of a decode workspace: part_o, then part_ml at the next
+// 16-byte boundary.
+size_t ws_part_o_bytes(int32_t batch, int32_t q_heads, int32_t total_splits, int32_t head_dim) {
+  return ((size_t)batch * q_heads * total_splits * head_dim * 4 + 15) / 16 * 16;
+}
+
+size_t ws_bytes(int32_t batch, int32_t q_heads, int32_t total_splits, int32_t head_dim) {
+  return ws_part_o_bytes(batch, q_heads, total_splits, head_dim) + (size_t)batch * q_heads * total_splits * 2 * 4;
+}
+
+kvq_status merge_launch(const char *fn, const kvq_cache *cache, const float *part_o, const float *part_ml,
+                        int32_t q_heads, int32_t num_splits, int32_t num_near_splits, float *out, float *lse,
+                        hipStream_t stream);
+
+// Attention into the partials at `ws`, then the merge into out/lse.
+kvq_status decode_into(const char *fn, const kvq_cache *cache, const void *q, int32_t q_dtype, int32_t q_heads,
+                       int32_t seq_len, int32_t num_splits, int32_t num_near_splits, uint8_t *ws, float *out,
+                       float *lse, hipStream_t stream) {
+  float *part_o = reinterpret_cast<float *>(ws);
+  float *part_ml = reinterpret_cast<float *>(
+      ws + ws_part_o_bytes(cache->batch, q_heads, num_splits + num_near_splits, cache->head_dim));
+  kvq::AttendArgs a;
+  kvq_status st = attend_args(fn, cache, q, q_dtype, q_heads, seq_len, num_splits, num_near_splits, part_o, part_ml,
+                              &a);
+  if (st != KVQ_OK) return st;
+  if (!out) return kvq::fail(KVQ_EINVAL, "%s: out is NULL", fn);
+  bool ok = true;
+  const hipError_t e = kvq::launch_attend(a, stream, &ok);
+  st = attend_status(fn, cache, q_heads, ok, e);
+  if (st != KVQ_OK) return st;
+  return merge_launch(fn, cache, part_o, part_ml, q_heads, num_splits, num_near_splits, out, lse, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t num_splits, int32_t num_near_splits,
+                                  int32_t head_dim) {
+  if (batch < 1 || q_heads < 1 || num_splits < 1 || num_near_splits < 0 || !kvq::valid_head_dim(head_dim)) return 0;
+  return ws_bytes(batch, q_heads, num_splits + num_near_splits, head_dim);
+}
+
+kvq_status kvq_decode(const kvq_cache *cache, const void *q, int32_t q_dtype, int32_t q_heads, int32_t seq_len,
+                      int32_t num_splits, int32_t num_near_splits, void *workspace, size_t workspace_bytes,
+                      float *out, float *lse, hipStream_t stream) {
+  const char *fn = "kvq_decode";
+  kvq::clear_error();
+  kvq_status st = check_cache(cache, fn);
+  if (st != KVQ_OK) return st;
+  if (q_heads < 1 || num_splits < 1 || num_near_splits < 0)
+    return kvq::fail(KVQ_EINVAL, "%s: q_heads=%d splits far=%d near=%d", fn, q_heads, num_splits, num_near_splits);
+  if (!workspace || !aligned(workspace, 16)) return kvq::fail(KVQ_EINVAL, "%s: workspace NULL or not 16-byte aligned", fn);
+  const size_t need = ws_bytes(cache->batch, q_heads, num_splits + num_near_splits, cache->head_dim);
+  if (workspace_bytes < need)
+    return kvq::fail(KVQ_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+  return decode_into(fn, cache, q, q_dtype, q_heads, seq_len, num_splits, num_near_splits,
+                     static_cast<uint8_t *>(workspace), out, lse, stream);
+}
+
 kvq_status kvq_merge(const kvq_cache *cache, const float *part_o, const float *part_ml, int32_t q_heads,
                      int32_t num_splits, int32_t num_near_splits, float *out, float *lse, hipStream_t stream) {
-  const char *fn = "kvq_merge";
   kvq::clear_error();
+  return merge_launch("kvq_merge", cache, part_o, part_ml, q_heads, num_splits, num_near_splits, out, lse, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+kvq_status merge_launch(const char *fn, const kvq_cache *cache, const float *part_o, const float *part_ml,
+                        int32_t q_heads, int32_t num_splits, int32_t num_near_splits, float *out, float *lse,
+                        hipStream_t stream) {
   if (!cache) return kvq::fail(KVQ_EINVAL, "%s: cache is NULL", fn);
   if (!kvq::valid_head_dim(cache->head_dim))
     return kvq::fail(KVQ_EUNSUPPORTED, "%s: head_dim=%d", fn, cache->head_dim);
@@ -242,4 +315,4 @@ kvq_status kvq_merge(const kvq_cache *cache, const float *part_o, const float *p
   return hip_status(e, fn);
 }
 
-}  // extern "C"
+}  // namespace

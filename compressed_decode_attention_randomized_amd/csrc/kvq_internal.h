@@ -10,6 +10,7 @@ namespace kvq {
 
 constexpr int kOutlierCount = 8;   // channels of the key outlier stream
 
+
 kvq_status fail(kvq_status st, const char *fmt, ...);
 void clear_error();
 bool valid_head_dim(int32_t d);

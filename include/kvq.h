@@ -259,6 +259,26 @@ kvq_status kvq_merge(const kvq_cache *cache, const float *part_o, const float *p
                      int32_t q_heads, int32_t num_splits, int32_t num_near_splits,
                      float *out, float *lse, hipStream_t stream);
 
+/* Decode attention and split merge in one call ("FoveatedKV", "Making it
+ * fast": the fused split-K pass over both tiers, then the merge of the split
+ * states with the single inverse rotation): kvq_decode_attention into split
+ * partials held in `workspace`, then kvq_merge into out/lse, two launches on
+ * `stream`.  Arguments, layouts and results as those two calls;
+ *   workspace        caller-owned device memory, 16-byte aligned, at least
+ *                    kvq_decode_workspace_bytes(batch, q_heads, num_splits,
+ *                    num_near_splits, head_dim) bytes; scratch only (its
+ *                    contents after the call are unspecified), so it must not
+ *                    be used by other work in flight on other streams.
+ * Errors: those of the two calls, and KVQ_EINVAL for a NULL, misaligned or
+ * too small workspace. */
+kvq_status kvq_decode(const kvq_cache *cache, const void *q, int32_t q_dtype, int32_t q_heads, int32_t seq_len,
+                      int32_t num_splits, int32_t num_near_splits, void *workspace, size_t workspace_bytes,
+                      float *out, float *lse, hipStream_t stream);
+
+/* Bytes of the workspace kvq_decode needs (0 for an invalid shape). */
+size_t kvq_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t num_splits, int32_t num_near_splits,
+                                  int32_t head_dim);
+
 /* Floats in part_o for the given shape (part_ml needs 2/head_dim of that). */
 size_t kvq_partials_floats(int32_t batch, int32_t q_heads, int32_t total_splits,
                            int32_t head_dim);

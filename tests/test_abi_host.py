@@ -184,3 +184,16 @@ def test_status_strings():
     for s in range(5):
         assert lib.kvq_status_string(s)
     assert lib.kvq_partials_floats(2, 4, 3, 128) == 2 * 4 * 3 * 128
+
+
+def test_decode_workspace_validation():
+    """kvq_decode refuses a missing or small workspace; the workspace size
+    follows the partials' layout."""
+    lib = kvq.load()
+    cs = _fake_cache()
+    assert lib.kvq_decode_workspace_bytes(2, 4, 3, 1, 128) == 2 * 4 * 4 * 128 * 4 + 2 * 4 * 4 * 2 * 4
+    n = lib.kvq_decode_workspace_bytes(2, 4, 3, 0, 128)
+    # both refused on the host (one byte short; NULL), so no launch is attempted
+    assert lib.kvq_decode(ctypes.byref(cs), 0x8000, 1, 4, 32, 3, 0, 0xA000, n - 1, 0xC000, 0, None) == kvq.KVQ_EINVAL
+    assert lib.kvq_decode(ctypes.byref(cs), 0x8000, 1, 4, 32, 3, 0, 0, n, 0xC000, 0, None) == kvq.KVQ_EINVAL
+    assert lib.kvq_decode_workspace_bytes(2, 4, 0, 0, 128) == 0
