@@ -22,7 +22,7 @@ KVQ_LM2, KVQ_LM3, KVQ_LM4, KVQ_FP8_E4M3 = 2, 3, 4, 8
 
 EXPORTED = ("kvq_row_bytes", "kvq_lloyd_max", "kvq_make_signs", "kvq_quantize_append",
             "kvq_decode_attention", "kvq_decode_attention_gated", "kvq_decode_attention_kernel", "kvq_merge",
-            "kvq_calibrate_outliers", "kvq_decode", "kvq_decode_workspace_bytes",
+            "kvq_calibrate_outliers", "kvq_decode", "kvq_decode_workspace_bytes", "kvq_decode_noalloc",
             "kvq_partials_floats",
             "kvq_status_string", "kvq_last_error")
 
@@ -76,6 +76,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvq_partials_floats": (SZ, [I32, I32, I32, I32]),
         "kvq_decode": (I32, [CP, P, I32, I32, I32, I32, I32, P, SZ, P, P, P]),
         "kvq_decode_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
+        "kvq_decode_noalloc": (I32, [CP, P, I32, I32, I32, I32, I32, P, P, P]),
         "kvq_status_string": (ctypes.c_char_p, [I32]),
         "kvq_last_error": (ctypes.c_char_p, []),
     }
@@ -339,8 +340,9 @@ class KVCache:
         return torch.empty(n, dtype=torch.uint8, device=self.k_codes.device)
 
     def decode_ws(self, q, seq_len: int, num_splits: int, num_near_splits: int = 0, workspace=None, out=None,
-                  lse=None):
-        """kvq_decode (split partials in `workspace`, from workspace() if None)."""
+                  lse=None, noalloc: bool = False):
+        """kvq_decode (split partials in `workspace`, from workspace() if None),
+        or kvq_decode_noalloc (the library's fixed device scratch) when noalloc."""
         import torch
         q_heads = int(q.shape[1])
         _need(q, "q", (self.batch, q_heads, self.head_dim))
@@ -351,6 +353,11 @@ class KVCache:
             _need(lse, "lse", (self.batch, q_heads), torch.float32)
         cs = self.struct()
         lp = 0 if lse is None else lse.data_ptr()
+        if noalloc:
+            _check(load().kvq_decode_noalloc(ctypes.byref(cs), q.data_ptr(), _dtype_code(q), q_heads, seq_len,
+                                             num_splits, num_near_splits, out.data_ptr(), lp,
+                                             _stream_handle(q.device)), "kvq_decode_noalloc")
+            return out
         if workspace is None:
             workspace = self.workspace(q_heads, num_splits, num_near_splits)
         if not (workspace.is_cuda and workspace.is_contiguous()):

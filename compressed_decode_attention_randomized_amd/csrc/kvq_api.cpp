@@ -286,6 +286,26 @@ kvq_status kvq_decode(const kvq_cache *cache, const void *q, int32_t q_dtype, in
                      static_cast<uint8_t *>(workspace), out, lse, stream);
 }
 
+kvq_status kvq_decode_noalloc(const kvq_cache *cache, const void *q, int32_t q_dtype, int32_t q_heads,
+                              int32_t seq_len, int32_t num_splits, int32_t num_near_splits, float *out, float *lse,
+                              hipStream_t stream) {
+  const char *fn = "kvq_decode_noalloc";
+  kvq::clear_error();
+  kvq_status st = check_cache(cache, fn);
+  if (st != KVQ_OK) return st;
+  if (q_heads < 1 || num_splits < 1 || num_near_splits < 0)
+    return kvq::fail(KVQ_EINVAL, "%s: q_heads=%d splits far=%d near=%d", fn, q_heads, num_splits, num_near_splits);
+  const size_t need = ws_bytes(cache->batch, q_heads, num_splits + num_near_splits, cache->head_dim);
+  if (need > kvq::kNoAllocScratchBytes)
+    return kvq::fail(KVQ_ERANGE, "%s: the split partials need %zu bytes; the fixed scratch holds %zu", fn, need,
+                     (size_t)kvq::kNoAllocScratchBytes);
+  void *ws = nullptr;
+  const hipError_t e = kvq::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return decode_into(fn, cache, q, q_dtype, q_heads, seq_len, num_splits, num_near_splits, static_cast<uint8_t *>(ws),
+                     out, lse, stream);
+}
+
 kvq_status kvq_merge(const kvq_cache *cache, const float *part_o, const float *part_ml, int32_t q_heads,
                      int32_t num_splits, int32_t num_near_splits, float *out, float *lse, hipStream_t stream) {
   kvq::clear_error();

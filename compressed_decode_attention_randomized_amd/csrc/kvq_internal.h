@@ -9,7 +9,10 @@
 namespace kvq {
 
 constexpr int kOutlierCount = 8;   // channels of the key outlier stream
+constexpr size_t kNoAllocScratchBytes = 16u << 20;   // fixed device scratch of kvq_decode_noalloc
 
+// This device's copy of the fixed scratch (resolved once per device).
+hipError_t noalloc_scratch(void **ptr);
 
 kvq_status fail(kvq_status st, const char *fmt, ...);
 void clear_error();

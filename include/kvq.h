@@ -279,6 +279,20 @@ kvq_status kvq_decode(const kvq_cache *cache, const void *q, int32_t q_dtype, in
 size_t kvq_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t num_splits, int32_t num_near_splits,
                                   int32_t head_dim);
 
+/* kvq_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the split partials go to a fixed device scratch
+ * array the library holds, one per GPU it runs on, until the process ends
+ * (16 MiB: for example batch 16, 64 query heads, 32 splits at head_dim 128).
+ * The call itself allocates nothing; the first call on a device resolves that
+ * device's array once.  Calls that overlap on one GPU (several streams,
+ * threads) share the array and race: serialise them.  Calls whose partials
+ * need more than the array, kvq_decode_workspace_bytes(...) > 16 MiB, return
+ * KVQ_ERANGE.  Other arguments and errors as kvq_decode. */
+kvq_status kvq_decode_noalloc(const kvq_cache *cache, const void *q, int32_t q_dtype, int32_t q_heads,
+                              int32_t seq_len, int32_t num_splits, int32_t num_near_splits, float *out, float *lse,
+                              hipStream_t stream);
+
 /* Floats in part_o for the given shape (part_ml needs 2/head_dim of that). */
 size_t kvq_partials_floats(int32_t batch, int32_t q_heads, int32_t total_splits,
                            int32_t head_dim);

@@ -186,10 +186,15 @@ def test_status_strings():
     assert lib.kvq_partials_floats(2, 4, 3, 128) == 2 * 4 * 3 * 128
 
 
-def test_decode_workspace_validation():
-    """kvq_decode refuses a missing or small workspace; the workspace size
-    follows the partials' layout."""
+def test_noalloc_size_limit_and_workspace_validation():
+    """kvq_decode_noalloc refuses partials larger than its fixed scratch
+    (16 MiB) before any launch; kvq_decode refuses a missing or small
+    workspace; the workspace size follows the partials' layout."""
     lib = kvq.load()
+    cs = _fake_cache(batch=64, kv_heads=64)
+    assert lib.kvq_decode_workspace_bytes(64, 64, 64, 0, 128) > 16 << 20
+    r = lib.kvq_decode_noalloc(ctypes.byref(cs), 0x8000, 1, 64, 32, 64, 0, 0xC000, 0, None)
+    assert r == kvq.KVQ_ERANGE and "fixed scratch" in lib.kvq_last_error().decode()
     cs = _fake_cache()
     assert lib.kvq_decode_workspace_bytes(2, 4, 3, 1, 128) == 2 * 4 * 4 * 128 * 4 + 2 * 4 * 4 * 2 * 4
     n = lib.kvq_decode_workspace_bytes(2, 4, 3, 0, 128)
