@@ -5,20 +5,23 @@
 // every code row is read from HBM once for all G heads.
 //
 // Per work-group:
-//   1. the G queries are loaded into LDS; for far splits they are sign-flipped
-//      and Walsh-Hadamard transformed there (the query is rotated once, keys
-//      are never rotated back); each is pre-scaled by log2(e)/sqrt(d) (near)
-//      or log2(e)/d (far: rotation normalisation times the softmax scale);
+//   1. every lane requests its row of the first block of tokens; meanwhile
+//      wave 0 loads the G queries and, for far splits, sign-flips and
+//      Walsh-Hadamard transforms them in registers (the query is rotated
+//      once, keys are never rotated back) and stores them to LDS, one
+//      barrier; each lane takes its coordinates pre-scaled by
+//      log2(e)/sqrt(d) (near) or log2(e)/d (far: rotation normalisation
+//      times the softmax scale);
 //   2. each token row is processed by D/DPL lanes, each lane owning DPL
 //      consecutive coordinates: the lane reads its slice of the packed key row
-//      (one vector load), looks its codes up in LDS (two 2- or 3-bit codes
-//      per read from a pair table, 4-bit codes one per read; fp8 keys are
-//      converted in hardware, two per instruction) and accumulates
-//      q~ . c[code] for the G heads; the slice sums are combined by
-//      xor-shuffles and multiplied by the fp16 norm;
-//   3. online softmax per lane slot in base 2 (one exp2 per score, the running
-//      state rescaled only when the maximum grows); values are accumulated in
-//      the rotated domain straight from their codes;
+//      (nontemporal vector loads), looks its codes up in LDS (two 2- or 3-bit
+//      codes per read from a pair table, 4-bit codes one per read at offsets
+//      taken with SDWA byte selects; fp8 keys are converted in hardware, two
+//      per instruction) and accumulates q~ . c[code] for the G heads; the
+//      slice sums are combined by DPP adds and multiplied by the fp16 norm;
+//   3. online softmax per lane slot in base 2 (one exp2 per score; the state
+//      is rescaled only when a score passes the reference point by kSlack);
+//      values are accumulated in the rotated domain straight from their codes;
 //   4. the slot states are merged by xor-shuffles inside the wave and through
 //      LDS across the four waves; the split writes (m, l) and sum p v / l.
 // Key side streams (far tier), both folded into each lane's partial score
@@ -39,6 +42,7 @@
 #include <stdint.h>
 
 #include "kvq_internal.h"
+#include "kvq_lane.h"
 
 namespace kvq {
 namespace {
@@ -82,34 +86,40 @@ struct FarGate {
 };
 
 // Loads NB bytes (NB a multiple of 2) at p into 32-bit words, using the widest
-// access the slice alignment allows.
+// access the slice alignment allows.  Cache rows are read once per launch, so
+// the loads carry the nontemporal hint (streamed past the caches instead of
+// allocated in them: a plain read of a 947 MB buffer by 4864 work-groups
+// measured 5.94 TB/s with ordinary 16-byte loads and 6.43 TB/s with these).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int NB>
 __device__ inline void load_slice(const uint8_t *p, uint32_t (&w)[(NB + 3) / 4]) {
   if constexpr (NB % 16 == 0) {
 #pragma unroll
     for (int i = 0; i < NB / 16; ++i) {
-      const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
       w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
     }
   } else if constexpr (NB % 8 == 0) {
 #pragma unroll
     for (int i = 0; i < NB / 8; ++i) {
-      const uint2 v = reinterpret_cast<const uint2 *>(p)[i];
+      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p) + i);
       w[2 * i] = v.x; w[2 * i + 1] = v.y;
     }
   } else if constexpr (NB % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < NB / 4; ++i) w[i] = reinterpret_cast<const uint32_t *>(p)[i];
+    for (int i = 0; i < NB / 4; ++i) w[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p) + i);
   } else {
 #pragma unroll
     for (int i = 0; i < (NB + 3) / 4; ++i) w[i] = 0;
 #pragma unroll
     for (int i = 0; i < NB / 2; ++i) {
-      const uint32_t h = reinterpret_cast<const uint16_t *>(p)[i];
+      const uint32_t h = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p) + i);
       w[i >> 1] |= h << (16 * (i & 1));
     }
   }
 }
+__device__ inline uint32_t load_u16(const uint16_t *p) { return __builtin_nontemporal_load(p); }
 
 // Code e of an LSB-first bit stream held in 32-bit words.
 template <int B>
@@ -119,18 +129,53 @@ __device__ inline uint32_t code_at(const uint32_t *w, int e) {
   return ((w[wi] >> sh) | (w[wi + 1] << (32 - sh))) & ((1u << B) - 1u);
 }
 
+// Table offsets (4 c) of the eight 4-bit codes of w, code e at bits 4e..4e+3:
+// byte k of w << 2 holds code 2k at bits 2..5 and byte k of w >> 2 code
+// 2k + 1, so each offset is one v_and_b32 with an SDWA byte select (the
+// compiler would fold the pre-shifts back into a shift and a mask per code).
+template <int K>
+__device__ inline uint32_t masked_byte(uint32_t w) {
+  uint32_t r;
+  if constexpr (K == 0) r = w & 0x3Cu;
+  if constexpr (K == 1) asm("v_and_b32_sdwa %0, 60, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(w));
+  if constexpr (K == 2) asm("v_and_b32_sdwa %0, 60, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(w));
+  if constexpr (K == 3) asm("v_and_b32_sdwa %0, 60, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(w));
+  return r;
+}
+__device__ inline void nibble_offsets(uint32_t w, uint32_t (&o)[8]) {
+  const uint32_t a = w << 2, b = w >> 2;
+  o[0] = masked_byte<0>(a); o[1] = masked_byte<0>(b);
+  o[2] = masked_byte<1>(a); o[3] = masked_byte<1>(b);
+  o[4] = masked_byte<2>(a); o[5] = masked_byte<2>(b);
+  o[6] = masked_byte<3>(a); o[7] = masked_byte<3>(b);
+}
+__device__ inline float table_at(const float *lut, uint32_t off) {
+  return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(lut) + off);
+}
+
 __device__ inline float half_to_float(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
 // Running softmax state of one lane slot for G heads (base-2 logits).
+// m is a reference point, not necessarily the running maximum: the state is
+// rescaled only when a score exceeds m by more than kSlack, so weights
+// 2^(s - m) stay below 2^kSlack and l, acc hold sum 2^(s - m) (v) for that m.
+// The quotient acc / l is the same for any m; the rescale, a branch a wave
+// takes whenever one of its slots needs it, then runs a few times per slot
+// instead of at every new maximum.  mx tracks the true maximum (one max per
+// score), and the split's l is restated against it when it is written, so
+// (m, l) keeps its meaning (split maximum, sum of exp(s - maximum)); m never
+// exceeds mx and mx never exceeds m + kSlack.
+constexpr float kSlack = 8.f;
 template <int G, int DPL>
 struct State {
-  float m[G], l[G], acc[G][DPL];
+  float m[G], mx[G], l[G], acc[G][DPL];
   __device__ void init() {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       m[h] = -INFINITY;
+      mx[h] = -INFINITY;
       l[h] = 0.f;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
@@ -138,8 +183,8 @@ struct State {
   }
   // Adds one token with scores s[h] (already -inf if the token is absent);
   // returns the weights p[h] for the value accumulation.  For G >= 2 the
-  // exponentials are the hardware's v_exp_f32 (weights are at most 1; one
-  // that would be below 2^-126 becomes 0, which no fp32 sum of weights
+  // exponentials are the hardware's v_exp_f32 (weights are at most 2^kSlack;
+  // one that would be below 2^-126 becomes 0, which no fp32 sum of weights
   // would notice): 3-6% on those launches; the G = 1 launches measured
   // slower with it (two_tier 171.9 -> 184.4 us) and keep exp2f.
   __device__ static float exp2w(float x) {
@@ -149,7 +194,7 @@ struct State {
   __device__ void add_scores(const float (&s)[G], float (&p)[G]) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      if (s[h] > m[h]) {
+      if (s[h] > m[h] + kSlack) {
         const float alpha = exp2w(m[h] - s[h]);
         l[h] *= alpha;
 #pragma unroll
@@ -158,6 +203,7 @@ struct State {
       }
       p[h] = (s[h] == -INFINITY) ? 0.f : exp2w(s[h] - m[h]);
       l[h] += p[h];
+      mx[h] = fmaxf(mx[h], s[h]);
     }
   }
   // Merge with the state held by lane (lane ^ mask).
@@ -166,6 +212,7 @@ struct State {
     for (int h = 0; h < G; ++h) {
       const float mo = __shfl_xor(m[h], mask);
       const float lo = __shfl_xor(l[h], mask);
+      mx[h] = fmaxf(mx[h], __shfl_xor(mx[h], mask));
       const float M = fmaxf(m[h], mo);
       const float a = (m[h] == -INFINITY) ? 0.f : exp2f(m[h] - M);
       const float b = (mo == -INFINITY) ? 0.f : exp2f(mo - M);
@@ -273,7 +320,7 @@ struct FarTier {
   }
   __device__ void load_keys(int t, int ds) {
     load_slice<KNB>(krow0 + (size_t)t * KROW + ds * KNB, kw);
-    nk = (KB == 8) ? 1.f : half_to_float(kn0[t]);
+    nk = (KB == 8) ? 1.f : half_to_float(load_u16(kn0 + t));
     if constexpr (OUT) {
       oc = *reinterpret_cast<const uint2 *>(oc0 + (size_t)t * kOutlierCount);
       osc = os0[t];
@@ -287,7 +334,7 @@ struct FarTier {
   }
   __device__ void load_values(int t, int ds) {
     load_slice<VNB>(vrow0 + (size_t)t * VROW + ds * VNB, vw);
-    nv = half_to_float(vn0[t]);
+    nv = half_to_float(load_u16(vn0 + t));
   }
   __device__ void score(const float (&qr)[G][DPL], float (&part)[G]) const {
 #pragma unroll
@@ -306,6 +353,18 @@ struct FarTier {
         const float2_t c = pair_entry(pairk, pair_at<KB>(kw, e >> 1), slot8);
 #pragma unroll
         for (int h = 0; h < G; ++h) part[h] = fmaf(qr[h][e + 1], c.y, fmaf(qr[h][e], c.x, part[h]));
+      }
+    } else if constexpr (KB == 4 && DPL % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < DPL / 8; ++i) {
+        uint32_t o[8];
+        nibble_offsets(kw[i], o);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float c = table_at(lutk, o[u]);
+#pragma unroll
+          for (int h = 0; h < G; ++h) part[h] = fmaf(qr[h][8 * i + u], c, part[h]);
+        }
       }
     } else {
 #pragma unroll
@@ -359,6 +418,18 @@ struct FarTier {
           st.acc[h][e + 1] = fmaf(w[h], c.y, st.acc[h][e + 1]);
         }
       }
+    } else if constexpr (VB == 4 && DPL % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < DPL / 8; ++i) {
+        uint32_t o[8];
+        nibble_offsets(vw[i], o);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float c = table_at(lutv, o[u]);
+#pragma unroll
+          for (int h = 0; h < G; ++h) st.acc[h][8 * i + u] = fmaf(w[h], c, st.acc[h][8 * i + u]);
+        }
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
@@ -405,26 +476,25 @@ struct NearTier {
 };
 
 // Online softmax over tokens [t0, t1): each lane slot takes every TPB-th
-// token.  PIPE: the next block's rows are requested before this block's
-// arithmetic (two blocks of loads in flight per wave, at the cost of the
-// second block's registers).
-
-template <int G, int DPL, int LPT, bool PIPE, typename Tier>
-__device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G, DPL> &st, int t0, int t1) {
+// token.  On entry cur holds the lane's row of the first block (first_block,
+// issued before the query prologue so that round trip overlaps it); the
+// next block's rows are requested before this block's arithmetic, so one
+// block is in flight while a wave computes.  (Buffers kept in fixed
+// registers by unrolling two blocks per iteration need no copies, but the
+// scheduler then interleaves the two blocks and the kernel needs 20-30 more
+// VGPRs, a wave per SIMD fewer.)
+template <int G, int DPL, int LPT, typename Tier>
+__device__ void token_loop(Tier &cur, const float (&qr)[G][DPL], State<G, DPL> &st, int t0, int t1) {
   constexpr int TPW = 64 / LPT;
   constexpr int TPB = TPW * kWaves;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ds = lane % LPT, ts = lane / LPT;
-  if (t0 >= t1) return;                       // empty split: no row to read
   int t = t0 + wave * TPW + ts;
-  Tier cur = proto;
-  if constexpr (PIPE) cur.load(t < t1 ? t : t0, ds);
   for (int base = t0; base < t1; base += TPB) {
     const bool valid = t < t1;
     const int tn = t + TPB;
-    Tier nxt = proto;
-    if constexpr (PIPE) nxt.load(tn < t1 ? tn : t0, ds);
-    else cur.load(valid ? t : t0, ds);
+    Tier nxt = cur;
+    nxt.load(tn < t1 ? tn : t0, ds);
     float part[G];
     cur.score(qr, part);
 #pragma unroll
@@ -435,9 +505,17 @@ __device__ void token_loop(const Tier &proto, const float (&qr)[G][DPL], State<G
     for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
     st.add_scores(s, p);
     cur.accumulate(p, st);
-    if constexpr (PIPE) cur = nxt;
+    cur = nxt;
     t = tn;
   }
+}
+
+// Loads the lane's row of the first block of [t0, t1) into X (see token_loop).
+template <int LPT, typename Tier>
+__device__ void first_block(Tier &X, int t0, int t1) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = t0 + wave * (64 / LPT) + lane / LPT;
+  if (t0 < t1) X.load(t < t1 ? t : t0, lane % LPT);
 }
 
 // Far-tier loop with the score gate and spike flags.  A token whose score is
@@ -515,231 +593,79 @@ __device__ void token_loop_gated(const Tier &proto, const float (&qr)[G][DPL], S
   if (vb) B.accumulate(pb, st);
 }
 
-// NEAR: the launch has near-tier splits (without them the kernel carries no
-// registers for the near path).
-// GATED: score gate and spike flags; X: key side stream (none, outliers, QJL).
-template <int D, int KB, int VB, int G, bool NEAR, bool GATED, int X = kNoExtra>
-__global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
-  constexpr bool OUT = X == kOutliers, QJL = X == kQjl;
-  // G = 1: 32 coordinates per lane, except where near-tier fp16 rows would
-  // double the pipelined registers; G >= 4 with a near tier (where the far
-  // codes allow whole-word slices): 8, so the near rows' fp16 slices and the
-  // G x DPL arrays leave room for three or four waves per SIMD (the
-  // decode-buffer launch: 27.5 -> 25.5 us; on far-only launches the extra
-  // reduction round and the softmax repeated over twice the lanes cost more
-  // than the occupancy gains).  Loads pipelined at every G (the next block's
-  // rows cost a few registers beside the G x DPL query and accumulator
-  // arrays, and halve the memory round trips a wave waits on).
-  constexpr int DPL = (G == 1 && !NEAR) ? 32 : ((NEAR && G >= 4 && KB != 3 && VB != 3) ? 8 : 16);
-  constexpr bool kPipe = true;
-  constexpr int LPT = D / DPL;
-  static_assert(LPT >= 1 && LPT <= 64, "lane mapping");
-
-  __shared__ float qs[G][D];
-  constexpr int kPairK = pair_table_bytes<KB>(), kPairV = pair_table_bytes<VB>();
-  __shared__ float lutk[16];
-  __shared__ float lutv[16];
-  __shared__ __attribute__((aligned(16))) uint8_t pairtab[(kPairK + kPairV) > 0 ? kPairK + kPairV : 16];
-  __shared__ float red_ml[kWaves][G][2];
-  __shared__ float red_acc[kWaves][G][D];
-  __shared__ float ps[QJL ? G : 1][QJL ? D : 1];
-
-  const int tid = threadIdx.x;
-  const int split = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int b = bh / P.kv_heads, hkv = bh - b * P.kv_heads;
-  const bool near = NEAR && split < P.num_near_splits;
-  const int total_splits = P.num_near_splits + P.num_splits;
-
-  // ---- query heads hkv*G .. hkv*G+G-1 into LDS, rotated for far splits ----
-  for (int i = tid; i < G * D; i += kBlock) {
-    const int h = i / D, j = i - (i / D) * D;
-    const size_t qi = ((size_t)b * P.q_heads + hkv * G + h) * D + j;
-    float v = P.q_f16 ? half_to_float(static_cast<const uint16_t *>(P.q)[qi]) : static_cast<const float *>(P.q)[qi];
-    if (!near && P.signs[j] < 0) v = -v;
-    qs[h][j] = v;
+// Query rows hkv*G .. hkv*G+G-1 of batch entry b into qs, sign-flipped and
+// Walsh-Hadamard transformed when `rotate` (far splits).  Wave 0 does it in
+// registers: lane i holds coordinates i*E .. i*E+E-1 (E = D/64) of each
+// row, the butterflies of stride below E run inside the lane and the others
+// across lanes by DPP and permlane swaps (no LDS round trip, no barrier per
+// stage); the other waves go on with their own prologue work.  The caller's
+// barrier publishes qs.
+template <int D, int G>
+__device__ void query_rows(const Params &P, int b, int hkv, bool rotate, float (*qs)[D]) {
+  constexpr int E = D / 64;
+  if ((threadIdx.x >> 6) != 0) return;
+  const int lane = threadIdx.x & 63;
+  float v[G][E];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      v[h][e] = P.q_f16 ? half_to_float(static_cast<const uint16_t *>(P.q)[row + e])
+                        : static_cast<const float *>(P.q)[row + e];
   }
-  if (!near) {
-    if (KB != 8 && tid < (1 << KB)) lutk[tid] = P.k_centroids[tid];
-    if (tid < (1 << VB)) lutv[tid] = P.v_centroids[tid];
-    // pair tables: entry (c[f & m], c[f >> B]) of field f in 32 slots
-    if constexpr (kPairK > 0) {
-      for (int i = tid; i < kPairK / 8; i += kBlock) {
-        const int f = i >> 5;
-        *reinterpret_cast<float2_t *>(pairtab + i * 8) =
-            (float2_t){P.k_centroids[f & ((1 << KB) - 1)], P.k_centroids[f >> KB]};
-      }
+  if (rotate) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool neg = P.signs[lane * E + e] < 0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) v[h][e] = neg ? -v[h][e] : v[h][e];
     }
-    if constexpr (kPairV > 0) {
-      for (int i = tid; i < kPairV / 8; i += kBlock) {
-        const int f = i >> 5;
-        *reinterpret_cast<float2_t *>(pairtab + kPairK + i * 8) =
-            (float2_t){P.v_centroids[f & ((1 << VB) - 1)], P.v_centroids[f >> VB]};
-      }
-    }
-  }
-  __syncthreads();
-  if (!near) {
-    for (int len = 1; len < D; len <<= 1) {
-      for (int i = tid; i < G * D / 2; i += kBlock) {
-        const int h = i / (D / 2), k = i - h * (D / 2);
-        const int lo = (k / len) * 2 * len + (k % len);
-        const float a = qs[h][lo], c = qs[h][lo + len];
-        qs[h][lo] = a + c;
-        qs[h][lo + len] = a - c;
-      }
-      __syncthreads();
-    }
-  }
-
-  const float prescale = near ? kLog2e / sqrtf((float)D) : kLog2e / (float)D;
-  if constexpr (QJL) {
-    if (!near) {
-      // p = S (q~ pre-scaled) per head.  Thread t takes the four columns
-      // 4c..4c+3 of S^T (c = t % (D/4), one 16-byte load per row) over its
-      // range of rows (t / (D/4)), sixteen loads in flight; the ranges of a
-      // wave are summed by shuffles, the four waves' sums through red_acc
-      // (unused until the epilogue), in a fixed order.
-      constexpr int CG = D / 4, R = kBlock / CG, JR = D / R, JC = JR < 16 ? JR : 16;
-      const int c = tid % CG, r = tid / CG;
-      float acc[G][4];
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.f;
-      const float4 *col = reinterpret_cast<const float4 *>(P.qjl_proj) + c;
-      for (int j0 = r * JR; j0 < (r + 1) * JR; j0 += JC) {
-        float4 sv[JC];
+    for (int len = 1; len < E; len <<= 1) {
 #pragma unroll
-        for (int u = 0; u < JC; ++u) sv[u] = col[(size_t)(j0 + u) * CG];
-#pragma unroll
-        for (int u = 0; u < JC; ++u) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float qv = qs[h][j0 + u];
-            acc[h][0] = fmaf(sv[u].x, qv, acc[h][0]);
-            acc[h][1] = fmaf(sv[u].y, qv, acc[h][1]);
-            acc[h][2] = fmaf(sv[u].z, qv, acc[h][2]);
-            acc[h][3] = fmaf(sv[u].w, qv, acc[h][3]);
-          }
-        }
-      }
-      const int lane0 = tid & 63, wave0 = tid >> 6;
-#pragma unroll
-      for (int m = CG; m < 64; m <<= 1) {
+      for (int e = 0; e < E; ++e) {
+        if (e & len) continue;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[h][e] += __shfl_xor(acc[h][e], m);
+          const float x = v[h][e], y = v[h][e + len];
+          v[h][e] = x + y;
+          v[h][e + len] = x - y;
         }
       }
-      if (lane0 < CG) {
+    }
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-          *reinterpret_cast<float4 *>(&red_acc[wave0][h][4 * c]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      }
-      __syncthreads();
-      for (int o = tid; o < G * D; o += kBlock) {
-        const int h = o / D, i = o - (o / D) * D;
-        float v = 0.f;
+    for (int h = 0; h < G; ++h) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) v += red_acc[w][h][i];
-        ps[h][i] = v * prescale;
-      }
-      __syncthreads();
+      for (int e = 0; e < E; ++e) v[h][e] = fwht_lanes(v[h][e], lane);
     }
   }
-
-  const int lane = tid & 63, wave = tid >> 6;
-  const int ds = lane % LPT;
-  float qr[G][DPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) qr[h][e] = qs[h][ds * DPL + e] * prescale;
+    for (int e = 0; e < E; ++e) qs[h][lane * E + e] = v[h][e];
   }
+}
 
-  State<G, DPL> st;
-  st.init();
-  if (near) {
-    if constexpr (NEAR) {
-      const int chunk = ((P.near_len + P.num_near_splits - 1) / P.num_near_splits + 31) / 32 * 32;
-      const int t0 = min(P.near_len, split * chunk), t1 = min(P.near_len, t0 + chunk);
-      NearTier<D, G, DPL> tier;
-      const size_t base = (size_t)bh * P.near_len * D * 2;
-      tier.krow0 = reinterpret_cast<const uint8_t *>(P.near_k) + base;
-      tier.vrow0 = reinterpret_cast<const uint8_t *>(P.near_v) + base;
-      token_loop<G, DPL, LPT, kPipe>(tier, qr, st, t0, t1);
-    }
-  } else {
-    const int fs = split - P.num_near_splits;
-    const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + 31) / 32 * 32;
-    const int t0 = min(P.seq_len, fs * chunk), t1 = min(P.seq_len, t0 + chunk);
-    FarTier<D, KB, VB, G, DPL, X> tier;
-    if constexpr (QJL) {
+// The lane's DPL query coordinates (slice ds), pre-scaled.
+template <int D, int G, int DPL>
+__device__ void lane_query(const float (*qs)[D], float scale, float (&qr)[G][DPL]) {
+  const int ds = (threadIdx.x & 63) % (D / DPL);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float sum = 0.f;
+  for (int h = 0; h < G; ++h) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) {
-          const float v = ps[h][ds * DPL + e];
-          tier.pq[h][e] = 2.f * v;
-          sum += v;
-        }
-        tier.psum[h] = sum;
-      }
-      tier.zs0 = P.qjl_signs + (size_t)bh * P.capacity * (D / 8);
-      tier.zn0 = P.qjl_norms + (size_t)bh * P.capacity;
-    }
-    if constexpr (OUT) {
-      // the query at the outlier channels (original domain), scaled to log2 units of s
-      // the lane's channels k = ds + LPT u (< 8); others get q = 0
-      const float sc = kLog2e / sqrtf((float)D);
-      const int32_t *oi = P.out_idx + (size_t)bh * kOutlierCount;
-      constexpr int kOPL = decltype(tier)::kOPL;
-      const int ods = (tid & 63) % LPT;
-#pragma unroll
-      for (int u = 0; u < kOPL; ++u) {
-        const int k = ods + LPT * u;
-        const bool has = k < kOutlierCount;
-        const int c = has ? oi[k] : 0;
-        tier.osel[u] = has ? (uint32_t)(8 * k) : 0u;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const size_t qrow = ((size_t)b * P.q_heads + hkv * G + h) * D;
-          const float v = P.q_f16 ? half_to_float(static_cast<const uint16_t *>(P.q)[qrow + c])
-                                  : static_cast<const float *>(P.q)[qrow + c];
-          tier.qo[h][u] = has ? v * sc : 0.f;
-        }
-      }
-      tier.oc0 = P.out_codes + (size_t)bh * P.capacity * kOutlierCount;
-      tier.os0 = P.out_scales + (size_t)bh * P.capacity;
-    }
-    tier.krow0 = P.k_codes + (size_t)bh * P.capacity * (D * KB / 8);
-    tier.vrow0 = P.v_codes + (size_t)bh * P.capacity * (D * VB / 8);
-    tier.kn0 = P.k_norms + (size_t)bh * P.capacity;
-    tier.vn0 = P.v_norms + (size_t)bh * P.capacity;
-    tier.lutk = lutk;
-    tier.lutv = lutv;
-    tier.pairk = pairtab;
-    tier.pairv = pairtab + kPairK;
-    tier.slot8 = (uint32_t)(tid & 31) * 8;
-    if constexpr (GATED) {
-      constexpr float kGate2 = 16.f * kLog2e;     // e^-16 in log2 units
-      FarGate<G> fg;
-      const size_t row0 = (size_t)b * P.q_heads + (size_t)hkv * G;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        fg.gate[h] = P.gate_ref ? P.gate_ref[row0 + h] * kLog2e - kGate2 : -INFINITY;
-        fg.spike[h] = P.spike_ref ? P.spike_ref[row0 + h] * kLog2e : INFINITY;
-      }
-      fg.bits = P.spike_ref ? P.spike_bits + row0 * P.spike_words : nullptr;
-      fg.words = P.spike_words;
-      token_loop_gated<G, DPL, LPT>(tier, qr, st, t0, t1, fg);
-    } else {
-      token_loop<G, DPL, LPT, kPipe>(tier, qr, st, t0, t1);
-    }
+    for (int e = 0; e < DPL; ++e) qr[h][e] = qs[h][ds * DPL + e] * scale;
   }
+}
 
-  // ---- merge the lane slots of this wave, then the four waves ----
+// Merges the lane slots of each wave, then the four waves, and writes the
+// split's normalised partial output and its (m, l).
+template <int D, int G, int DPL>
+__device__ void write_split(const Params &P, State<G, DPL> &st, int b, int hkv, int split,
+                            float (*red_ml)[G][3], float (*red_acc)[G][D]) {
+  constexpr int LPT = D / DPL;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ds = lane % LPT;
+  const int total_splits = P.num_near_splits + P.num_splits;
 #pragma unroll
   for (int m = LPT; m < 64; m <<= 1) st.merge_xor(m);
   if (lane < LPT) {
@@ -750,15 +676,19 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
       if (lane == 0) {
         red_ml[wave][h][0] = st.m[h];
         red_ml[wave][h][1] = st.l[h];
+        red_ml[wave][h][2] = st.mx[h];
       }
     }
   }
   __syncthreads();
   for (int i = tid; i < G * D; i += kBlock) {
     const int h = i / D, j = i - (i / D) * D;
-    float M = -INFINITY;
+    float M = -INFINITY, MX = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][h][0]);
+    for (int w = 0; w < kWaves; ++w) {
+      M = fmaxf(M, red_ml[w][h][0]);
+      MX = fmaxf(MX, red_ml[w][h][2]);
+    }
     float l = 0.f, o = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -770,10 +700,233 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     const size_t row = ((size_t)b * P.q_heads + hkv * G + h) * total_splits + split;
     P.part_o[row * D + j] = (l > 0.f) ? o / l : 0.f;
     if (j == 0) {
-      P.part_ml[row * 2 + 0] = (M == -INFINITY) ? -INFINITY : M * kLn2;
-      P.part_ml[row * 2 + 1] = l;
+      // l restated against the split maximum: M <= MX <= M + kSlack
+      P.part_ml[row * 2 + 0] = (MX == -INFINITY) ? -INFINITY : MX * kLn2;
+      P.part_ml[row * 2 + 1] = (MX == -INFINITY) ? 0.f : l * exp2f(M - MX);
     }
   }
+}
+
+// NEAR: the launch has near-tier splits (without them the kernel carries no
+// registers for the near path).
+// GATED: score gate and spike flags; X: key side stream (none, outliers, QJL).
+template <int D, int KB, int VB, int G, bool NEAR, bool GATED, int X = kNoExtra>
+__global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
+  constexpr bool OUT = X == kOutliers, QJL = X == kQjl;
+  // Coordinates per lane.  G = 1 without a near tier: 32 (two 16-byte fp8
+  // or 32-bit-code slices per token, half the per-token softmax lanes of
+  // 16); with one, 16 on both tiers (near-tier fp16 rows would double the
+  // buffered registers at 32, and 32 on the far splits alone measured slower
+  // on the two-tier cache, 163.7 against 158.3 us); G >= 4 with a near tier
+  // (where the far codes allow whole-word slices): 8 on both, so the near
+  // rows' fp16 slices and the G x DPL arrays leave room for three or four
+  // waves per SIMD (the decode-buffer launch: 27.5 -> 25.5 us; on far-only
+  // launches the extra reduction round and the softmax repeated over twice
+  // the lanes cost more than the occupancy gains); 16 otherwise.
+  constexpr int DPLN = (NEAR && G >= 4 && KB != 3 && VB != 3) ? 8 : 16;
+  constexpr int DPLF = (G == 1 && !NEAR) ? 32 : DPLN;
+  constexpr int LPTN = D / DPLN, LPTF = D / DPLF;
+  static_assert(LPTF >= 1 && LPTN <= 64, "lane mapping");
+
+  __shared__ float qs[G][D];
+  constexpr int kPairK = pair_table_bytes<KB>(), kPairV = pair_table_bytes<VB>();
+  __shared__ float lutk[16];
+  __shared__ float lutv[16];
+  __shared__ __attribute__((aligned(16))) uint8_t pairtab[(kPairK + kPairV) > 0 ? kPairK + kPairV : 16];
+  __shared__ float red_ml[kWaves][G][3];
+  __shared__ float red_acc[kWaves][G][D];
+  __shared__ float ps[QJL ? G : 1][QJL ? D : 1];
+
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / P.kv_heads, hkv = bh - b * P.kv_heads;
+
+  if constexpr (NEAR) {
+    if (split < P.num_near_splits) {
+      const int chunk = ((P.near_len + P.num_near_splits - 1) / P.num_near_splits + 31) / 32 * 32;
+      const int t0 = min(P.near_len, split * chunk), t1 = min(P.near_len, t0 + chunk);
+      NearTier<D, G, DPLN> tier;
+      const size_t base = (size_t)bh * P.near_len * D * 2;
+      tier.krow0 = reinterpret_cast<const uint8_t *>(P.near_k) + base;
+      tier.vrow0 = reinterpret_cast<const uint8_t *>(P.near_v) + base;
+      first_block<LPTN>(tier, t0, t1);
+      query_rows<D, G>(P, b, hkv, false, qs);
+      __syncthreads();
+      float qr[G][DPLN];
+      lane_query<D, G, DPLN>(qs, kLog2e / sqrtf((float)D), qr);
+      State<G, DPLN> st;
+      st.init();
+      token_loop<G, DPLN, LPTN>(tier, qr, st, t0, t1);
+      write_split<D, G, DPLN>(P, st, b, hkv, split, red_ml, red_acc);
+      return;
+    }
+  }
+
+  // ---- far split ----
+  const int fs = split - P.num_near_splits;
+  const int chunk = ((P.seq_len + P.num_splits - 1) / P.num_splits + 31) / 32 * 32;
+  const int t0 = min(P.seq_len, fs * chunk), t1 = min(P.seq_len, t0 + chunk);
+  using Far = FarTier<D, KB, VB, G, DPLF, X>;
+  Far tier;
+  tier.krow0 = P.k_codes + (size_t)bh * P.capacity * (D * KB / 8);
+  tier.vrow0 = P.v_codes + (size_t)bh * P.capacity * (D * VB / 8);
+  tier.kn0 = P.k_norms + (size_t)bh * P.capacity;
+  tier.vn0 = P.v_norms + (size_t)bh * P.capacity;
+  tier.lutk = lutk;
+  tier.lutv = lutv;
+  tier.pairk = pairtab;
+  tier.pairv = pairtab + kPairK;
+  tier.slot8 = (uint32_t)(tid & 31) * 8;
+  if constexpr (OUT) {
+    tier.oc0 = P.out_codes + (size_t)bh * P.capacity * kOutlierCount;
+    tier.os0 = P.out_scales + (size_t)bh * P.capacity;
+  }
+  if constexpr (QJL) {
+    tier.zs0 = P.qjl_signs + (size_t)bh * P.capacity * (D / 8);
+    tier.zn0 = P.qjl_norms + (size_t)bh * P.capacity;
+  }
+  if constexpr (!GATED) first_block<LPTF>(tier, t0, t1);
+
+  // ---- rotated query into LDS, centroid tables ----
+  query_rows<D, G>(P, b, hkv, true, qs);
+  if (KB != 8 && tid < (1 << KB)) lutk[tid] = P.k_centroids[tid];
+  if (tid < (1 << VB)) lutv[tid] = P.v_centroids[tid];
+  // pair tables: entry (c[f & m], c[f >> B]) of field f in 32 slots
+  if constexpr (kPairK > 0) {
+    for (int i = tid; i < kPairK / 8; i += kBlock) {
+      const int f = i >> 5;
+      *reinterpret_cast<float2_t *>(pairtab + i * 8) =
+          (float2_t){P.k_centroids[f & ((1 << KB) - 1)], P.k_centroids[f >> KB]};
+    }
+  }
+  if constexpr (kPairV > 0) {
+    for (int i = tid; i < kPairV / 8; i += kBlock) {
+      const int f = i >> 5;
+      *reinterpret_cast<float2_t *>(pairtab + kPairK + i * 8) =
+          (float2_t){P.v_centroids[f & ((1 << VB) - 1)], P.v_centroids[f >> VB]};
+    }
+  }
+  __syncthreads();
+
+  const float prescale = kLog2e / (float)D;
+  if constexpr (QJL) {
+    // p = S (q~ pre-scaled) per head.  Thread t takes the four columns
+    // 4c..4c+3 of S^T (c = t % (D/4), one 16-byte load per row) over its
+    // range of rows (t / (D/4)), sixteen loads in flight; the ranges of a
+    // wave are summed by shuffles, the four waves' sums through red_acc
+    // (unused until the epilogue), in a fixed order.
+    constexpr int CG = D / 4, R = kBlock / CG, JR = D / R, JC = JR < 16 ? JR : 16;
+    const int c = tid % CG, r = tid / CG;
+    float acc[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.f;
+    const float4 *col = reinterpret_cast<const float4 *>(P.qjl_proj) + c;
+    for (int j0 = r * JR; j0 < (r + 1) * JR; j0 += JC) {
+      float4 sv[JC];
+#pragma unroll
+      for (int u = 0; u < JC; ++u) sv[u] = col[(size_t)(j0 + u) * CG];
+#pragma unroll
+      for (int u = 0; u < JC; ++u) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float qv = qs[h][j0 + u];
+          acc[h][0] = fmaf(sv[u].x, qv, acc[h][0]);
+          acc[h][1] = fmaf(sv[u].y, qv, acc[h][1]);
+          acc[h][2] = fmaf(sv[u].z, qv, acc[h][2]);
+          acc[h][3] = fmaf(sv[u].w, qv, acc[h][3]);
+        }
+      }
+    }
+    const int lane0 = tid & 63, wave0 = tid >> 6;
+#pragma unroll
+    for (int m = CG; m < 64; m <<= 1) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[h][e] += __shfl_xor(acc[h][e], m);
+      }
+    }
+    if (lane0 < CG) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        *reinterpret_cast<float4 *>(&red_acc[wave0][h][4 * c]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+    }
+    __syncthreads();
+    for (int o = tid; o < G * D; o += kBlock) {
+      const int h = o / D, i = o - (o / D) * D;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += red_acc[w][h][i];
+      ps[h][i] = v * prescale;
+    }
+    __syncthreads();
+  }
+
+  const int ds = (tid & 63) % LPTF;
+  float qr[G][DPLF];
+  lane_query<D, G, DPLF>(qs, prescale, qr);
+  if constexpr (QJL) {
+    float pq[G][DPLF], psum[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPLF; ++e) {
+        const float v = ps[h][ds * DPLF + e];
+        pq[h][e] = 2.f * v;
+        sum += v;
+      }
+      psum[h] = sum;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      tier.psum[h] = psum[h];
+#pragma unroll
+      for (int e = 0; e < DPLF; ++e) tier.pq[h][e] = pq[h][e];
+    }
+  }
+  if constexpr (OUT) {
+    // the query at the outlier channels (original domain), scaled to log2 units of s
+    // the lane's channels k = ds + LPT u (< 8); others get q = 0
+    const float sc = kLog2e / sqrtf((float)D);
+    const int32_t *oi = P.out_idx + (size_t)bh * kOutlierCount;
+    constexpr int kOPL = Far::kOPL;
+#pragma unroll
+    for (int u = 0; u < kOPL; ++u) {
+      const int k = ds + LPTF * u;
+      const bool has = k < kOutlierCount;
+      const int c = has ? oi[k] : 0;
+      const uint32_t sel = has ? (uint32_t)(8 * k) : 0u;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const size_t qrow = ((size_t)b * P.q_heads + hkv * G + h) * D;
+        const float v = P.q_f16 ? half_to_float(static_cast<const uint16_t *>(P.q)[qrow + c])
+                                : static_cast<const float *>(P.q)[qrow + c];
+        tier.qo[h][u] = has ? v * sc : 0.f;
+      }
+      tier.osel[u] = sel;
+    }
+  }
+
+  State<G, DPLF> st;
+  st.init();
+  if constexpr (GATED) {
+    constexpr float kGate2 = 16.f * kLog2e;     // e^-16 in log2 units
+    FarGate<G> fg;
+    const size_t row0 = (size_t)b * P.q_heads + (size_t)hkv * G;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      fg.gate[h] = P.gate_ref ? P.gate_ref[row0 + h] * kLog2e - kGate2 : -INFINITY;
+      fg.spike[h] = P.spike_ref ? P.spike_ref[row0 + h] * kLog2e : INFINITY;
+    }
+    fg.bits = P.spike_ref ? P.spike_bits + row0 * P.spike_words : nullptr;
+    fg.words = P.spike_words;
+    token_loop_gated<G, DPLF, LPTF>(tier, qr, st, t0, t1, fg);
+  } else {
+    token_loop<G, DPLF, LPTF>(tier, qr, st, t0, t1);
+  }
+  write_split<D, G, DPLF>(P, st, b, hkv, split, red_ml, red_acc);
 }
 
 template <int D, int KB, int VB, int G>
