@@ -117,8 +117,8 @@ WORKLOADS = {
                                head_dim=256, seq_len=4096, k_bits=4, v_bits=4, dtype="f16",
                                splits=4, outlier_channels=8, outlier_scale=10.0),
     "two_tier": Workload("two_tier", 5, batch=16, q_heads=16, kv_heads=16, head_dim=128,
-                         seq_len=16384, k_bits=8, v_bits=4, dtype="f16", splits=16,
-                         near_fraction=0.1, near_splits=3),
+                         seq_len=16384, k_bits=8, v_bits=4, dtype="f16", splits=18,
+                         near_fraction=0.1, near_splits=5),
     # the llama7b_layer cache with its 256 most recent tokens kept in fp16 (a
     # decode buffer scored in the same pass through the near-tier path)
     "decode_buffer": Workload("decode_buffer", 6, batch=8, q_heads=32, kv_heads=8,
