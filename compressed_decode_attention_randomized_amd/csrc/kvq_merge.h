@@ -122,17 +122,67 @@ __device__ inline void merge_row(const float *__restrict__ po, const float *__re
     return;
   }
 
-  // More splits: the maximum first, then groups of 64 / E rows (64 registers
-  // of partial rows), each group's rows and states requested together.
+  // More splits: groups of 64 / E rows (64 registers of partial rows).
   constexpr int kG = 64 / E;
+  float near_acc[E], far_acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) near_acc[e] = far_acc[e] = 0.f;
+  if (S <= 64) {
+    // Up to 64 splits: lane s holds split s's state, requested with the
+    // first group's rows, so up to kG splits take one round trip.
+    float m = -INFINITY, l = 0.f;
+    if (lane < S) {
+      m = ml[2 * lane];
+      l = ml[2 * lane + 1];
+    }
+    float v[kG][E];
+#pragma unroll
+    for (int u = 0; u < kG; ++u) {
+      if (u < S) {
+        merge_load_row<E>(po + (size_t)u * D, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[u][e] = 0.f;
+      }
+    }
+    const float M = wave_max(m, lane);
+    const float w = (m == -INFINITY || l == 0.f) ? 0.f : l * expf(m - M);
+    const float W = wave_sum(w, lane);
+    for (int g0 = 0; g0 < S; g0 += kG) {
+      if (g0 > 0) {
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+          if (g0 + u < S) {
+            merge_load_row<E>(po + (size_t)(g0 + u) * D, v[u]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[u][e] = 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const int sp = g0 + u;
+        const float wk = (sp < S) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), sp & 63)) : 0.f;
+        const bool near = sp < near_splits;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (near) near_acc[e] = fmaf(wk, v[u][e], near_acc[e]);
+          else far_acc[e] = fmaf(wk, v[u][e], far_acc[e]);
+        }
+      }
+    }
+    merge_finish<D>(near_acc, far_acc, W, M, sg, out_row, lse, lane);
+    return;
+  }
+
+  // More than 64 splits: the maximum first, then each group's rows and
+  // states requested together.
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
   M = wave_max(M, lane);
 
   float W = 0.f;
-  float near_acc[E], far_acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) near_acc[e] = far_acc[e] = 0.f;
   for (int g0 = 0; g0 < S; g0 += kG) {
     float v[kG][E];
 #pragma unroll
