@@ -1,7 +1,8 @@
-// Split-K GQA decode attention on 4-bit or 2-bit Lloyd-Max keys and values,
+// Split-K GQA decode attention on 4-, 3- or 2-bit Lloyd-Max keys and values,
 // head dimension 256: the pair-table matrix-core tile of the head-dimension-
-// 128 kernel (shared tile code; quad-table entries for 2-bit codes), with
-// twice the registers per tile.
+// 128 kernel (shared tile code; quad-table entries for 2-bit codes, tables
+// indexed by 6-bit fields of two codes for 3-bit ones), with twice the
+// registers per tile.
 //
 // Work mapping: a work-group of 8 waves (two per SIMD: the query operand and
 // the value accumulator take 128 registers at this head size) fills a
@@ -55,14 +56,18 @@ struct WParams {
   float *part_o, *part_ml;
 };
 
-// Pair tables (4-bit) or quad tables (2-bit) of the key codebook in the
-// first 64 KB of `tab` and, when the value codebook differs, of the value
-// codebook in the next 64 KB; run by the four set-up waves.  Thread t < 256
-// writes the 16-byte chunks t + 256k, k = 0..15: row (code byte)
-// t/16 + 16k, so the low four bits of the row, t/16 = 4 wave + lane/16, are
-// the same for every k and the high four bits are k.
+// Pair tables (4-bit, 3-bit) or quad tables (2-bit) of the key codebook in
+// the first 64 KB of `tab` and, when the value codebook differs, of the
+// value codebook in the next 64 KB; run by the four set-up waves.  Thread
+// t < 256 writes the 16-byte chunks t + 256k, k = 0..15 (0..3 for the 64
+// rows of a 3-bit table): row (code byte or field) t/16 + 16k, so the low
+// four bits of the row, t/16 = 4 wave + lane/16, are the same for every k
+// and the high bits are k.
 //   4-bit: a row holds 32 slots of (e(c[r % 16]), e(c[r / 16])), a chunk two
 //          slots;
+//   3-bit: a row holds 32 slots of (e(c[r & 7]), e(c[r >> 3])), a chunk two
+//          slots; r & 7 is lane/16 + 4 (wave & 1) and r >> 3 is
+//          wave/2 + 2k;
 //   2-bit: a row holds 16 slots of (e(c[r & 3]), e(c[(r >> 2) & 3]),
 //          e(c[(r >> 4) & 3]), e(c[r >> 6])), a chunk one slot.
 // Centroids come through uniform addresses (scalar loads); per-wave parts are
@@ -91,6 +96,9 @@ __device__ inline void fill_tables(uint8_t *tab, const float *kcen, const float 
       case 2: pick<8, 1>(ck, cv, lk, lv); break;
       default: pick<12, 1>(ck, cv, lk, lv); break;
     }
+  } else if constexpr (BITS == 3) {
+    if (wave & 1) pick<4, 1>(ck, cv, lk, lv);
+    else pick<0, 1>(ck, cv, lk, lv);
   } else {
     pick<0, 1>(ck, cv, lk, lv);
   }
@@ -101,7 +109,21 @@ __device__ inline void fill_tables(uint8_t *tab, const float *kcen, const float 
     lo_v = (r4 == u) ? lv[u] : lo_v;
   }
   const uint32_t lok = split_entry(lo_k * kCodeScale), lov = split_entry(lo_v * kCodeScale);
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 3) {
+    const bool upper = wave >> 1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t hi = split_entry((upper ? ck[2 * k + 1] : ck[2 * k]) * kCodeScale);
+      *reinterpret_cast<uint4_t *>(tab + (tid + 256 * k) * 16) = (uint4_t){lok, hi, lok, hi};
+    }
+    if (!same) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t hi = split_entry((upper ? cv[2 * k + 1] : cv[2 * k]) * kCodeScale);
+        *reinterpret_cast<uint4_t *>(tab + 65536 + (tid + 256 * k) * 16) = (uint4_t){lov, hi, lov, hi};
+      }
+    }
+  } else if constexpr (BITS == 4) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const uint32_t hi = split_entry(ck[k] * kCodeScale);
@@ -286,7 +308,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
   for (int kb = 0; kb < D / 16; ++kb) bk[kb] = *reinterpret_cast<const uint4_t *>(&qtab[qrow][g * 64 + 4 * kb]);
   const float sfac = col ? qfac[grp * G + (n >> 1)] : 0.f;
   // table slot: lane % 32 of 8-byte pair entries, lane % 16 of 16-byte quad entries
-  const uint32_t kslot = (BITS == 4) ? (uint32_t)(lane & 31) * 8 : (uint32_t)(lane & 15) * 16;
+  const uint32_t kslot = (BITS != 2) ? (uint32_t)(lane & 31) * 8 : (uint32_t)(lane & 15) * 16;
   const uint32_t vslot = kslot | v_table[0];
   float m1 = -1.f;
   asm volatile("" : "+s"(m1));                       // no instruction: keeps -1 from being folded
@@ -413,8 +435,12 @@ bool wide_attend_supported(const AttendArgs &a) {
   const int G = a.q_heads / a.kv_heads;
   const bool fits = (int64_t)a.capacity * a.head_dim * a.k_format / 8 < (1ll << 31) &&
                     (int64_t)a.batch * a.kv_heads * a.num_splits < (1ll << 30);
-  return a.head_dim == D && (a.k_format == 4 || a.k_format == 2) && a.v_format == a.k_format &&
-         a.num_near_splits == 0 && G >= 1 && G <= kGMax && fits;
+  // 3-bit codes at G = 1 stay on the VALU kernel, which is faster there: the
+  // tile's 16 matrix-core columns then carry one head, and 3-bit fields cost
+  // two address operations per table read against one for 4-bit bytes
+  const bool width = a.k_format == 4 || a.k_format == 2 || (a.k_format == 3 && G >= 2);
+  return a.head_dim == D && width && a.v_format == a.k_format && a.num_near_splits == 0 && G >= 1 && G <= kGMax &&
+         fits;
 }
 
 hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream, int part_base) {
@@ -430,6 +456,7 @@ hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream, int part_
             a.v_centroids, a.part_o + (size_t)part_base * D, a.part_ml + (size_t)part_base * 2};
   dim3 grid((unsigned)((units + (1 << lg) - 1) >> lg));
   if (a.k_format == 4) hipLaunchKernelGGL(attend_wide_kernel<4>, grid, dim3(kBlock), 0, stream, P);
+  else if (a.k_format == 3) hipLaunchKernelGGL(attend_wide_kernel<3>, grid, dim3(kBlock), 0, stream, P);
   else hipLaunchKernelGGL(attend_wide_kernel<2>, grid, dim3(kBlock), 0, stream, P);
   return hipGetLastError();
 }

@@ -139,12 +139,16 @@ __device__ inline void split_pair(float w0, float w1, float m1, uint32_t &hp, ui
 }
 
 // Registers of one tile for head dimension D (128 or 256) and BITS-bit
-// codes (4, or 2 with quad entries: see quad_addr).
+// codes (4; 2 with quad entries, see quad_read; 3 at D = 256 with 6-bit
+// pair fields, see field_addr).
 template <int D, int BITS = 4>
 struct Tile {
+  static_assert(BITS != 3 || D == 256, "3-bit tiles are laid out for head dimension 256");
   static constexpr int kRow = D * BITS / 8;       // packed bytes per vector
   static constexpr int kKeyWords = kRow / 16;     // key slice: token n, bytes [kRow/4 g, kRow/4 (g+1))
-  static constexpr int kValWords = kRow / 64;     // value words per token: bytes [kRow/16 n, kRow/16 (n+1))
+  // value words per token: bytes [kRow/16 n, kRow/16 (n+1)); for 3-bit codes
+  // (6 bytes at 6n) the 8 bytes from the word boundary at or below 6n
+  static constexpr int kValWords = (BITS == 3) ? 2 : kRow / 64;
   uint32_t kw[kKeyWords];
   uint32_t vw[4][kValWords];                      // tokens 4g+i
   uint2_t kn, vn;                                 // fp16 norms of tokens 4g..4g+3
@@ -167,7 +171,7 @@ template <int D, int BITS = 4>
 __device__ inline void set_offsets(Sources &src, int g, int n) {
   constexpr int kRow = Tile<D, BITS>::kRow;
   src.ko = n * kRow + g * (kRow / 4);
-  src.vo = 4 * g * kRow + n * (kRow / 16);
+  src.vo = 4 * g * kRow + ((BITS == 3) ? (n * (kRow / 16)) & ~3 : n * (kRow / 16));
   src.no = 4 * g * 2;
 }
 
@@ -182,11 +186,21 @@ __device__ inline void load_tile(Tile<D, BITS> &t, const Sources &src, int tb, b
   const __amdgpu_buffer_rsrc_t kn = make_rsrc(src.kn, skip ? 0u : src.norm_bytes);
   const __amdgpu_buffer_rsrc_t vn = make_rsrc(src.vn, skip ? 0u : src.norm_bytes);
   const int cs = tb * T::kRow, ns = tb * 2;
+  if constexpr (BITS == 3) {
+    // a 24-byte key slice starts at a multiple of 8 bytes, not always of 16
 #pragma unroll
-  for (int i = 0; i < T::kKeyWords / 4; ++i) {
-    const uint4_t k = __builtin_amdgcn_raw_buffer_load_b128(kc, src.ko + 16 * i, cs, kStream);
+    for (int i = 0; i < T::kKeyWords / 2; ++i) {
+      const uint2_t k = __builtin_amdgcn_raw_buffer_load_b64(kc, src.ko + 8 * i, cs, kStream);
+      t.kw[2 * i] = k.x;
+      t.kw[2 * i + 1] = k.y;
+    }
+  } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) t.kw[4 * i + e] = k[e];
+    for (int i = 0; i < T::kKeyWords / 4; ++i) {
+      const uint4_t k = __builtin_amdgcn_raw_buffer_load_b128(kc, src.ko + 16 * i, cs, kStream);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t.kw[4 * i + e] = k[e];
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -204,7 +218,7 @@ __device__ inline void load_tile(Tile<D, BITS> &t, const Sources &src, int tb, b
 
 // Buffer loads one tile issues (the s_waitcnt vmcnt that leaves one tile in flight).
 template <int D, int BITS = 4>
-constexpr int kTileLoads = Tile<D, BITS>::kKeyWords / 4 + 4 + 2;
+constexpr int kTileLoads = Tile<D, BITS>::kKeyWords / (BITS == 3 ? 2 : 4) + 4 + 2;
 
 // 2-bit codes: a byte holds four codes, and the quad table maps it to
 // (e(c[b & 3]), e(c[(b >> 2) & 3]), e(c[(b >> 4) & 3]), e(c[b >> 6])), 16
@@ -216,8 +230,25 @@ __device__ inline uint4_t quad_read(const uint8_t *tab, uint32_t addr) {
   return *reinterpret_cast<const uint4_t *>(tab + addr);
 }
 
+// 3-bit codes: two neighbouring codes form a 6-bit field (the first code in
+// its low three bits), and the pair table maps a field f to (e(c[f & 7]),
+// e(c[f >> 3])), 8 bytes, replicated over 32 lane slots like the 4-bit
+// table (address = f*256 + slot*8).  The field at bit P of a lane's packed
+// words, as that address: a bit-field extract and a shift-or, or for a field
+// across a word boundary a funnel shift and an and-or.
+template <int P, int N>
+__device__ inline uint32_t field_addr(const uint32_t (&w)[N], uint32_t slot) {
+  constexpr int W = P / 32, O = P % 32;
+  if constexpr (O + 6 <= 32) {
+    return (__builtin_amdgcn_ubfe(w[W], (uint32_t)O, 6u) << 8) | slot;
+  } else {
+    static_assert(W + 1 < N, "field past the lane's words");
+    return (__builtin_amdgcn_alignbit(w[W + 1], w[W], (uint32_t)(O - 8)) & 0x3F00u) | slot;
+  }
+}
+
 // Key block kb: coordinates 4kb..4kb+3 of the lane's slice = bytes 2kb, 2kb+1
-// (4-bit) or byte kb (2-bit).
+// (4-bit), byte kb (2-bit) or the fields at bits 12kb and 12kb+6 (3-bit).
 template <int D, int BITS, int KB = 0>
 __device__ inline void key_scores(const uint32_t (&kw)[Tile<D, BITS>::kKeyWords], const uint4_t (&bk)[D / 16],
                                   const uint8_t *tab, uint32_t slot, float4_t &dk) {   // slot: key slot register
@@ -228,6 +259,8 @@ __device__ inline void key_scores(const uint32_t (&kw)[Tile<D, BITS>::kKeyWords]
       const uint2_t e0 = table_read(tab, pair_addr<2 * (KB % 2)>(w, slot));
       const uint2_t e1 = table_read(tab, pair_addr<2 * (KB % 2) + 1>(w, slot));
       a = as_half8(e0, e1);
+    } else if constexpr (BITS == 3) {
+      a = as_half8(table_read(tab, field_addr<12 * KB>(kw, slot)), table_read(tab, field_addr<12 * KB + 6>(kw, slot)));
     } else {
       a = __builtin_bit_cast(half8_t, quad_read(tab, pair_addr<KB % 4>(kw[KB / 4], slot)));
     }
@@ -244,16 +277,39 @@ __device__ inline void key_scores(const uint32_t (&kw)[Tile<D, BITS>::kKeyWords]
 //   2-bit: byte j of x[r] holds coordinate 4j + r of tokens 4g..4g+3 (2 bits
 //          each, token 4g lowest); one quad-table read gives the operand of
 //          tile 4j + r.
+//   3-bit: the 6-bit field j of ev[c][p] (od[c][p]) holds coordinate
+//          8c + 2j (8c + 2j + 1) of tokens 4g+2p (low three bits) and
+//          4g+2p+1; two pair-table reads give the operand of tile 8c + 2j
+//          (+1).
 template <int D, int BITS>
 struct ValueBytes {
-  static constexpr int kWords = (BITS == 4) ? D / 128 : 1;
+  static constexpr int kWords = (BITS == 4) ? D / 128 : (BITS == 3) ? 2 : 1;
   uint32_t ev[kWords][2], od[kWords][2];
   uint32_t x[4];
 };
 
 template <int D, int BITS>
-__device__ inline void value_bytes(const Tile<D, BITS> &t, ValueBytes<D, BITS> &vb) {
-  if constexpr (BITS == 4) {
+__device__ inline void value_bytes(const Tile<D, BITS> &t, ValueBytes<D, BITS> &vb, int n) {
+  if constexpr (BITS == 3) {
+    // lane n's 16 codes of a token start at bit 16 (n & 1) of its two words;
+    // c0: codes 0..7 (coordinates 16n..16n+7), c1: codes 8..15, each in the
+    // low 24 bits (bits above are ignored)
+    const uint32_t sh = (uint32_t)(n & 1) * 16u;
+    uint32_t c0[4], c1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c0[i] = __builtin_amdgcn_alignbit(t.vw[i][1], t.vw[i][0], sh);
+      c1[i] = __builtin_amdgcn_alignbit(t.vw[i][1] >> sh, c0[i], 24u);
+    }
+    constexpr uint32_t kLow3 = 0x001C71C7u;         // bits 6j..6j+2, j = 0..3
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      vb.ev[0][p] = (c0[2 * p] & kLow3) | ((c0[2 * p + 1] << 3) & ~kLow3);
+      vb.od[0][p] = ((c0[2 * p] >> 3) & kLow3) | (c0[2 * p + 1] & ~kLow3);
+      vb.ev[1][p] = (c1[2 * p] & kLow3) | ((c1[2 * p + 1] << 3) & ~kLow3);
+      vb.od[1][p] = ((c1[2 * p] >> 3) & kLow3) | (c1[2 * p + 1] & ~kLow3);
+    }
+  } else if constexpr (BITS == 4) {
 #pragma unroll
     for (int w = 0; w < D / 128; ++w) {
 #pragma unroll
@@ -290,6 +346,15 @@ __device__ inline void value_update(const ValueBytes<D, BITS> &vb, const uint8_t
       const uint2_t b0 = table_read(tab, pair_addr<B>(vb.od[W][0], slot));
       const uint2_t b1 = table_read(tab, pair_addr<B>(vb.od[W][1], slot));
       dv[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(b0, b1), dv[2 * M + 1], 0, 0, 0);
+      value_update<D, BITS, M + 1>(vb, tab, slot, aw, dv);
+    }
+  } else if constexpr (BITS == 3) {
+    if constexpr (M < D / 16) {
+      constexpr int C = M / 8, J = (M % 8) / 2;      // tile M = 8C + 2J (+1 for the odd words)
+      const uint32_t(&w)[2] = (M & 1) ? vb.od[C] : vb.ev[C];
+      const uint2_t a0 = table_read(tab, (__builtin_amdgcn_ubfe(w[0], 6u * J, 6u) << 8) | slot);
+      const uint2_t a1 = table_read(tab, (__builtin_amdgcn_ubfe(w[1], 6u * J, 6u) << 8) | slot);
+      dv[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(a0, a1), dv[M], 0, 0, 0);
       value_update<D, BITS, M + 1>(vb, tab, slot, aw, dv);
     }
   } else {
@@ -351,7 +416,7 @@ __device__ inline void process_tile(const Tile<D, BITS> &t, const uint4_t (&bk)[
   }
 
   ValueBytes<D, BITS> vb;
-  value_bytes<D, BITS>(t, vb);
+  value_bytes<D, BITS>(t, vb, n);
 
   // weights w = exp2(s - m) * norm of the lane's two tokens, split as
   // w = hi + lo (fp16 each, about 22 bits together) into the packed pairs

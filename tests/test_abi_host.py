@@ -162,8 +162,11 @@ def test_attention_kernel_choice():
     assert name(head_dim=256) == "attend_wide_kernel"                     # 4-bit, d=256, G <= 8
     assert name(head_dim=256, hq=16) == "attend_wide_kernel"             # G=8
     assert name(head_dim=256, k_format=2, v_format=2) == "attend_wide_kernel"
+    assert name(head_dim=256, k_format=3, v_format=3, hq=16) == "attend_wide_kernel"   # 3-bit, d=256, G=8
+    assert name(head_dim=256, k_format=3, v_format=3, hq=2) == "attend_kernel"         # 3-bit at G=1: VALU kernel
+    assert name(head_dim=256, k_format=3, v_format=4) == "attend_kernel"  # mixed widths: VALU kernel
     assert name(k_format=2, v_format=2) == "attend_mfma_kernel"
-    assert name(k_format=3, v_format=3) is None                           # 3-bit values at G=2: not built
+    assert name(k_format=3, v_format=3) is None                           # 3-bit values at d=128, G=2: not built
     assert name(head_dim=64) == "attend_kernel"
     assert name(k_format=8, k_norms=0, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_kernel"
     # 4-bit codes beside an fp16 near tier: near splits on the VALU kernel, far on a pair-table kernel
@@ -174,7 +177,7 @@ def test_attention_kernel_choice():
     assert name(**qjl) == "attend_kernel"                                 # the QJL sketch: VALU kernel only
     assert name(k_format=3, v_format=4, hq=8) == "attend_kernel"          # 3-bit keys beside 4-bit values, G=4
     assert name(k_format=3, v_format=4, hq=16) is None                    # G=8 is not built for the VALU kernel
-    assert name(k_format=3, v_format=3, hq=4) is None                     # 3-bit values: G=1 only
+    assert name(k_format=3, v_format=3, hq=4) is None                     # 3-bit values at d=128: G=1 only
     assert name(k_format=3, v_format=3, hq=2) == "attend_kernel"
     assert name(hq=3) is None and name(head_dim=96) is None
 

@@ -212,7 +212,7 @@ def test_mha_and_gqa2(dev):
 
 
 @pytest.mark.parametrize("d,bits,kernel", [(128, 4, "attend_pair_kernel"), (256, 4, "attend_wide_kernel"),
-                                           (256, 2, "attend_wide_kernel")])
+                                           (256, 3, "attend_wide_kernel"), (256, 2, "attend_wide_kernel")])
 def test_distinct_value_codebook(dev, d, bits, kernel):
     """Keys and values decoded through different codebooks (the value table
     replaced after the append by 1.2 times the Lloyd-Max centroids): the
@@ -241,12 +241,14 @@ def test_distinct_value_codebook(dev, d, bits, kernel):
     _rows_close("distinct value codebook", out.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("hq,bits", [(8, 4), (16, 4), (24, 4), (64, 4), (8, 2), (24, 2), (64, 2)])
+@pytest.mark.parametrize("hq,bits", [(8, 4), (16, 4), (24, 4), (64, 4), (16, 3), (24, 3), (32, 3), (64, 3),
+                                     (8, 2), (24, 2), (64, 2)])
 def test_head_dim_256_unit_groups(dev, hq, bits):
-    """Head dimension 256, 4- and 2-bit, G = 1, 2, 3, 8 query heads per KV head, with
-    512 (b * Hkv, split) units: more than the compute units, so a work-group
-    serves several units (for G <= 4), with ragged and empty splits (200
-    tokens in chunks of 32 over 8 splits) and every head checked."""
+    """Head dimension 256, 4-, 3- and 2-bit, G = 1 (4- and 2-bit), 2, 3, 4 (3-bit), 8
+    query heads per KV head, with 512 (b * Hkv, split) units: more than the
+    compute units, so a work-group serves several units (for G <= 4), with
+    ragged and empty splits (200 tokens in chunks of 32 over 8 splits) and
+    every head checked."""
     wl = W.WORKLOADS["bitwidth_sweep"].scaled(batch=8, q_heads=hq, kv_heads=8, seq_len=200, splits=8).with_bits(bits)
     cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, wl.seq_len, _fmt(bits), _fmt(bits),
                                  seed=W.SIGN_SEED, device=dev)
