@@ -315,7 +315,7 @@ def measure(wl: W.Workload, args, dev, steps: int, reps: int, want_inputs: bool 
     step_bytes = att_bytes + by["append_token"]
     att = _stats_us(att_ms)
     st = _stats_us(step_ms)
-    kernel = "attend_kernel" if args.gate else caches[0].attention_kernel(wl.q_heads, near_splits)
+    kernel = "attend_kernel" if args.gate else caches[0].attention_kernel(wl.q_heads, S, near_splits)
     achieved = att_bytes / (att["avg_us"] / 1e6) / 1e9
     traffic = read_traffic(wl.name, kernel_source_sha(kernel))
     res = {

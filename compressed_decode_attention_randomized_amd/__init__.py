@@ -71,7 +71,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvq_decode_attention": (I32, [CP, P, I32, I32, I32, I32, I32, P, P, P]),
         "kvq_decode_attention_gated": (I32, [CP, P, I32, I32, I32, I32, I32, P, P, P, P, P, P]),
         "kvq_calibrate_outliers": (I32, [CP, P, I32, I32, P, P]),
-        "kvq_decode_attention_kernel": (ctypes.c_char_p, [CP, I32, I32]),
+        "kvq_decode_attention_kernel": (ctypes.c_char_p, [CP, I32, I32, I32]),
         "kvq_merge": (I32, [CP, P, P, I32, I32, I32, P, P, P]),
         "kvq_partials_floats": (SZ, [I32, I32, I32, I32]),
         "kvq_decode": (I32, [CP, P, I32, I32, I32, I32, I32, P, SZ, P, P, P]),
@@ -319,10 +319,10 @@ class KVCache:
                                 _stream_handle(part_o.device)), "kvq_merge")
         return out
 
-    def attention_kernel(self, q_heads: int, num_near_splits: int = 0) -> str:
+    def attention_kernel(self, q_heads: int, num_splits: int, num_near_splits: int = 0) -> str:
         """Name of the kernel kvq_decode_attention launches for this cache."""
         cs = self.struct()
-        name = load().kvq_decode_attention_kernel(ctypes.byref(cs), q_heads, num_near_splits)
+        name = load().kvq_decode_attention_kernel(ctypes.byref(cs), q_heads, num_splits, num_near_splits)
         if not name:
             raise KVQError(KVQ_EINVAL, "kvq_decode_attention_kernel", load().kvq_last_error().decode())
         return name.decode()

@@ -204,11 +204,16 @@ kvq_status kvq_calibrate_outliers(const kvq_cache *cache, const void *keys, int3
                                           n_tokens, idx_out, stream), fn);
 }
 
-const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads, int32_t num_near_splits) {
+const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads, int32_t num_splits,
+                                        int32_t num_near_splits) {
   kvq::clear_error();
   if (check_cache(cache, "kvq_decode_attention_kernel") != KVQ_OK) return nullptr;
   if (q_heads < 1 || q_heads % cache->kv_heads) return nullptr;
-  kvq::AttendArgs a{nullptr, 0, cache->batch, cache->kv_heads, q_heads, cache->head_dim, cache->capacity, 0, 1,
+  if (num_splits < 1 || num_near_splits < 0) {
+    kvq::fail(KVQ_EINVAL, "kvq_decode_attention_kernel: num_splits %d, num_near_splits %d", num_splits, num_near_splits);
+    return nullptr;
+  }
+  kvq::AttendArgs a{nullptr, 0, cache->batch, cache->kv_heads, q_heads, cache->head_dim, cache->capacity, 0, num_splits,
                     num_near_splits, cache->near_len, cache->k_format, cache->v_format,
                     static_cast<const uint8_t *>(cache->k_codes), static_cast<const uint8_t *>(cache->v_codes),
                     cache->k_norms, cache->v_norms, cache->signs, cache->k_centroids, cache->v_centroids,

@@ -1025,6 +1025,7 @@ const char *attend_kernel_name(const AttendArgs &a) {
   const char *valu = valu_attend_supported(a) ? "attend_kernel" : nullptr;
   if (a.outlier_idx || a.qjl_proj) return valu;
   if (a.num_near_splits > 0) {
+    if (pair_near_supported(a)) return "attend_pair_kernel";
     const AttendArgs f = far_part(a);
     if (pair_attend_supported(f)) return valu ? "attend_pair_kernel+attend_kernel" : nullptr;
     if (wide_attend_supported(f)) return valu ? "attend_wide_kernel+attend_kernel" : nullptr;
@@ -1044,11 +1045,16 @@ hipError_t launch_attend_gated(const AttendArgs &a, hipStream_t stream, bool *su
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported) {
   // Key side streams (outliers, QJL sketch) are scored by the VALU kernel only.
   if (a.outlier_idx || a.qjl_proj) return launch_valu(a, stream, supported);
-  // A near tier (fp16 rows, original domain) beside 4-bit or 2-bit far codes
+  // A near tier (fp16 rows, original domain) beside 4-bit codes at d = 128:
+  // both tiers in one launch of the pair-table kernel.  Beside other codes
   // that a pair-table kernel covers: the near splits run on the VALU kernel
   // and the far splits on the pair-table kernel, two launches on the stream
   // writing disjoint partial rows.
   if (a.num_near_splits > 0) {
+    if (pair_near_supported(a)) {
+      *supported = true;
+      return launch_attend_pair(a, stream);
+    }
     const AttendArgs f = far_part(a);
     const bool pair = pair_attend_supported(f), wide = !pair && wide_attend_supported(f);
     if (pair || wide) {

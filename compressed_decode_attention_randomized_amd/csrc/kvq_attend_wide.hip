@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
   }
   // the last split's partial tile [t1f, t1)
   if (gwave == 0 && t1f < t1) {
-    load_tile<D, BITS>(ta, src, t1f, false);
+    load_tail_tile<D, BITS>(ta, src, t1f);
     process_tile<D, BITS, true>(ta, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
   }
 

@@ -86,10 +86,15 @@ const char *attend_kernel_name(const AttendArgs &a);
 // Matrix-core variant (Lloyd-Max 2/4-bit keys and values, no near tier, G <= 8).
 bool mfma_attend_supported(const AttendArgs &a);
 hipError_t launch_attend_mfma(const AttendArgs &a, hipStream_t stream, bool *supported);
-// Pair-table variant (4-bit keys and values, head_dim 128, no near tier, G <= 8).
+// Pair-table variant (4-bit keys and values, head_dim 128, G <= 8).
+// pair_attend_supported: no near tier.  pair_near_supported: with an fp16
+// near tier in the same launch (at most as many near splits as far splits,
+// one work-group per far split).  For a launch without near splits,
 // part_base: far split 0 goes to partial row index part_base of rows that
-// hold part_base + num_splits splits (the near-tier splits come first).
+// hold part_base + num_splits splits (the near-tier splits come first); with
+// near splits the rows are laid out that way with part_base = near splits.
 bool pair_attend_supported(const AttendArgs &a);
+bool pair_near_supported(const AttendArgs &a);
 hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream, int part_base = 0);
 // Pair-table variant for head_dim 256 (2- or 4-bit keys and values, no near tier, G <= 8).
 bool wide_attend_supported(const AttendArgs &a);

@@ -216,6 +216,24 @@ __device__ inline void load_tile(Tile<D, BITS> &t, const Sources &src, int tb, b
   t.vn = __builtin_amdgcn_raw_buffer_load_b64(vn, src.no, ns, kStream);
 }
 
+// Loads of the partial last tile at token tb through descriptors that start
+// at the tile and end at the slice's end: its rows past the slice read as
+// zero from the descriptor's range check on the lane offset alone (the
+// full-tile loads above keep the tile offset in a scalar register; their
+// rows always lie inside the slice).
+template <int D, int BITS = 4>
+__device__ inline void load_tail_tile(Tile<D, BITS> &t, const Sources &src, int tb) {
+  constexpr int kRow = Tile<D, BITS>::kRow;
+  Sources s = src;
+  s.kc += (size_t)tb * kRow;
+  s.vc += (size_t)tb * kRow;
+  s.kn += tb;
+  s.vn += tb;
+  s.code_bytes -= (uint32_t)tb * kRow;
+  s.norm_bytes -= (uint32_t)tb * 2;
+  load_tile<D, BITS>(t, s, 0, false);
+}
+
 // Buffer loads one tile issues (the s_waitcnt vmcnt that leaves one tile in flight).
 template <int D, int BITS = 4>
 constexpr int kTileLoads = Tile<D, BITS>::kKeyWords / (BITS == 3 ? 2 : 4) + 4 + 2;
@@ -367,26 +385,32 @@ __device__ inline void value_update(const ValueBytes<D, BITS> &vb, const uint8_t
   }
 }
 
-// One 16-token tile of the online softmax.  TAIL masks tokens at or past t1.
+// The online-softmax step of one 16-token tile, shared by the code tiles
+// and the fp16 near-tier tiles of the head-dimension-128 kernel.  TAIL masks
+// tokens at or past t1.
 //
-// Columns 2h and 2h+1 of the score tile hold the two parts of head h's
+// Columns 2h and 2h+1 of the score tile dk hold the two parts of head h's
 // scores, so lanes 2h and 2h+1 of a lane row share the work of their four
 // tokens: lane 2h finishes tokens 4g, 4g+1 and lane 2h+1 tokens 4g+2, 4g+3
 // (one exponential per score), then they trade weight halves: A row 2h takes
 // the high fp16 parts of all four weights, row 2h+1 the low parts.  Both
 // lanes of a head keep the same softmax reference.
-template <int D, int BITS, bool TAIL>
-__device__ inline void process_tile(const Tile<D, BITS> &t, const uint4_t (&bk)[D / 16], const uint8_t *tab,
-                                    uint32_t kslot, uint32_t vslot, float sfac, float m1, int tb, int t1, int g, int n,
-                                    float4_t (&dv)[D / 16], float &m_run, float &l_run, float &m_top) {
-  float4_t dk = {0.f, 0.f, 0.f, 0.f};
-  key_scores<D, BITS>(t.kw, bk, tab, kslot, dk);
-
+//
+// tile_scores: the lane's two scores, scaled by sfac times the tokens' fp16
+// key norms (knp, NORMS) or by sfac alone, with the state moved (and the
+// accumulator rescaled) when a score passes the reference.
+template <int D, bool TAIL, bool NORMS>
+__device__ inline void tile_scores(const float4_t &dk, uint32_t knp, float sfac, int tb, int t1, int g, int n,
+                                   float4_t (&dv)[D / 16], float &m_run, float &l_run, float &m_top, float (&s)[2]) {
   const bool odd = n & 1;
-  const uint32_t knp = odd ? t.kn.y : t.kn.x;        // fp16 norms of this lane's two tokens
-  const uint32_t vnp = odd ? t.vn.y : t.vn.x;
   const float f0 = add_swap1(dk[0]), f1 = add_swap1(dk[1]), f2 = add_swap1(dk[2]), f3 = add_swap1(dk[3]);
-  float s[2] = {(odd ? f2 : f0) * half_mul<0>(knp, sfac), (odd ? f3 : f1) * half_mul<1>(knp, sfac)};
+  if constexpr (NORMS) {
+    s[0] = (odd ? f2 : f0) * half_mul<0>(knp, sfac);
+    s[1] = (odd ? f3 : f1) * half_mul<1>(knp, sfac);
+  } else {
+    s[0] = (odd ? f2 : f0) * sfac;
+    s[1] = (odd ? f3 : f1) * sfac;
+  }
   if constexpr (TAIL) {
     const int tok = tb + 4 * g + 2 * (int)odd;
     s[0] = (tok < t1) ? s[0] : -INFINITY;
@@ -414,20 +438,23 @@ __device__ inline void process_tile(const Tile<D, BITS> &t, const uint4_t (&bk)[
       dv[dt][3] *= a1;
     }
   }
+}
 
-  ValueBytes<D, BITS> vb;
-  value_bytes<D, BITS>(t, vb, n);
-
-  // weights w = exp2(s - m) * norm of the lane's two tokens, split as
-  // w = hi + lo (fp16 each, about 22 bits together) into the packed pairs
-  // hp = (hi0, hi1) and lp = (lo0, lo1)
+// tile_weights: w = exp2(s - m) times the tokens' fp16 value norms (vnp,
+// NORMS) or alone, split as w = hi + lo (fp16 each, about 22 bits together)
+// and traded between the lanes of a head into the A operand of the value
+// products.
+template <bool TAIL, bool NORMS>
+__device__ inline half8_t tile_weights(const float (&s)[2], uint32_t vnp, float m1, int n, float m_run, float &l_run) {
+  const bool odd = n & 1;
   float w[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     float p = __builtin_amdgcn_exp2f(s[u] - m_run);
     if constexpr (TAIL) p = (s[u] == -INFINITY) ? 0.f : p;
     l_run += p;
-    w[u] = u ? half_mul<1>(vnp, p) : half_mul<0>(vnp, p);
+    if constexpr (NORMS) w[u] = u ? half_mul<1>(vnp, p) : half_mul<0>(vnp, p);
+    else w[u] = p;
   }
   uint32_t hp, lp;
   split_pair(w[0], w[1], m1, hp, lp);
@@ -437,7 +464,28 @@ __device__ inline void process_tile(const Tile<D, BITS> &t, const uint4_t (&bk)[
   const uint4_t a4 = {__builtin_amdgcn_perm(first, first, 0x01000100u), __builtin_amdgcn_perm(first, first, 0x03020302u),
                       __builtin_amdgcn_perm(second, second, 0x01000100u),
                       __builtin_amdgcn_perm(second, second, 0x03020302u)};
-  value_update<D, BITS>(vb, tab, vslot, __builtin_bit_cast(half8_t, a4), dv);
+  return __builtin_bit_cast(half8_t, a4);
+}
+
+// One 16-token tile of packed codes.
+template <int D, int BITS, bool TAIL>
+__device__ inline void process_tile(const Tile<D, BITS> &t, const uint4_t (&bk)[D / 16], const uint8_t *tab,
+                                    uint32_t kslot, uint32_t vslot, float sfac, float m1, int tb, int t1, int g, int n,
+                                    float4_t (&dv)[D / 16], float &m_run, float &l_run, float &m_top) {
+  float4_t dk = {0.f, 0.f, 0.f, 0.f};
+  key_scores<D, BITS>(t.kw, bk, tab, kslot, dk);
+
+  const bool odd = n & 1;
+  const uint32_t knp = odd ? t.kn.y : t.kn.x;        // fp16 norms of this lane's two tokens
+  const uint32_t vnp = odd ? t.vn.y : t.vn.x;
+  float s[2];
+  tile_scores<D, TAIL, true>(dk, knp, sfac, tb, t1, g, n, dv, m_run, l_run, m_top, s);
+
+  ValueBytes<D, BITS> vb;
+  value_bytes<D, BITS>(t, vb, n);
+
+  const half8_t aw = tile_weights<TAIL, true>(s, vnp, m1, n, m_run, l_run);
+  value_update<D, BITS>(vb, tab, vslot, aw, dv);
 }
 
 }  // namespace pair

@@ -238,13 +238,17 @@ kvq_status kvq_calibrate_outliers(const kvq_cache *cache, const void *keys, int3
                                   int32_t n_tokens, int32_t *idx_out, hipStream_t stream);
 
 /* Name of the attention kernel kvq_decode_attention launches for this cache,
- * query-head count and near-split count (for profiles and reports): a static
- * string, or NULL if the cache description is invalid or the call would
- * return KVQ_EUNSUPPORTED (kvq_last_error then says why).  A cache with a near
- * tier whose far codes a pair-table kernel covers is served by two launches
- * on the stream (near splits, then far splits); the name is then
+ * query-head count and split counts (for profiles and reports): a static
+ * string, or NULL if the arguments are invalid (num_splits < 1 among them)
+ * or the call would return KVQ_EUNSUPPORTED (kvq_last_error then says why).
+ * A near tier beside 4-bit codes at head_dim 128 shares the pair-table
+ * launch when the near splits are at most the far splits and the far splits
+ * fit one work-group per compute unit ("attend_pair_kernel"); a near tier
+ * beside other codes that a pair-table kernel covers is served by two
+ * launches on the stream (near splits, then far splits), named
  * "<far kernel>+attend_kernel". */
-const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads, int32_t num_near_splits);
+const char *kvq_decode_attention_kernel(const kvq_cache *cache, int32_t q_heads, int32_t num_splits,
+                                        int32_t num_near_splits);
 
 /* Split merge and the single inverse rotation ("Making it fast": split-K
  * partial softmax states merged; rotated-domain values mapped back once):

@@ -185,9 +185,10 @@ static void attention_validation() {
   CHECK(kvq_decode_noalloc(&big, q, KVQ_F16, 64, 512, 64, 0, out, lse, nullptr) == KVQ_ERANGE);
 
   // kernel name: valid and invalid descriptions
-  CHECK(kvq_decode_attention_kernel(&c, 8, 0) != nullptr);
-  CHECK(kvq_decode_attention_kernel(&c, 6, 0) == nullptr);
-  CHECK(kvq_decode_attention_kernel(nullptr, 8, 0) == nullptr);
+  CHECK(kvq_decode_attention_kernel(&c, 8, 4, 0) != nullptr);
+  CHECK(kvq_decode_attention_kernel(&c, 6, 4, 0) == nullptr);
+  CHECK(kvq_decode_attention_kernel(&c, 8, 0, 0) == nullptr);
+  CHECK(kvq_decode_attention_kernel(nullptr, 8, 4, 0) == nullptr);
 
   // outlier calibration
   int32_t *idx = fake<int32_t>(0x3000000);

@@ -152,8 +152,8 @@ def test_attention_kernel_choice():
     """The kernel kvq_decode_attention dispatches to (no launch involved)."""
     lib = kvq.load()
 
-    def name(hq=4, SN=0, **over):
-        r = lib.kvq_decode_attention_kernel(ctypes.byref(_fake_cache(**over)), hq, SN)
+    def name(hq=4, SN=0, S=4, **over):
+        r = lib.kvq_decode_attention_kernel(ctypes.byref(_fake_cache(**over)), hq, S, SN)
         return None if r is None else r.decode()
 
     assert name() == "attend_pair_kernel"                                # 4-bit K and V, d=128, G=2
@@ -169,9 +169,17 @@ def test_attention_kernel_choice():
     assert name(k_format=3, v_format=3) is None                           # 3-bit values at d=128, G=2: not built
     assert name(head_dim=64) == "attend_kernel"
     assert name(k_format=8, k_norms=0, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_kernel"
-    # 4-bit codes beside an fp16 near tier: near splits on the VALU kernel, far on a pair-table kernel
-    assert name(near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_pair_kernel+attend_kernel"
+    # 4-bit codes at d=128 beside an fp16 near tier: both tiers in one pair-table launch while the
+    # near splits are at most the far splits and the far splits fit one work-group per compute unit
+    near = dict(near_len=4, near_k=0xC000, near_v=0xD000)
+    assert name(**near, SN=1) == "attend_pair_kernel"
+    assert name(**near, SN=4, S=4) == "attend_pair_kernel"
+    assert name(**near, SN=5, S=4) == "attend_pair_kernel+attend_kernel"     # more near than far splits
+    assert name(**near, SN=1, S=65) == "attend_pair_kernel+attend_kernel"    # 4 pairs x 65 splits > 256 CUs
+    assert name(**near, SN=1, S=64) == "attend_pair_kernel"
+    # near splits on the VALU kernel, far splits on the d=256 pair-table kernel
     assert name(head_dim=256, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_wide_kernel+attend_kernel"
+    assert name(S=0) is None
     assert name(hq=2, k_format=3, v_format=3, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_kernel"
     qjl = dict(qjl_dim=128, qjl_proj=0xC000, qjl_signs=0xD000, qjl_norms=0xE000)
     assert name(**qjl) == "attend_kernel"                                 # the QJL sketch: VALU kernel only

@@ -8,6 +8,7 @@ Bars:
   * attention: max |diff| <= 2e-3 and, per (b, query head), ||diff|| / ||ref||
     <= 1e-3, in fp32 accumulation against the float64 oracle.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -226,7 +227,7 @@ def test_distinct_value_codebook(dev, d, bits, kernel):
     c, _ = O.codebook(wl.v_bits, d)
     cv = (1.2 * c.astype(np.float64)).astype(np.float32)
     cache.v_centroids.copy_(torch.from_numpy(cv).to(dev))
-    assert cache.attention_kernel(wl.q_heads) == kernel
+    assert cache.attention_kernel(wl.q_heads, wl.splits) == kernel
     q = _t(inp.q, dev)
     part_o, part_ml = cache.attend(q, T, wl.splits, 0)
     out = cache.merge(part_o, part_ml, wl.splits, 0)
@@ -252,7 +253,7 @@ def test_head_dim_256_unit_groups(dev, hq, bits):
     wl = W.WORKLOADS["bitwidth_sweep"].scaled(batch=8, q_heads=hq, kv_heads=8, seq_len=200, splits=8).with_bits(bits)
     cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, wl.seq_len, _fmt(bits), _fmt(bits),
                                  seed=W.SIGN_SEED, device=dev)
-    assert cache.attention_kernel(wl.q_heads) == "attend_wide_kernel"
+    assert cache.attention_kernel(wl.q_heads, wl.splits) == "attend_wide_kernel"
     run_case(dev, wl)
 
 
@@ -265,7 +266,7 @@ def test_head_dim_128_two_bit(dev, hq, kv, T, splits):
     wl = W.WORKLOADS["llama7b_layer"].scaled(batch=2, q_heads=hq, kv_heads=kv, seq_len=T, splits=splits).with_bits(2)
     cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, 16, _fmt(2), _fmt(2), seed=W.SIGN_SEED,
                                  device=dev)
-    assert cache.attention_kernel(wl.q_heads) == "attend_mfma_kernel"
+    assert cache.attention_kernel(wl.q_heads, wl.splits) == "attend_mfma_kernel"
     run_case(dev, wl)
 
 
@@ -277,22 +278,48 @@ def test_fp8_keys_without_near_tier(dev, hq):
     run_case(dev, wl)
 
 
-@pytest.mark.parametrize("d,bits,hq,kernel", [(128, 4, 32, "attend_pair_kernel+attend_kernel"),
-                                              (128, 4, 8, "attend_pair_kernel+attend_kernel"),
+@pytest.mark.parametrize("d,bits,hq,kernel", [(128, 4, 32, "attend_pair_kernel"),
+                                              (128, 4, 8, "attend_pair_kernel"),
                                               (256, 4, 8, "attend_wide_kernel+attend_kernel"),
                                               (256, 2, 8, "attend_wide_kernel+attend_kernel"),
                                               (64, 4, 32, "attend_kernel")])
 def test_decode_buffer_shapes(dev, d, bits, hq, kernel):
     """The 10% most recent tokens kept in fp16 beside 4- or 2-bit codes, at
-    three head sizes; with a pair-table kernel for the codes the near and far
-    splits are two launches writing one set of partial rows."""
+    three head sizes: at d = 128 both tiers in one pair-table launch, at
+    d = 256 the near and far splits are two launches writing one set of
+    partial rows."""
     wl = W.WORKLOADS["decode_buffer"].scaled(batch=2, q_heads=hq, head_dim=d, seq_len=613, splits=5,
                                              near_fraction=0.1).with_bits(bits)
     cache = kvq.KVCache.allocate(1, wl.kv_heads, d, 8, _fmt(bits), _fmt(bits), seed=W.SIGN_SEED, device=dev,
                                  near_k=torch.zeros((1, wl.kv_heads, 4, d), dtype=torch.float16, device=dev),
                                  near_v=torch.zeros((1, wl.kv_heads, 4, d), dtype=torch.float16, device=dev))
-    assert cache.attention_kernel(wl.q_heads, 2) == kernel
+    assert cache.attention_kernel(wl.q_heads, wl.splits, 2) == kernel
     run_case(dev, wl, near_splits=2)
+
+
+@pytest.mark.parametrize("hq,T,S,SN,frac,q32", [(8, 613, 5, 2, 0.1, False),     # G = 1, ragged near splits
+                                                (16, 613, 5, 5, 0.1, False),    # G = 2, near splits = far splits
+                                                (32, 1000, 4, 1, 0.05, True),   # G = 4, one near split, fp32 query
+                                                (64, 700, 3, 3, 0.03, False),   # G = 8, 21 near tokens: 2 empty splits
+                                                (32, 300, 16, 16, 0.5, False)])  # 256 work-groups, 11 empty near splits
+def test_decode_buffer_one_launch(dev, hq, T, S, SN, frac, q32):
+    """fp16 near tier and 4-bit codes at d = 128 in one pair-table launch:
+    every (b, query head) output and every split's partial state (near
+    splits in the original domain, far splits rotated) against the oracle,
+    over query groups 1-8, near split counts from 1 to the far split count,
+    ragged and empty near splits and an fp32 query."""
+    wl = W.WORKLOADS["decode_buffer"].scaled(batch=2, q_heads=hq, seq_len=T, splits=S, near_splits=SN,
+                                             near_fraction=frac)
+    inp = W.generate(wl)
+    if q32:
+        inp = dataclasses.replace(inp, q=inp.q.astype(np.float32))
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, 8, _fmt(4), _fmt(4), seed=W.SIGN_SEED,
+                                 device=dev, near_k=torch.zeros((wl.batch, wl.kv_heads, 4, wl.head_dim),
+                                                                dtype=torch.float16, device=dev),
+                                 near_v=torch.zeros((wl.batch, wl.kv_heads, 4, wl.head_dim),
+                                                    dtype=torch.float16, device=dev))
+    assert cache.attention_kernel(wl.q_heads, S, SN) == "attend_pair_kernel"
+    run_case(dev, wl, inp=inp)
 
 
 @pytest.mark.parametrize("hq", [8, 32])
@@ -407,7 +434,7 @@ def test_outlier_two_stream(dev, d, bits, hq, kv):
     cache.calibrate(_t(inp.k[:, :, :128], dev))
     idx = O.calibrate_outliers(inp.k[:, :, :128])
     assert np.array_equal(cache.outlier_idx.cpu().numpy(), idx)
-    assert cache.attention_kernel(wl.q_heads) == "attend_kernel"
+    assert cache.attention_kernel(wl.q_heads, wl.splits) == "attend_kernel"
     cache.append(_t(inp.k, dev), _t(inp.v, dev), start_pos=0)
     q = _t(inp.q, dev)
     out = cache.decode(q, T, wl.splits).cpu().numpy()
@@ -479,7 +506,7 @@ def test_qjl_residual_sketch(dev, d, kb, vb, hq, kv, dtype, near):
                                  near_k=None if kn is None else _t(kn, dev),
                                  near_v=None if vn is None else _t(vn, dev),
                                  qjl_proj_t=_t(np.ascontiguousarray(S.T), dev))
-    assert cache.attention_kernel(wl.q_heads, 2 if near else 0) == "attend_kernel"
+    assert cache.attention_kernel(wl.q_heads, wl.splits, 2 if near else 0) == "attend_kernel"
     cache.append(_t(kf, dev), _t(vf, dev), start_pos=0)
     SN = 2 if near else 0
     out = cache.decode(_t(inp.q, dev), T, wl.splits, SN).cpu().numpy()
@@ -671,7 +698,7 @@ def test_largest_attention_grid(dev, d, bits, hkv, G, kernel):
                                              splits=1).with_bits(bits)
     inp = W.generate(wl)
     cache = kvq.KVCache.allocate(B, hkv, d, 20, _fmt(bits), _fmt(bits), seed=W.SIGN_SEED, device=dev)
-    assert cache.attention_kernel(wl.q_heads) == kernel
+    assert cache.attention_kernel(wl.q_heads, wl.splits) == kernel
     cache.append(_t(inp.k, dev), _t(inp.v, dev), 0)
     out = cache.decode(_t(inp.q, dev), 20, 1)
     torch.cuda.synchronize()
@@ -734,7 +761,7 @@ def _full_size(dev, name, bits=None, every_row=False, all_heads=False, sample_he
     rng = np.random.default_rng(0)
     s = _signs(d)
     G = wl.group
-    print(f"{wl.name}: cache written and decoded; kernel {cache.attention_kernel(wl.q_heads, SN)}", flush=True)
+    print(f"{wl.name}: cache written and decoded; kernel {cache.attention_kernel(wl.q_heads, wl.splits, SN)}", flush=True)
     if every_row:
         for tag, gp, gn, x, nb in (("K", cache.k_codes, cache.k_norms, kf, wl.k_bits),
                                    ("V", cache.v_codes, cache.v_norms, vf, wl.v_bits)):
