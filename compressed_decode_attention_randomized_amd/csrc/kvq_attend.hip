@@ -1023,7 +1023,8 @@ AttendArgs far_part(const AttendArgs &a) {
 const char *attend_kernel_name(const AttendArgs &a) {
   // NULL where launch_attend would return KVQ_EUNSUPPORTED
   const char *valu = valu_attend_supported(a) ? "attend_kernel" : nullptr;
-  if (a.outlier_idx || a.qjl_proj) return valu;
+  if (a.qjl_proj) return valu;
+  if (a.outlier_idx) return (a.num_near_splits == 0 && wide_attend_supported(a)) ? "attend_wide_kernel" : valu;
   if (a.num_near_splits > 0) {
     if (pair_near_supported(a)) return "attend_pair_kernel";
     const AttendArgs f = far_part(a);
@@ -1043,8 +1044,17 @@ hipError_t launch_attend_gated(const AttendArgs &a, hipStream_t stream, bool *su
 }
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported) {
-  // Key side streams (outliers, QJL sketch) are scored by the VALU kernel only.
-  if (a.outlier_idx || a.qjl_proj) return launch_valu(a, stream, supported);
+  // The QJL sketch is scored by the VALU kernel only; the outlier stream
+  // beside 4-bit codes at d = 128 without a near tier by the two-wave-per-
+  // SIMD matrix-core kernel, otherwise by the VALU kernel.
+  if (a.qjl_proj) return launch_valu(a, stream, supported);
+  if (a.outlier_idx) {
+    if (a.num_near_splits == 0 && wide_attend_supported(a)) {
+      *supported = true;
+      return launch_attend_wide(a, stream);
+    }
+    return launch_valu(a, stream, supported);
+  }
   // A near tier (fp16 rows, original domain) beside 4-bit codes at d = 128:
   // both tiers in one launch of the pair-table kernel.  Beside other codes
   // that a pair-table kernel covers: the near splits run on the VALU kernel

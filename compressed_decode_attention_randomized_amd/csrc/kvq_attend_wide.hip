@@ -1,12 +1,20 @@
 // Split-K GQA decode attention on 4-, 3- or 2-bit Lloyd-Max keys and values,
-// head dimension 256: the pair-table matrix-core tile of the head-dimension-
-// 128 kernel (shared tile code; quad-table entries for 2-bit codes, tables
-// indexed by 6-bit fields of two codes for 3-bit ones), with twice the
-// registers per tile.
+// head dimension 256, and on 4-bit keys with a key outlier stream at head
+// dimension 128: the pair-table matrix-core tile of the head-dimension-128
+// kernel (shared tile code; quad-table entries for 2-bit codes, tables
+// indexed by 6-bit fields of two codes for 3-bit ones) at two waves per
+// SIMD, which leaves registers for the larger tiles and the side stream.
 //
-// Work mapping: a work-group of 8 waves (two per SIMD: the query operand and
-// the value accumulator take 128 registers at this head size) fills a
-// compute unit and shares one pair table.  Its wave groups serve 2^lg
+// Outlier stream ("Outlier Two-Stream Cache": the keys' largest-variance
+// channels kept as int8 codes with a per-token scale, beside the codes of
+// the keys with those channels zeroed): each lane adds
+// scale * sum_k q[idx_k] code_k / sqrt(d) to its two tokens' scores before
+// the softmax update, the int8 codes and scales of its tokens loaded with
+// the tile and q at the 8 channels held in registers.
+//
+// Work mapping: a work-group of 8 waves (two per SIMD: at d = 256 the query
+// operand and the value accumulator take 128 registers) fills a compute
+// unit and shares one pair table.  Its wave groups serve 2^lg
 // consecutive units of the flattened (b * Hkv + KV head, split) space, so
 // with few query heads per KV head a work-group covers splits of several
 // (b, KV head) pairs and the grid needs no second round of work-groups; a
@@ -31,12 +39,9 @@ namespace {
 
 using namespace pair;
 
-constexpr int D = 256;
 constexpr int kWaves = 8;
 constexpr int kMinWaves = 2;                   // waves per SIMD the register budget is sized for
 constexpr int kBlock = kWaves * 64;
-constexpr int kVDL = D / 16;                    // value coordinates per lane
-constexpr int kRowPad = D + 4;                  // query table row stride (words)
 constexpr int kZeroRow = 2 * kGMax;             // all-zero query row for the unused B columns
 constexpr int kSetupWaves = 4;                  // waves that build the tables and the rotated queries
 
@@ -54,7 +59,81 @@ struct WParams {
   const int8_t *signs;
   const float *k_centroids, *v_centroids;
   float *part_o, *part_ml;
+  // key outlier stream (OUT kernels): [b * Hkv + KV head][8] channels,
+  // [..][capacity][8] int8 codes, [..][capacity] scales
+  const int32_t *out_idx;
+  const int8_t *out_codes;
+  const float *out_scales;
 };
+
+// Outlier stream registers of one tile: the int8 codes (two 8-byte rows)
+// and scales of the lane's two tokens 4g + 2 (n & 1) + {0, 1}.
+struct OutTile {
+  uint4_t oc;
+  uint2_t os;
+};
+
+struct OutSources {
+  const int8_t *oc;
+  const float *os;
+  uint32_t code_bytes, scale_bytes;
+  uint32_t co, so;                     // per-lane offsets
+};
+
+__device__ inline void load_out(OutTile &t, const OutSources &src, int tb, bool skip) {
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(src.oc, skip ? 0u : src.code_bytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(src.os, skip ? 0u : src.scale_bytes);
+  t.oc = __builtin_amdgcn_raw_buffer_load_b128(cr, src.co, tb * kOutlierCount, kStream);
+  t.os = __builtin_amdgcn_raw_buffer_load_b64(sr, src.so, tb * 4, kStream);
+}
+
+// The partial last tile: descriptors from the tile to the slice's end.
+__device__ inline void load_out_tail(OutTile &t, const OutSources &src, int tb) {
+  OutSources s = src;
+  s.oc += (size_t)tb * kOutlierCount;
+  s.os += tb;
+  s.code_bytes -= (uint32_t)tb * kOutlierCount;
+  s.scale_bytes -= (uint32_t)tb * 4;
+  load_out(t, s, 0, false);
+}
+
+// scale * sum_k qo_k code_k for the lane's two tokens (qo: q at the channels
+// times log2(e) / sqrt(d), zero for unused columns).
+__device__ inline void outlier_terms(const OutTile &t, const float (&qo)[kOutlierCount], float (&s)[2]) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t w0 = u ? t.oc.z : t.oc.x, w1 = u ? t.oc.w : t.oc.y;
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kOutlierCount; ++k) {
+      const uint32_t w = (k < 4) ? w0 : w1;
+      const float c = (float)(int8_t)(uint8_t)(w >> (8 * (k & 3)));
+      acc = __builtin_fmaf(qo[k], c, acc);
+    }
+    s[u] = __builtin_fmaf(__builtin_bit_cast(float, u ? t.os.y : t.os.x), acc, s[u]);
+  }
+}
+
+// process_tile with the outlier stream's term added before the softmax update.
+template <int D, bool TAIL>
+__device__ inline void process_tile_out(const Tile<D, 4> &t, const OutTile &ot, const float (&qo)[kOutlierCount],
+                                        const uint4_t (&bk)[D / 16], const uint8_t *tab, uint32_t kslot, uint32_t vslot,
+                                        float sfac, float m1, int tb, int t1, int g, int n, float4_t (&dv)[D / 16],
+                                        float &m_run, float &l_run, float &m_top) {
+  float4_t dk = {0.f, 0.f, 0.f, 0.f};
+  key_scores<D, 4>(t.kw, bk, tab, kslot, dk);
+  const bool odd = n & 1;
+  const uint32_t knp = odd ? t.kn.y : t.kn.x;
+  const uint32_t vnp = odd ? t.vn.y : t.vn.x;
+  float s[2];
+  raw_scores<true>(dk, knp, sfac, n, s);
+  outlier_terms(ot, qo, s);
+  tile_update<D, TAIL>(s, tb, t1, g, n, dv, m_run, l_run, m_top);
+  ValueBytes<D, 4> vb;
+  value_bytes<D, 4>(t, vb, n);
+  const half8_t aw = tile_weights<TAIL, true>(s, vnp, m1, n, m_run, l_run);
+  value_update<D, 4>(vb, tab, vslot, aw, dv);
+}
 
 // Pair tables (4-bit, 3-bit) or quad tables (2-bit) of the key codebook in
 // the first 64 KB of `tab` and, when the value codebook differs, of the
@@ -161,13 +240,17 @@ __device__ inline void fill_tables(uint8_t *tab, const float *kcen, const float 
   if (tid == 0) v_table[0] = same ? 0u : 0x10000u;
 }
 
-template <int BITS>
+template <int D, int BITS, bool OUT>
 __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams P) {
+  static_assert(D == 256 || (D == 128 && BITS == 4), "head dimension 256, or 128 with 4-bit codes");
   using TileT = Tile<D, BITS>;
   constexpr int kRow = TileT::kRow;
+  constexpr int kVDL = D / 16;                    // value coordinates per lane
+  constexpr int kRowPad = D + 4;                  // query table row stride (words)
+  constexpr int kLoads = kTileLoads<D, BITS> + (OUT ? 2 : 0);
   // s_waitcnt vmcnt(loads of one tile) expcnt(7) lgkmcnt(15)
-  constexpr int kWaitOlderTile = 0x0F70 | kTileLoads<D, BITS>;
-  static_assert(kTileLoads<D, BITS> <= 15, "tile loads");
+  constexpr int kWaitOlderTile = 0x0F70 | kLoads;
+  static_assert(kLoads <= 15, "tile loads");
   // pair tables during the loop, the waves' value rows afterwards
   __shared__ __attribute__((aligned(16))) uint8_t tab[2 * 65536];
   __shared__ __attribute__((aligned(16))) uint32_t qtab[2 * kGMax + 1][kRowPad];
@@ -177,6 +260,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
   __shared__ uint32_t next_tile[kWaves];
   __shared__ uint32_t ready;                         // set-up waves done
   __shared__ uint32_t v_table[1];                    // offset of the value table: 0 when shared with the keys
+  __shared__ float qout[OUT ? kGMax : 1][kOutlierCount];   // q at the outlier channels, in log2 units of s
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -209,6 +293,15 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
   src.code_bytes = cap * kRow;
   src.norm_bytes = cap * 2;
   set_offsets<D, BITS>(src, g, n);
+  OutSources osrc;
+  if constexpr (OUT) {
+    osrc.oc = P.out_codes + (size_t)pr * cap * kOutlierCount;
+    osrc.os = P.out_scales + (size_t)pr * cap;
+    osrc.code_bytes = cap * kOutlierCount;
+    osrc.scale_bytes = cap * 4;
+    osrc.co = (uint32_t)(4 * g + 2 * (n & 1)) * kOutlierCount;
+    osrc.so = (uint32_t)(4 * g + 2 * (n & 1)) * 4;
+  }
 
   // ---- set-up ----
   // Waves 0-3 build the code tables and the rotated queries; waves 4-7 first
@@ -222,17 +315,18 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
 
   int ia = gwave, ic = gwave + gw;                   // first tiles of this wave; later ones from its group's counter
   TileT ta, tc;
+  OutTile oa, oc;
   if (wave < kSetupWaves) {
     fill_tables<BITS>(tab, P.k_centroids, P.v_centroids, wave, lane, tid, v_table);
     if (tid < D) qtab[kZeroRow][tid] = 0u;
 
     // ---- rotated queries: rows r = wave and wave + 4 (head r % G of the
     // unit r / G of this work-group) ----
-    // Lane l holds coordinates 4l..4l+3: sign flip, the stride-1 and
-    // stride-2 butterflies in the lane, strides 4..128 across lanes (xor
-    // 1..32).  The rotated vector is scaled so that its largest |z| lies in
-    // (64, 128] and stored in the two B-operand forms (z_hi, z_hi) (row 2r)
-    // and (z_lo, 0) (row 2r+1).
+    // Lane l holds coordinates E l .. E l + E-1 (E = D / 64): sign flip, the
+    // butterflies of strides below E in the lane, strides E..D/2 across
+    // lanes (xor 1..32).  The rotated vector is scaled so that its largest
+    // |z| lies in (64, 128] and stored in the two B-operand forms
+    // (z_hi, z_hi) (row 2r) and (z_lo, 0) (row 2r+1).
     const int q_f16 = P.q_f16;
     const uint32_t q_es = q_f16 ? 2u : 4u;
     for (int rr = 0; rr < 2; ++rr) {
@@ -245,38 +339,68 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
       const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(static_cast<const uint8_t *>(P.q) + q_row * D * q_es,
                                                     has_q ? (uint32_t)D * q_es : 0u);
       const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(P.signs, has_q ? (uint32_t)D : 0u);
-      // both forms are read; the one of the other element size goes unused
-      // (for fp16 rows its upper lanes lie past the row and read as zero)
-      const uint2_t qh = __builtin_amdgcn_raw_buffer_load_b64(qsrc, lane * 8, 0, 0);
-      const uint4_t qf = __builtin_amdgcn_raw_buffer_load_b128(qsrc, lane * 16, 0, 0);
-      const uint32_t sg = __builtin_amdgcn_raw_buffer_load_b32(ssrc, lane * 4, 0, 0);   // signs of 4l..4l+3
-      float z[4];
+      constexpr int E = D / 64;
+      float z[E];
+      if constexpr (E == 4) {
+        // both forms are read; the one of the other element size goes unused
+        // (for fp16 rows its upper lanes lie past the row and read as zero)
+        const uint2_t qh = __builtin_amdgcn_raw_buffer_load_b64(qsrc, lane * 8, 0, 0);
+        const uint4_t qf = __builtin_amdgcn_raw_buffer_load_b128(qsrc, lane * 16, 0, 0);
+        const uint32_t sg = __builtin_amdgcn_raw_buffer_load_b32(ssrc, lane * 4, 0, 0);   // signs of 4l..4l+3
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t hw = (e < 2) ? qh.x : qh.y;
-        const float v = q_f16 ? half_value((hw >> (16 * (e & 1))) & 0xFFFFu) : __builtin_bit_cast(float, qf[e]);
-        z[e] = ((sg >> (8 * e + 7)) & 1u) ? -v : v;
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t hw = (e < 2) ? qh.x : qh.y;
+          const float v = q_f16 ? half_value((hw >> (16 * (e & 1))) & 0xFFFFu) : __builtin_bit_cast(float, qf[e]);
+          z[e] = ((sg >> (8 * e + 7)) & 1u) ? -v : v;
+        }
+        const float a0 = z[0] + z[1], a1 = z[0] - z[1], a2 = z[2] + z[3], a3 = z[2] - z[3];
+        z[0] = a0 + a2;
+        z[1] = a1 + a3;
+        z[2] = a0 - a2;
+        z[3] = a1 - a3;
+      } else {
+        const uint32_t qh = __builtin_amdgcn_raw_buffer_load_b32(qsrc, lane * 4, 0, 0);
+        const uint2_t qf = __builtin_amdgcn_raw_buffer_load_b64(qsrc, lane * 8, 0, 0);
+        const uint32_t sg = __builtin_amdgcn_raw_buffer_load_b16(ssrc, lane * 2, 0, 0);   // signs of 2l, 2l+1
+        const float v0 = q_f16 ? half_value(qh & 0xFFFFu) : __builtin_bit_cast(float, qf.x);
+        const float v1 = q_f16 ? half_value(qh >> 16) : __builtin_bit_cast(float, qf.y);
+        const float w0 = (sg & 0x80u) ? -v0 : v0, w1 = (sg & 0x8000u) ? -v1 : v1;
+        z[0] = w0 + w1;
+        z[1] = w0 - w1;
       }
-      const float a0 = z[0] + z[1], a1 = z[0] - z[1], a2 = z[2] + z[3], a3 = z[2] - z[3];
-      float y[4] = {a0 + a2, a1 + a3, a0 - a2, a1 - a3};
       float am = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        y[e] = fwht_lanes(y[e], lane);
-        am = fmaxf(am, fabsf(y[e]));
+      for (int e = 0; e < E; ++e) {
+        z[e] = fwht_lanes(z[e], lane);
+        am = fmaxf(am, fabsf(z[e]));
       }
       const float zmax = wave_max(am, lane);
       const float qscale = (zmax > 0.f) ? exp2f(7.f - ceilf(log2f(zmax))) : 1.f;
-      uint4_t f0, f1;
+      uint32_t f0[E], f1[E];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float zs = y[e] * qscale;
+      for (int e = 0; e < E; ++e) {
+        const float zs = z[e] * qscale;
         const _Float16 hs = (_Float16)zs;
         f0[e] = pack2(hs, hs);
         f1[e] = pack2((_Float16)(zs - (float)hs), (_Float16)0.f);
       }
-      *reinterpret_cast<uint4_t *>(&qtab[2 * r][lane * 4]) = f0;
-      *reinterpret_cast<uint4_t *>(&qtab[2 * r + 1][lane * 4]) = f1;
+      if constexpr (E == 4) {
+        *reinterpret_cast<uint4_t *>(&qtab[2 * r][lane * 4]) = (uint4_t){f0[0], f0[1], f0[2], f0[3]};
+        *reinterpret_cast<uint4_t *>(&qtab[2 * r + 1][lane * 4]) = (uint4_t){f1[0], f1[1], f1[2], f1[3]};
+      } else {
+        *reinterpret_cast<uint2_t *>(&qtab[2 * r][lane * 2]) = (uint2_t){f0[0], f0[1]};
+        *reinterpret_cast<uint2_t *>(&qtab[2 * r + 1][lane * 2]) = (uint2_t){f1[0], f1[1]};
+      }
+      if constexpr (OUT) {
+        // q at the unit's outlier channels (original domain), in log2 units of s
+        if (lane < kOutlierCount) {
+          const int32_t *oi = P.out_idx + (size_t)(has_q ? u / S : 0) * kOutlierCount;
+          const int c = has_q ? oi[lane] : 0;
+          const float v = q_f16 ? half_value(__builtin_amdgcn_raw_buffer_load_b16(qsrc, (uint32_t)c * 2, 0, 0))
+                                : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qsrc, (uint32_t)c * 4, 0, 0));
+          qout[r][lane] = has_q ? v * (kLog2e / sqrtf((float)D)) : 0.f;
+        }
+      }
       if (lane == 0) qfac[r] = has_q ? kLog2e / ((float)D * kCodeScale * qscale) : 0.f;
     }
     // this wave's table, query and factor writes complete before its count
@@ -285,8 +409,10 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
   }
   __builtin_amdgcn_sched_barrier(0);
   load_tile<D, BITS>(ta, src, t0 + ia * kTile, ia >= ntiles);
+  if constexpr (OUT) load_out(oa, osrc, t0 + ia * kTile, ia >= ntiles);
   __builtin_amdgcn_sched_barrier(0);
   load_tile<D, BITS>(tc, src, t0 + ic * kTile, ic >= ntiles);
+  if constexpr (OUT) load_out(oc, osrc, t0 + ic * kTile, ic >= ntiles);
   __builtin_amdgcn_sched_barrier(0);
 
   // Wait for the set-up counts (bounded: every set-up wave reaches its count
@@ -305,8 +431,17 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
   const int qrow = col ? grp * 2 * G + n : kZeroRow;
   uint4_t bk[D / 16];
 #pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) bk[kb] = *reinterpret_cast<const uint4_t *>(&qtab[qrow][g * 64 + 4 * kb]);
+  for (int kb = 0; kb < D / 16; ++kb) bk[kb] = *reinterpret_cast<const uint4_t *>(&qtab[qrow][g * (D / 4) + 4 * kb]);
   const float sfac = col ? qfac[grp * G + (n >> 1)] : 0.f;
+  float qo[kOutlierCount];
+#pragma unroll
+  for (int k = 0; k < kOutlierCount; ++k) qo[k] = 0.f;
+  if constexpr (OUT) {
+    if (col) {
+#pragma unroll
+      for (int k = 0; k < kOutlierCount; ++k) qo[k] = qout[grp * G + (n >> 1)][k];
+    }
+  }
   // table slot: lane % 32 of 8-byte pair entries, lane % 16 of 16-byte quad entries
   const uint32_t kslot = (BITS != 2) ? (uint32_t)(lane & 31) * 8 : (uint32_t)(lane & 15) * 16;
   const uint32_t vslot = kslot | v_table[0];
@@ -327,27 +462,43 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
     uint32_t nx = 0u;
     if (lane == 0) nx = atomicAdd(&next_tile[grp], 1u);
     __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-    process_tile<D, BITS, false>(ta, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
+    if constexpr (OUT)
+      process_tile_out<D, false>(ta, oa, qo, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run,
+                                 m_top);
+    else
+      process_tile<D, BITS, false>(ta, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
     asm volatile("" : "+v"(nx));                     // keeps the read of the answer here
     const int na = __builtin_amdgcn_readfirstlane(nx);
     load_tile<D, BITS>(ta, src, t0 + na * kTile, na >= ntiles);
+    if constexpr (OUT) load_out(oa, osrc, t0 + na * kTile, na >= ntiles);
     int nc = ntiles;
     if (ic < ntiles) {
       uint32_t ny = 0u;
       if (lane == 0) ny = atomicAdd(&next_tile[grp], 1u);
       __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-      process_tile<D, BITS, false>(tc, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run, l_run, m_top);
+      if constexpr (OUT)
+        process_tile_out<D, false>(tc, oc, qo, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run,
+                                   l_run, m_top);
+      else
+        process_tile<D, BITS, false>(tc, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run, l_run,
+                                     m_top);
       asm volatile("" : "+v"(ny));
       nc = __builtin_amdgcn_readfirstlane(ny);
     }
     load_tile<D, BITS>(tc, src, t0 + nc * kTile, nc >= ntiles);
+    if constexpr (OUT) load_out(oc, osrc, t0 + nc * kTile, nc >= ntiles);
     ia = na;
     ic = nc;
   }
   // the last split's partial tile [t1f, t1)
   if (gwave == 0 && t1f < t1) {
     load_tail_tile<D, BITS>(ta, src, t1f);
-    process_tile<D, BITS, true>(ta, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
+    if constexpr (OUT) {
+      load_out_tail(oa, osrc, t1f);
+      process_tile_out<D, true>(ta, oa, qo, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
+    } else {
+      process_tile<D, BITS, true>(ta, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
+    }
   }
 
   // ---- wave epilogue: (m, l) per head to LDS; after the barrier (the
@@ -362,13 +513,13 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
   __syncthreads();                                   // every wave is done with the tables
   float *red_acc = reinterpret_cast<float *>(tab);   // [wave][head][D]
   // accumulator rows 4g, 4g+1 (head 2g) and 4g+2, 4g+3 (head 2g+1);
-  // coordinate 16n + dt in dv[dt]
+  // coordinate kVDL n + dt in dv[dt]
 #pragma unroll
   for (int hp = 0; hp < 2; ++hp) {
     if (2 * g + hp < G) {
-      float *r = red_acc + (size_t)(wave * kGMax + 2 * g + hp) * D + 16 * n;
+      float *r = red_acc + (size_t)(wave * kGMax + 2 * g + hp) * D + kVDL * n;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < kVDL / 4; ++q)
         *reinterpret_cast<float4_t *>(r + 4 * q) =
             (float4_t){dv[4 * q][2 * hp] + dv[4 * q][2 * hp + 1], dv[4 * q + 1][2 * hp] + dv[4 * q + 1][2 * hp + 1],
                        dv[4 * q + 2][2 * hp] + dv[4 * q + 2][2 * hp + 1], dv[4 * q + 3][2 * hp] + dv[4 * q + 3][2 * hp + 1]};
@@ -434,13 +585,16 @@ int wide_group_log2(int64_t units, int G, int cus) {
 bool wide_attend_supported(const AttendArgs &a) {
   const int G = a.q_heads / a.kv_heads;
   const bool fits = (int64_t)a.capacity * a.head_dim * a.k_format / 8 < (1ll << 31) &&
+                    (int64_t)a.capacity * kOutlierCount < (1ll << 31) &&
                     (int64_t)a.batch * a.kv_heads * a.num_splits < (1ll << 30);
+  if (a.qjl_proj || a.num_near_splits != 0 || G < 1 || G > kGMax || !fits || a.v_format != a.k_format) return false;
+  // the outlier stream: 4-bit keys and values at d = 128
+  if (a.outlier_idx) return a.head_dim == 128 && a.k_format == 4;
   // 3-bit codes at G = 1 stay on the VALU kernel, which is faster there: the
   // tile's 16 matrix-core columns then carry one head, and 3-bit fields cost
   // two address operations per table read against one for 4-bit bytes
   const bool width = a.k_format == 4 || a.k_format == 2 || (a.k_format == 3 && G >= 2);
-  return a.head_dim == D && width && a.v_format == a.k_format && a.num_near_splits == 0 && G >= 1 && G <= kGMax &&
-         fits;
+  return a.head_dim == 256 && width;
 }
 
 hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream, int part_base) {
@@ -451,13 +605,16 @@ hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream, int part_
   const int64_t units = (int64_t)a.batch * a.kv_heads * a.num_splits;
   const int lg = wide_group_log2(units, G, cus);
   const int chunk = ((a.seq_len + a.num_splits - 1) / a.num_splits + kChunkTok - 1) / kChunkTok * kChunkTok;
+  const int D = a.head_dim;
   WParams P{a.q, a.q_f16, a.kv_heads, a.capacity, a.seq_len, a.num_splits, G, chunk, lg, (int)units,
             part_base + a.num_splits, a.k_codes, a.v_codes, a.k_norms, a.v_norms, a.signs, a.k_centroids,
-            a.v_centroids, a.part_o + (size_t)part_base * D, a.part_ml + (size_t)part_base * 2};
+            a.v_centroids, a.part_o + (size_t)part_base * D, a.part_ml + (size_t)part_base * 2,
+            a.outlier_idx, a.outlier_codes, a.outlier_scales};
   dim3 grid((unsigned)((units + (1 << lg) - 1) >> lg));
-  if (a.k_format == 4) hipLaunchKernelGGL(attend_wide_kernel<4>, grid, dim3(kBlock), 0, stream, P);
-  else if (a.k_format == 3) hipLaunchKernelGGL(attend_wide_kernel<3>, grid, dim3(kBlock), 0, stream, P);
-  else hipLaunchKernelGGL(attend_wide_kernel<2>, grid, dim3(kBlock), 0, stream, P);
+  if (a.outlier_idx) hipLaunchKernelGGL((attend_wide_kernel<128, 4, true>), grid, dim3(kBlock), 0, stream, P);
+  else if (a.k_format == 4) hipLaunchKernelGGL((attend_wide_kernel<256, 4, false>), grid, dim3(kBlock), 0, stream, P);
+  else if (a.k_format == 3) hipLaunchKernelGGL((attend_wide_kernel<256, 3, false>), grid, dim3(kBlock), 0, stream, P);
+  else hipLaunchKernelGGL((attend_wide_kernel<256, 2, false>), grid, dim3(kBlock), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -397,11 +397,12 @@ __device__ inline void value_update(const ValueBytes<D, BITS> &vb, const uint8_t
 // lanes of a head keep the same softmax reference.
 //
 // tile_scores: the lane's two scores, scaled by sfac times the tokens' fp16
-// key norms (knp, NORMS) or by sfac alone, with the state moved (and the
-// accumulator rescaled) when a score passes the reference.
-template <int D, bool TAIL, bool NORMS>
-__device__ inline void tile_scores(const float4_t &dk, uint32_t knp, float sfac, int tb, int t1, int g, int n,
-                                   float4_t (&dv)[D / 16], float &m_run, float &l_run, float &m_top, float (&s)[2]) {
+// key norms (knp, NORMS) or by sfac alone (raw_scores), then the state moved
+// (and the accumulator rescaled) when a score passes the reference
+// (tile_update, which masks tokens at or past t1 first).  A key side stream
+// adds its term to the raw scores before the update.
+template <bool NORMS>
+__device__ inline void raw_scores(const float4_t &dk, uint32_t knp, float sfac, int n, float (&s)[2]) {
   const bool odd = n & 1;
   const float f0 = add_swap1(dk[0]), f1 = add_swap1(dk[1]), f2 = add_swap1(dk[2]), f3 = add_swap1(dk[3]);
   if constexpr (NORMS) {
@@ -411,8 +412,13 @@ __device__ inline void tile_scores(const float4_t &dk, uint32_t knp, float sfac,
     s[0] = (odd ? f2 : f0) * sfac;
     s[1] = (odd ? f3 : f1) * sfac;
   }
+}
+
+template <int D, bool TAIL>
+__device__ inline void tile_update(float (&s)[2], int tb, int t1, int g, int n, float4_t (&dv)[D / 16], float &m_run,
+                                   float &l_run, float &m_top) {
   if constexpr (TAIL) {
-    const int tok = tb + 4 * g + 2 * (int)odd;
+    const int tok = tb + 4 * g + 2 * (n & 1);
     s[0] = (tok < t1) ? s[0] : -INFINITY;
     s[1] = (tok + 1 < t1) ? s[1] : -INFINITY;
   }
@@ -438,6 +444,13 @@ __device__ inline void tile_scores(const float4_t &dk, uint32_t knp, float sfac,
       dv[dt][3] *= a1;
     }
   }
+}
+
+template <int D, bool TAIL, bool NORMS>
+__device__ inline void tile_scores(const float4_t &dk, uint32_t knp, float sfac, int tb, int t1, int g, int n,
+                                   float4_t (&dv)[D / 16], float &m_run, float &l_run, float &m_top, float (&s)[2]) {
+  raw_scores<NORMS>(dk, knp, sfac, n, s);
+  tile_update<D, TAIL>(s, tb, t1, g, n, dv, m_run, l_run, m_top);
 }
 
 // tile_weights: w = exp2(s - m) times the tokens' fp16 value norms (vnp,

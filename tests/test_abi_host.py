@@ -183,6 +183,12 @@ def test_attention_kernel_choice():
     assert name(hq=2, k_format=3, v_format=3, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_kernel"
     qjl = dict(qjl_dim=128, qjl_proj=0xC000, qjl_signs=0xD000, qjl_norms=0xE000)
     assert name(**qjl) == "attend_kernel"                                 # the QJL sketch: VALU kernel only
+    out = dict(outlier_count=8, outlier_idx=0xC000, outlier_codes=0xD000, outlier_scales=0xE000)
+    assert name(**out) == "attend_wide_kernel"                            # outlier stream, 4-bit, d=128, G=2
+    assert name(**out, hq=16) == "attend_wide_kernel"                     # G=8
+    assert name(**out, head_dim=256) == "attend_kernel"
+    assert name(**out, k_format=3, v_format=3, hq=2) == "attend_kernel"
+    assert name(**out, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_kernel"
     assert name(k_format=3, v_format=4, hq=8) == "attend_kernel"          # 3-bit keys beside 4-bit values, G=4
     assert name(k_format=3, v_format=4, hq=16) is None                    # G=8 is not built for the VALU kernel
     assert name(k_format=3, v_format=3, hq=4) is None                     # 3-bit values at d=128: G=1 only

@@ -416,16 +416,24 @@ def test_score_gate_and_spike_flags(dev, name, hq, kv, d):
     assert got.sum() > 0
 
 
-@pytest.mark.parametrize("d,bits,hq,kv", [(128, 4, 32, 8), (128, 4, 4, 4), (256, 3, 4, 4), (64, 2, 8, 4)])
-def test_outlier_two_stream(dev, d, bits, hq, kv):
+@pytest.mark.parametrize("d,bits,hq,kv,B,S,kernel", [(128, 4, 32, 8, 2, 3, "attend_wide_kernel"),
+                                                   (128, 4, 4, 4, 2, 3, "attend_wide_kernel"),
+                                                   (128, 4, 16, 8, 2, 5, "attend_wide_kernel"),
+                                                   (128, 4, 64, 8, 2, 3, "attend_wide_kernel"),
+                                                   (128, 4, 16, 8, 8, 8, "attend_wide_kernel"),
+                                                   (256, 3, 4, 4, 2, 3, "attend_kernel"),
+                                                   (64, 2, 8, 4, 2, 3, "attend_kernel")])
+def test_outlier_two_stream(dev, d, bits, hq, kv, B, S, kernel):
     """Key outlier stream: calibration on the first 128 tokens gives the
     oracle's channels; appended keys have the inlier codes and norms of the
     keys with those channels zeroed, and the int8 codes and scales of the
     channels, bit for bit; attention matches the two-stream oracle; and the
     stream brings the result closer to unquantised attention than the plain
-    codec (the workload's keys carry outlier channels)."""
-    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=2, q_heads=hq, kv_heads=kv, head_dim=d, seq_len=600,
-                                             splits=3).with_bits(bits)
+    codec (the workload's keys carry outlier channels).  4-bit codes at
+    d = 128 go to the matrix-core kernel: G = 1, 2, 4, 8, a ragged last tile
+    (600 tokens), and 512 (b * Hkv, split) units (two per work-group)."""
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=B, q_heads=hq, kv_heads=kv, head_dim=d, seq_len=600,
+                                             splits=S).with_bits(bits)
     inp = W.generate(wl)
     T = wl.seq_len
     s = _signs(d)
@@ -434,7 +442,7 @@ def test_outlier_two_stream(dev, d, bits, hq, kv):
     cache.calibrate(_t(inp.k[:, :, :128], dev))
     idx = O.calibrate_outliers(inp.k[:, :, :128])
     assert np.array_equal(cache.outlier_idx.cpu().numpy(), idx)
-    assert cache.attention_kernel(wl.q_heads, wl.splits) == "attend_kernel"
+    assert cache.attention_kernel(wl.q_heads, wl.splits) == kernel
     cache.append(_t(inp.k, dev), _t(inp.v, dev), start_pos=0)
     q = _t(inp.q, dev)
     out = cache.decode(q, T, wl.splits).cpu().numpy()
