@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   src.vc = P.v_codes + (size_t)bh * cap * kRow;
   src.kn = P.k_norms + (size_t)bh * cap;
   src.vn = P.v_norms + (size_t)bh * cap;
-  src.code_bytes = cap * kRow;
+  src.kcode_bytes = src.vcode_bytes = cap * kRow;
   src.norm_bytes = cap * 2;
   set_offsets<D>(src, g, n);
 
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
     uint32_t nx = 0u;
     if (lane == 0) nx = atomicAdd(&next_tile[grp], 1u);
     __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-    process_tile<D, 4, false>(ta, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
+    process_tile<D, 4, 4, false>(ta, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
     asm volatile("" : "+v"(nx));                     // keeps the read of the answer here
     const int na = __builtin_amdgcn_readfirstlane(nx);
     load_tile(ta, src, t0 + na * kTile, na >= ntiles);
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
       uint32_t ny = 0u;
       if (lane == 0) ny = atomicAdd(&next_tile[grp], 1u);
       __builtin_amdgcn_s_waitcnt(kWaitOlderTile);
-      process_tile<D, 4, false>(tc, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run, l_run, m_top);
+      process_tile<D, 4, 4, false>(tc, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run, l_run, m_top);
       asm volatile("" : "+v"(ny));
       nc = __builtin_amdgcn_readfirstlane(ny);
     }
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_pair_kernel(PParams 
   // the last split's partial tile [t1f, t1)
   if (gwave == 0 && t1f < t1) {
     load_tail_tile(ta, src, t1f);
-    process_tile<D, 4, true>(ta, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
+    process_tile<D, 4, 4, true>(ta, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
   }
   }
 

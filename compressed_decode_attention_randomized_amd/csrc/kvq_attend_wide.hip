@@ -116,7 +116,7 @@ __device__ inline void outlier_terms(const OutTile &t, const float (&qo)[kOutlie
 
 // process_tile with the outlier stream's term added before the softmax update.
 template <int D, bool TAIL>
-__device__ inline void process_tile_out(const Tile<D, 4> &t, const OutTile &ot, const float (&qo)[kOutlierCount],
+__device__ inline void process_tile_out(const Tile<D, 4, 4> &t, const OutTile &ot, const float (&qo)[kOutlierCount],
                                         const uint4_t (&bk)[D / 16], const uint8_t *tab, uint32_t kslot, uint32_t vslot,
                                         float sfac, float m1, int tb, int t1, int g, int n, float4_t (&dv)[D / 16],
                                         float &m_run, float &l_run, float &m_top) {
@@ -136,12 +136,12 @@ __device__ inline void process_tile_out(const Tile<D, 4> &t, const OutTile &ot, 
 }
 
 // Pair tables (4-bit, 3-bit) or quad tables (2-bit) of the key codebook in
-// the first 64 KB of `tab` and, when the value codebook differs, of the
-// value codebook in the next 64 KB; run by the four set-up waves.  Thread
-// t < 256 writes the 16-byte chunks t + 256k, k = 0..15 (0..3 for the 64
-// rows of a 3-bit table): row (code byte or field) t/16 + 16k, so the low
-// four bits of the row, t/16 = 4 wave + lane/16, are the same for every k
-// and the high bits are k.
+// the first 64 KB of `tab` and, when the value codebook differs (another
+// width or other centroids), of the value codebook in the next 64 KB; run
+// by the four set-up waves.  Thread t < 256 writes the 16-byte chunks
+// t + 256k, k = 0..15 (0..3 for the 64 rows of a 3-bit table): row (code
+// byte or field) t/16 + 16k, so the low four bits of the row,
+// t/16 = 4 wave + lane/16, are the same for every k and the high bits are k.
 //   4-bit: a row holds 32 slots of (e(c[r % 16]), e(c[r / 16])), a chunk two
 //          slots;
 //   3-bit: a row holds 32 slots of (e(c[r & 7]), e(c[r >> 3])), a chunk two
@@ -149,105 +149,61 @@ __device__ inline void process_tile_out(const Tile<D, 4> &t, const OutTile &ot, 
 //          wave/2 + 2k;
 //   2-bit: a row holds 16 slots of (e(c[r & 3]), e(c[(r >> 2) & 3]),
 //          e(c[(r >> 4) & 3]), e(c[r >> 6])), a chunk one slot.
-// Centroids come through uniform addresses (scalar loads); per-wave parts are
-// chosen by a scalar switch so that constant indices keep them in SGPRs.
+// Centroids come through uniform addresses (scalar loads: every index below
+// is a constant or depends on the wave only).
 template <int BITS>
-__device__ inline void fill_tables(uint8_t *tab, const float *kcen, const float *vcen, int wave, int lane, int tid,
-                                   uint32_t *v_table) {
-  constexpr int NC = 1 << BITS;
-  float ck[16], cv[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    ck[i] = (i < NC) ? kcen[i] : 0.f;
-    cv[i] = (i < NC) ? vcen[i] : 0.f;
-  }
-  bool same = true;
-#pragma unroll
-  for (int i = 0; i < NC; ++i) same = same && (ck[i] == cv[i]);
+__device__ inline void fill_table(uint8_t *t, const float *c, int wave, int lane, int tid) {
   const int r4 = lane >> 4;
-  // entries of the row's low four bits: code t/16 (4-bit) or codes r4 and
-  // wave (2-bit)
-  float lk[4], lv[4];
-  if constexpr (BITS == 4) {
-    switch (wave) {
-      case 0: pick<0, 1>(ck, cv, lk, lv); break;
-      case 1: pick<4, 1>(ck, cv, lk, lv); break;
-      case 2: pick<8, 1>(ck, cv, lk, lv); break;
-      default: pick<12, 1>(ck, cv, lk, lv); break;
-    }
-  } else if constexpr (BITS == 3) {
-    if (wave & 1) pick<4, 1>(ck, cv, lk, lv);
-    else pick<0, 1>(ck, cv, lk, lv);
-  } else {
-    pick<0, 1>(ck, cv, lk, lv);
-  }
-  float lo_k = lk[0], lo_v = lv[0];
+  // entries of the row's low four bits: code t/16 = 4 wave + lane/16
+  // (4-bit), lane/16 + 4 (wave & 1) (3-bit), or codes r4 and wave (2-bit)
+  const int base = (BITS == 4) ? 4 * wave : (BITS == 3) ? 4 * (wave & 1) : 0;
+  float lo = c[base];
 #pragma unroll
-  for (int u = 1; u < 4; ++u) {
-    lo_k = (r4 == u) ? lk[u] : lo_k;
-    lo_v = (r4 == u) ? lv[u] : lo_v;
-  }
-  const uint32_t lok = split_entry(lo_k * kCodeScale), lov = split_entry(lo_v * kCodeScale);
+  for (int u = 1; u < 4; ++u) lo = (r4 == u) ? c[base + u] : lo;
+  const uint32_t le = split_entry(lo * kCodeScale);
   if constexpr (BITS == 3) {
-    const bool upper = wave >> 1;
+    const int upper = wave >> 1;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t hi = split_entry((upper ? ck[2 * k + 1] : ck[2 * k]) * kCodeScale);
-      *reinterpret_cast<uint4_t *>(tab + (tid + 256 * k) * 16) = (uint4_t){lok, hi, lok, hi};
-    }
-    if (!same) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t hi = split_entry((upper ? cv[2 * k + 1] : cv[2 * k]) * kCodeScale);
-        *reinterpret_cast<uint4_t *>(tab + 65536 + (tid + 256 * k) * 16) = (uint4_t){lov, hi, lov, hi};
-      }
+      const uint32_t hi = split_entry(c[2 * k + upper] * kCodeScale);
+      *reinterpret_cast<uint4_t *>(t + (tid + 256 * k) * 16) = (uint4_t){le, hi, le, hi};
     }
   } else if constexpr (BITS == 4) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const uint32_t hi = split_entry(ck[k] * kCodeScale);
-      *reinterpret_cast<uint4_t *>(tab + (tid + 256 * k) * 16) = (uint4_t){lok, hi, lok, hi};
-    }
-    if (!same) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t hi = split_entry(cv[k] * kCodeScale);
-        *reinterpret_cast<uint4_t *>(tab + 65536 + (tid + 256 * k) * 16) = (uint4_t){lov, hi, lov, hi};
-      }
+      const uint32_t hi = split_entry(c[k] * kCodeScale);
+      *reinterpret_cast<uint4_t *>(t + (tid + 256 * k) * 16) = (uint4_t){le, hi, le, hi};
     }
   } else {
-    float wk, wv;
-    switch (wave) {
-      case 0: wk = ck[0]; wv = cv[0]; break;
-      case 1: wk = ck[1]; wv = cv[1]; break;
-      case 2: wk = ck[2]; wv = cv[2]; break;
-      default: wk = ck[3]; wv = cv[3]; break;
-    }
-    const uint32_t mk = split_entry(wk * kCodeScale), mv = split_entry(wv * kCodeScale);
+    const uint32_t m = split_entry(c[wave] * kCodeScale);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const uint32_t e2 = split_entry(ck[k & 3] * kCodeScale), e3 = split_entry(ck[k >> 2] * kCodeScale);
-      *reinterpret_cast<uint4_t *>(tab + (tid + 256 * k) * 16) = (uint4_t){lok, mk, e2, e3};
-    }
-    if (!same) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t e2 = split_entry(cv[k & 3] * kCodeScale), e3 = split_entry(cv[k >> 2] * kCodeScale);
-        *reinterpret_cast<uint4_t *>(tab + 65536 + (tid + 256 * k) * 16) = (uint4_t){lov, mv, e2, e3};
-      }
+      const uint32_t e2 = split_entry(c[k & 3] * kCodeScale), e3 = split_entry(c[k >> 2] * kCodeScale);
+      *reinterpret_cast<uint4_t *>(t + (tid + 256 * k) * 16) = (uint4_t){le, m, e2, e3};
     }
   }
+}
+
+template <int KB, int VB>
+__device__ inline void fill_tables(uint8_t *tab, const float *kcen, const float *vcen, int wave, int lane, int tid,
+                                   uint32_t *v_table) {
+  bool same = KB == VB;
+#pragma unroll
+  for (int i = 0; i < (1 << VB); ++i) same = same && (kcen[i] == vcen[i]);
+  fill_table<KB>(tab, kcen, wave, lane, tid);
+  if (!same) fill_table<VB>(tab + 65536, vcen, wave, lane, tid);
   if (tid == 0) v_table[0] = same ? 0u : 0x10000u;
 }
 
-template <int D, int BITS, bool OUT>
+template <int D, int KB, int VB, bool OUT>
 __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams P) {
-  static_assert(D == 256 || (D == 128 && BITS == 4), "head dimension 256, or 128 with 4-bit codes");
-  using TileT = Tile<D, BITS>;
-  constexpr int kRow = TileT::kRow;
+  static_assert(D == 256 || (D == 128 && VB == 4 && KB >= 3), "head dimension 256, or 128 with 4-bit values");
+  static_assert(!OUT || (KB == 4 && VB == 4), "the outlier stream beside 4-bit codes");
+  using TileT = Tile<D, KB, VB>;
+  constexpr int kKRow = TileT::kKRow, kVRow = TileT::kVRow;
   constexpr int kVDL = D / 16;                    // value coordinates per lane
   constexpr int kRowPad = D + 4;                  // query table row stride (words)
-  constexpr int kLoads = kTileLoads<D, BITS> + (OUT ? 2 : 0);
+  constexpr int kLoads = kTileLoads<D, KB, VB> + (OUT ? 2 : 0);
   // s_waitcnt vmcnt(loads of one tile) expcnt(7) lgkmcnt(15)
   constexpr int kWaitOlderTile = 0x0F70 | kLoads;
   static_assert(kLoads <= 15, "tile loads");
@@ -286,13 +242,14 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
   const int t1f = t0 + ntiles * kTile;
   const uint32_t cap = (uint32_t)P.capacity;
   Sources src;
-  src.kc = P.k_codes + (size_t)pr * cap * kRow;
-  src.vc = P.v_codes + (size_t)pr * cap * kRow;
+  src.kc = P.k_codes + (size_t)pr * cap * kKRow;
+  src.vc = P.v_codes + (size_t)pr * cap * kVRow;
   src.kn = P.k_norms + (size_t)pr * cap;
   src.vn = P.v_norms + (size_t)pr * cap;
-  src.code_bytes = cap * kRow;
+  src.kcode_bytes = cap * kKRow;
+  src.vcode_bytes = cap * kVRow;
   src.norm_bytes = cap * 2;
-  set_offsets<D, BITS>(src, g, n);
+  set_offsets<D, KB, VB>(src, g, n);
   OutSources osrc;
   if constexpr (OUT) {
     osrc.oc = P.out_codes + (size_t)pr * cap * kOutlierCount;
@@ -317,7 +274,7 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
   TileT ta, tc;
   OutTile oa, oc;
   if (wave < kSetupWaves) {
-    fill_tables<BITS>(tab, P.k_centroids, P.v_centroids, wave, lane, tid, v_table);
+    fill_tables<KB, VB>(tab, P.k_centroids, P.v_centroids, wave, lane, tid, v_table);
     if (tid < D) qtab[kZeroRow][tid] = 0u;
 
     // ---- rotated queries: rows r = wave and wave + 4 (head r % G of the
@@ -408,10 +365,10 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
     if (lane == 0) __hip_atomic_fetch_add(&ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __builtin_amdgcn_sched_barrier(0);
-  load_tile<D, BITS>(ta, src, t0 + ia * kTile, ia >= ntiles);
+  load_tile<D, KB, VB>(ta, src, t0 + ia * kTile, ia >= ntiles);
   if constexpr (OUT) load_out(oa, osrc, t0 + ia * kTile, ia >= ntiles);
   __builtin_amdgcn_sched_barrier(0);
-  load_tile<D, BITS>(tc, src, t0 + ic * kTile, ic >= ntiles);
+  load_tile<D, KB, VB>(tc, src, t0 + ic * kTile, ic >= ntiles);
   if constexpr (OUT) load_out(oc, osrc, t0 + ic * kTile, ic >= ntiles);
   __builtin_amdgcn_sched_barrier(0);
 
@@ -443,8 +400,8 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
     }
   }
   // table slot: lane % 32 of 8-byte pair entries, lane % 16 of 16-byte quad entries
-  const uint32_t kslot = (BITS != 2) ? (uint32_t)(lane & 31) * 8 : (uint32_t)(lane & 15) * 16;
-  const uint32_t vslot = kslot | v_table[0];
+  const uint32_t kslot = (KB != 2) ? (uint32_t)(lane & 31) * 8 : (uint32_t)(lane & 15) * 16;
+  const uint32_t vslot = ((VB != 2) ? (uint32_t)(lane & 31) * 8 : (uint32_t)(lane & 15) * 16) | v_table[0];
   float m1 = -1.f;
   asm volatile("" : "+s"(m1));                       // no instruction: keeps -1 from being folded
 
@@ -466,10 +423,10 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
       process_tile_out<D, false>(ta, oa, qo, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run,
                                  m_top);
     else
-      process_tile<D, BITS, false>(ta, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
+      process_tile<D, KB, VB, false>(ta, bk, tab, kslot, vslot, sfac, m1, t0 + ia * kTile, t1, g, n, dv, m_run, l_run, m_top);
     asm volatile("" : "+v"(nx));                     // keeps the read of the answer here
     const int na = __builtin_amdgcn_readfirstlane(nx);
-    load_tile<D, BITS>(ta, src, t0 + na * kTile, na >= ntiles);
+    load_tile<D, KB, VB>(ta, src, t0 + na * kTile, na >= ntiles);
     if constexpr (OUT) load_out(oa, osrc, t0 + na * kTile, na >= ntiles);
     int nc = ntiles;
     if (ic < ntiles) {
@@ -480,24 +437,24 @@ __global__ __launch_bounds__(kBlock, kMinWaves) void attend_wide_kernel(WParams 
         process_tile_out<D, false>(tc, oc, qo, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run,
                                    l_run, m_top);
       else
-        process_tile<D, BITS, false>(tc, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run, l_run,
+        process_tile<D, KB, VB, false>(tc, bk, tab, kslot, vslot, sfac, m1, t0 + ic * kTile, t1, g, n, dv, m_run, l_run,
                                      m_top);
       asm volatile("" : "+v"(ny));
       nc = __builtin_amdgcn_readfirstlane(ny);
     }
-    load_tile<D, BITS>(tc, src, t0 + nc * kTile, nc >= ntiles);
+    load_tile<D, KB, VB>(tc, src, t0 + nc * kTile, nc >= ntiles);
     if constexpr (OUT) load_out(oc, osrc, t0 + nc * kTile, nc >= ntiles);
     ia = na;
     ic = nc;
   }
   // the last split's partial tile [t1f, t1)
   if (gwave == 0 && t1f < t1) {
-    load_tail_tile<D, BITS>(ta, src, t1f);
+    load_tail_tile<D, KB, VB>(ta, src, t1f);
     if constexpr (OUT) {
       load_out_tail(oa, osrc, t1f);
       process_tile_out<D, true>(ta, oa, qo, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
     } else {
-      process_tile<D, BITS, true>(ta, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
+      process_tile<D, KB, VB, true>(ta, bk, tab, kslot, vslot, sfac, m1, t1f, t1, g, n, dv, m_run, l_run, m_top);
     }
   }
 
@@ -584,17 +541,19 @@ int wide_group_log2(int64_t units, int G, int cus) {
 
 bool wide_attend_supported(const AttendArgs &a) {
   const int G = a.q_heads / a.kv_heads;
-  const bool fits = (int64_t)a.capacity * a.head_dim * a.k_format / 8 < (1ll << 31) &&
+  const int bits = a.k_format > a.v_format ? a.k_format : a.v_format;
+  const bool fits = (int64_t)a.capacity * a.head_dim * bits / 8 < (1ll << 31) &&
                     (int64_t)a.capacity * kOutlierCount < (1ll << 31) &&
                     (int64_t)a.batch * a.kv_heads * a.num_splits < (1ll << 30);
-  if (a.qjl_proj || a.num_near_splits != 0 || G < 1 || G > kGMax || !fits || a.v_format != a.k_format) return false;
+  if (a.qjl_proj || a.num_near_splits != 0 || G < 1 || G > kGMax || !fits) return false;
   // the outlier stream: 4-bit keys and values at d = 128
-  if (a.outlier_idx) return a.head_dim == 128 && a.k_format == 4;
+  if (a.outlier_idx) return a.head_dim == 128 && a.k_format == 4 && a.v_format == 4;
   // 3-bit codes at G = 1 stay on the VALU kernel, which is faster there: the
   // tile's 16 matrix-core columns then carry one head, and 3-bit fields cost
   // two address operations per table read against one for 4-bit bytes
+  if (a.head_dim == 128) return a.k_format == 3 && a.v_format == 4 && G >= 2;
   const bool width = a.k_format == 4 || a.k_format == 2 || (a.k_format == 3 && G >= 2);
-  return a.head_dim == 256 && width;
+  return a.head_dim == 256 && a.v_format == a.k_format && width;
 }
 
 hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream, int part_base) {
@@ -611,10 +570,11 @@ hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream, int part_
             a.v_centroids, a.part_o + (size_t)part_base * D, a.part_ml + (size_t)part_base * 2,
             a.outlier_idx, a.outlier_codes, a.outlier_scales};
   dim3 grid((unsigned)((units + (1 << lg) - 1) >> lg));
-  if (a.outlier_idx) hipLaunchKernelGGL((attend_wide_kernel<128, 4, true>), grid, dim3(kBlock), 0, stream, P);
-  else if (a.k_format == 4) hipLaunchKernelGGL((attend_wide_kernel<256, 4, false>), grid, dim3(kBlock), 0, stream, P);
-  else if (a.k_format == 3) hipLaunchKernelGGL((attend_wide_kernel<256, 3, false>), grid, dim3(kBlock), 0, stream, P);
-  else hipLaunchKernelGGL((attend_wide_kernel<256, 2, false>), grid, dim3(kBlock), 0, stream, P);
+  if (a.outlier_idx) hipLaunchKernelGGL((attend_wide_kernel<128, 4, 4, true>), grid, dim3(kBlock), 0, stream, P);
+  else if (D == 128) hipLaunchKernelGGL((attend_wide_kernel<128, 3, 4, false>), grid, dim3(kBlock), 0, stream, P);
+  else if (a.k_format == 4) hipLaunchKernelGGL((attend_wide_kernel<256, 4, 4, false>), grid, dim3(kBlock), 0, stream, P);
+  else if (a.k_format == 3) hipLaunchKernelGGL((attend_wide_kernel<256, 3, 3, false>), grid, dim3(kBlock), 0, stream, P);
+  else hipLaunchKernelGGL((attend_wide_kernel<256, 2, 2, false>), grid, dim3(kBlock), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -120,6 +120,13 @@ __device__ inline void pick(const float (&ck)[16], const float (&cv)[16], float 
   }
 }
 
+// o[i] = c[B + i], i = 0..3, of one centroid table.
+template <int B>
+__device__ inline void pick1(const float (&c)[16], float (&o)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = c[B + i];
+}
+
 // f16(half H of a packed pair) * f: one v_fma_mix_f32 (the fma with a zero
 // addend of a converted fp16 and an fp32 value, rounded once to fp32:
 // equal to a conversion then a multiply).
@@ -138,17 +145,21 @@ __device__ inline void split_pair(float w0, float w1, float m1, uint32_t &hp, ui
   lp = __builtin_bit_cast(uint32_t, l);
 }
 
-// Registers of one tile for head dimension D (128 or 256) and BITS-bit
-// codes (4; 2 with quad entries, see quad_read; 3 at D = 256 with 6-bit
-// pair fields, see field_addr).
-template <int D, int BITS = 4>
+// Registers of one tile for head dimension D (128 or 256), KB-bit key codes
+// and VB-bit value codes (4; 2 with quad entries, see quad_read; 3 with
+// 6-bit pair fields, see field_addr; 3-bit values at D = 256 only).
+template <int D, int KB = 4, int VB = KB>
 struct Tile {
-  static_assert(BITS != 3 || D == 256, "3-bit tiles are laid out for head dimension 256");
-  static constexpr int kRow = D * BITS / 8;       // packed bytes per vector
-  static constexpr int kKeyWords = kRow / 16;     // key slice: token n, bytes [kRow/4 g, kRow/4 (g+1))
-  // value words per token: bytes [kRow/16 n, kRow/16 (n+1)); for 3-bit codes
+  static_assert(VB != 3 || D == 256, "3-bit value tiles are laid out for head dimension 256");
+  static constexpr int kKRow = D * KB / 8;        // packed key bytes per vector
+  static constexpr int kVRow = D * VB / 8;        // packed value bytes per vector
+  static constexpr int kKeyWords = kKRow / 16;    // key slice: token n, bytes [kKRow/4 g, kKRow/4 (g+1))
+  // value words per token: bytes [kVRow/16 n, kVRow/16 (n+1)); for 3-bit codes
   // (6 bytes at 6n) the 8 bytes from the word boundary at or below 6n
-  static constexpr int kValWords = (BITS == 3) ? 2 : kRow / 64;
+  static constexpr int kValWords = (VB == 3) ? 2 : kVRow / 64;
+  // buffer loads of the key slice: 16-byte loads, or for 3-bit codes (a
+  // slice starting on 4 or 8 bytes) 8-byte loads and a 4-byte one for an odd word
+  static constexpr int kKeyLoads = (KB == 3) ? (kKeyWords + 1) / 2 : kKeyWords / 4;
   uint32_t kw[kKeyWords];
   uint32_t vw[4][kValWords];                      // tokens 4g+i
   uint2_t kn, vn;                                 // fp16 norms of tokens 4g..4g+3
@@ -160,44 +171,45 @@ struct Tile {
 struct Sources {
   const uint8_t *kc, *vc;
   const uint16_t *kn, *vn;
-  uint32_t code_bytes, norm_bytes;
+  uint32_t kcode_bytes, vcode_bytes, norm_bytes;
   uint32_t ko, vo, no;                 // per-lane offsets: key slice, value word, norm pair
 };
 
-// Both code widths give lane (g, n) the key coordinates [D/4 g, D/4 (g+1))
+// Every code width gives lane (g, n) the key coordinates [D/4 g, D/4 (g+1))
 // of token n and the value coordinates [D/16 n, D/16 (n+1)) of tokens
 // 4g..4g+3.
-template <int D, int BITS = 4>
+template <int D, int KB = 4, int VB = KB>
 __device__ inline void set_offsets(Sources &src, int g, int n) {
-  constexpr int kRow = Tile<D, BITS>::kRow;
-  src.ko = n * kRow + g * (kRow / 4);
-  src.vo = 4 * g * kRow + ((BITS == 3) ? (n * (kRow / 16)) & ~3 : n * (kRow / 16));
+  constexpr int kKRow = Tile<D, KB, VB>::kKRow, kVRow = Tile<D, KB, VB>::kVRow;
+  src.ko = n * kKRow + g * (kKRow / 4);
+  src.vo = 4 * g * kVRow + ((VB == 3) ? (n * (kVRow / 16)) & ~3 : n * (kVRow / 16));
   src.no = 4 * g * 2;
 }
 
 // Loads of the tile at token tb.  A skipped tile reads through descriptors
 // of size zero, where buffer loads return zeros without touching memory, so
 // loads need no branch and a tile's wait sits at its first use.
-template <int D, int BITS = 4>
-__device__ inline void load_tile(Tile<D, BITS> &t, const Sources &src, int tb, bool skip) {
-  using T = Tile<D, BITS>;
-  const __amdgpu_buffer_rsrc_t kc = make_rsrc(src.kc, skip ? 0u : src.code_bytes);
-  const __amdgpu_buffer_rsrc_t vc = make_rsrc(src.vc, skip ? 0u : src.code_bytes);
+template <int D, int KB = 4, int VB = KB>
+__device__ inline void load_tile(Tile<D, KB, VB> &t, const Sources &src, int tb, bool skip) {
+  using T = Tile<D, KB, VB>;
+  const __amdgpu_buffer_rsrc_t kc = make_rsrc(src.kc, skip ? 0u : src.kcode_bytes);
+  const __amdgpu_buffer_rsrc_t vc = make_rsrc(src.vc, skip ? 0u : src.vcode_bytes);
   const __amdgpu_buffer_rsrc_t kn = make_rsrc(src.kn, skip ? 0u : src.norm_bytes);
   const __amdgpu_buffer_rsrc_t vn = make_rsrc(src.vn, skip ? 0u : src.norm_bytes);
-  const int cs = tb * T::kRow, ns = tb * 2;
-  if constexpr (BITS == 3) {
-    // a 24-byte key slice starts at a multiple of 8 bytes, not always of 16
+  const int ks = tb * T::kKRow, vs = tb * T::kVRow, ns = tb * 2;
+  if constexpr (KB == 3) {
 #pragma unroll
     for (int i = 0; i < T::kKeyWords / 2; ++i) {
-      const uint2_t k = __builtin_amdgcn_raw_buffer_load_b64(kc, src.ko + 8 * i, cs, kStream);
+      const uint2_t k = __builtin_amdgcn_raw_buffer_load_b64(kc, src.ko + 8 * i, ks, kStream);
       t.kw[2 * i] = k.x;
       t.kw[2 * i + 1] = k.y;
     }
+    if constexpr (T::kKeyWords % 2)
+      t.kw[T::kKeyWords - 1] = __builtin_amdgcn_raw_buffer_load_b32(kc, src.ko + 4 * (T::kKeyWords - 1), ks, kStream);
   } else {
 #pragma unroll
     for (int i = 0; i < T::kKeyWords / 4; ++i) {
-      const uint4_t k = __builtin_amdgcn_raw_buffer_load_b128(kc, src.ko + 16 * i, cs, kStream);
+      const uint4_t k = __builtin_amdgcn_raw_buffer_load_b128(kc, src.ko + 16 * i, ks, kStream);
 #pragma unroll
       for (int e = 0; e < 4; ++e) t.kw[4 * i + e] = k[e];
     }
@@ -205,9 +217,9 @@ __device__ inline void load_tile(Tile<D, BITS> &t, const Sources &src, int tb, b
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (T::kValWords == 1) {
-      t.vw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(vc, src.vo + i * T::kRow, cs, kStream);
+      t.vw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(vc, src.vo + i * T::kVRow, vs, kStream);
     } else {
-      const uint2_t v = __builtin_amdgcn_raw_buffer_load_b64(vc, src.vo + i * T::kRow, cs, kStream);
+      const uint2_t v = __builtin_amdgcn_raw_buffer_load_b64(vc, src.vo + i * T::kVRow, vs, kStream);
       t.vw[i][0] = v.x;
       t.vw[i][1] = v.y;
     }
@@ -221,22 +233,23 @@ __device__ inline void load_tile(Tile<D, BITS> &t, const Sources &src, int tb, b
 // zero from the descriptor's range check on the lane offset alone (the
 // full-tile loads above keep the tile offset in a scalar register; their
 // rows always lie inside the slice).
-template <int D, int BITS = 4>
-__device__ inline void load_tail_tile(Tile<D, BITS> &t, const Sources &src, int tb) {
-  constexpr int kRow = Tile<D, BITS>::kRow;
+template <int D, int KB = 4, int VB = KB>
+__device__ inline void load_tail_tile(Tile<D, KB, VB> &t, const Sources &src, int tb) {
+  using T = Tile<D, KB, VB>;
   Sources s = src;
-  s.kc += (size_t)tb * kRow;
-  s.vc += (size_t)tb * kRow;
+  s.kc += (size_t)tb * T::kKRow;
+  s.vc += (size_t)tb * T::kVRow;
   s.kn += tb;
   s.vn += tb;
-  s.code_bytes -= (uint32_t)tb * kRow;
+  s.kcode_bytes -= (uint32_t)tb * T::kKRow;
+  s.vcode_bytes -= (uint32_t)tb * T::kVRow;
   s.norm_bytes -= (uint32_t)tb * 2;
-  load_tile<D, BITS>(t, s, 0, false);
+  load_tile<D, KB, VB>(t, s, 0, false);
 }
 
 // Buffer loads one tile issues (the s_waitcnt vmcnt that leaves one tile in flight).
-template <int D, int BITS = 4>
-constexpr int kTileLoads = Tile<D, BITS>::kKeyWords / (BITS == 3 ? 2 : 4) + 4 + 2;
+template <int D, int KB = 4, int VB = KB>
+constexpr int kTileLoads = Tile<D, KB, VB>::kKeyLoads + 4 + 2;
 
 // 2-bit codes: a byte holds four codes, and the quad table maps it to
 // (e(c[b & 3]), e(c[(b >> 2) & 3]), e(c[(b >> 4) & 3]), e(c[b >> 6])), 16
@@ -267,9 +280,9 @@ __device__ inline uint32_t field_addr(const uint32_t (&w)[N], uint32_t slot) {
 
 // Key block kb: coordinates 4kb..4kb+3 of the lane's slice = bytes 2kb, 2kb+1
 // (4-bit), byte kb (2-bit) or the fields at bits 12kb and 12kb+6 (3-bit).
-template <int D, int BITS, int KB = 0>
-__device__ inline void key_scores(const uint32_t (&kw)[Tile<D, BITS>::kKeyWords], const uint4_t (&bk)[D / 16],
-                                  const uint8_t *tab, uint32_t slot, float4_t &dk) {   // slot: key slot register
+template <int D, int BITS, int KB = 0, int N>
+__device__ inline void key_scores(const uint32_t (&kw)[N], const uint4_t (&bk)[D / 16], const uint8_t *tab,
+                                  uint32_t slot, float4_t &dk) {   // slot: key slot register
   if constexpr (KB < D / 16) {
     half8_t a;
     if constexpr (BITS == 4) {
@@ -283,7 +296,7 @@ __device__ inline void key_scores(const uint32_t (&kw)[Tile<D, BITS>::kKeyWords]
       a = __builtin_bit_cast(half8_t, quad_read(tab, pair_addr<KB % 4>(kw[KB / 4], slot)));
     }
     dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8_t, bk[KB]), dk, 0, 0, 0);
-    key_scores<D, BITS, KB + 1>(kw, bk, tab, slot, dk);
+    key_scores<D, BITS, KB + 1, N>(kw, bk, tab, slot, dk);
   }
 }
 
@@ -306,8 +319,8 @@ struct ValueBytes {
   uint32_t x[4];
 };
 
-template <int D, int BITS>
-__device__ inline void value_bytes(const Tile<D, BITS> &t, ValueBytes<D, BITS> &vb, int n) {
+template <int D, int BITS, int KB>
+__device__ inline void value_bytes(const Tile<D, KB, BITS> &t, ValueBytes<D, BITS> &vb, int n) {
   if constexpr (BITS == 3) {
     // lane n's 16 codes of a token start at bit 16 (n & 1) of its two words;
     // c0: codes 0..7 (coordinates 16n..16n+7), c1: codes 8..15, each in the
@@ -337,7 +350,7 @@ __device__ inline void value_bytes(const Tile<D, BITS> &t, ValueBytes<D, BITS> &
       }
     }
   } else {
-    static_assert(Tile<D, BITS>::kValWords == 1, "one value word per token");
+    static_assert(Tile<D, KB, BITS>::kValWords == 1, "one value word per token");
     constexpr uint32_t kCrumb = 0x33333333u;
     // nibble k of a01: coordinate 2k of tokens 0 (bits 0-1) and 1 (bits
     // 2-3); of b01: coordinate 2k+1; likewise a23, b23 for tokens 2, 3
@@ -480,13 +493,13 @@ __device__ inline half8_t tile_weights(const float (&s)[2], uint32_t vnp, float 
   return __builtin_bit_cast(half8_t, a4);
 }
 
-// One 16-token tile of packed codes.
-template <int D, int BITS, bool TAIL>
-__device__ inline void process_tile(const Tile<D, BITS> &t, const uint4_t (&bk)[D / 16], const uint8_t *tab,
+// One 16-token tile of packed codes (KB-bit keys, VB-bit values).
+template <int D, int KB, int VB, bool TAIL>
+__device__ inline void process_tile(const Tile<D, KB, VB> &t, const uint4_t (&bk)[D / 16], const uint8_t *tab,
                                     uint32_t kslot, uint32_t vslot, float sfac, float m1, int tb, int t1, int g, int n,
                                     float4_t (&dv)[D / 16], float &m_run, float &l_run, float &m_top) {
   float4_t dk = {0.f, 0.f, 0.f, 0.f};
-  key_scores<D, BITS>(t.kw, bk, tab, kslot, dk);
+  key_scores<D, KB>(t.kw, bk, tab, kslot, dk);
 
   const bool odd = n & 1;
   const uint32_t knp = odd ? t.kn.y : t.kn.x;        // fp16 norms of this lane's two tokens
@@ -494,11 +507,11 @@ __device__ inline void process_tile(const Tile<D, BITS> &t, const uint4_t (&bk)[
   float s[2];
   tile_scores<D, TAIL, true>(dk, knp, sfac, tb, t1, g, n, dv, m_run, l_run, m_top, s);
 
-  ValueBytes<D, BITS> vb;
-  value_bytes<D, BITS>(t, vb, n);
+  ValueBytes<D, VB> vb;
+  value_bytes<D, VB>(t, vb, n);
 
   const half8_t aw = tile_weights<TAIL, true>(s, vnp, m1, n, m_run, l_run);
-  value_update<D, BITS>(vb, tab, vslot, aw, dv);
+  value_update<D, VB>(vb, tab, vslot, aw, dv);
 }
 
 }  // namespace pair

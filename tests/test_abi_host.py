@@ -189,8 +189,9 @@ def test_attention_kernel_choice():
     assert name(**out, head_dim=256) == "attend_kernel"
     assert name(**out, k_format=3, v_format=3, hq=2) == "attend_kernel"
     assert name(**out, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_kernel"
-    assert name(k_format=3, v_format=4, hq=8) == "attend_kernel"          # 3-bit keys beside 4-bit values, G=4
-    assert name(k_format=3, v_format=4, hq=16) is None                    # G=8 is not built for the VALU kernel
+    assert name(k_format=3, v_format=4, hq=8) == "attend_wide_kernel"     # 3-bit keys beside 4-bit values, G=4
+    assert name(k_format=3, v_format=4, hq=16) == "attend_wide_kernel"    # G=8
+    assert name(k_format=3, v_format=4, hq=2) == "attend_kernel"          # G=1: VALU kernel
     assert name(k_format=3, v_format=3, hq=4) is None                     # 3-bit values at d=128: G=1 only
     assert name(k_format=3, v_format=3, hq=2) == "attend_kernel"
     assert name(hq=3) is None and name(head_dim=96) is None

@@ -257,6 +257,20 @@ def test_head_dim_256_unit_groups(dev, hq, bits):
     run_case(dev, wl)
 
 
+@pytest.mark.parametrize("hq,kv,B,T,S", [(4, 2, 2, 1000, 4), (16, 8, 2, 613, 5), (32, 8, 2, 600, 3),
+                                         (64, 8, 2, 700, 3), (16, 8, 8, 300, 8)])
+def test_three_bit_keys_four_bit_values(dev, hq, kv, B, T, S):
+    """3-bit keys beside 4-bit values at d = 128 (the key layout of the
+    page's 68-byte TurboQuantProd key without its sketch) on the matrix-core
+    kernel: G = 2, 2, 4, 8 and 512 units; ragged last tiles; every split's
+    partial state checked."""
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=B, q_heads=hq, kv_heads=kv, seq_len=T, splits=S, k_bits=3)
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, 8, _fmt(3), _fmt(4), seed=W.SIGN_SEED,
+                                 device=dev)
+    assert cache.attention_kernel(wl.q_heads, S) == "attend_wide_kernel"
+    run_case(dev, wl)
+
+
 @pytest.mark.parametrize("hq,kv,T,splits", [(2, 2, 1000, 4), (8, 2, 1000, 7), (16, 2, 300, 16), (64, 8, 77, 3)])
 def test_head_dim_128_two_bit(dev, hq, kv, T, splits):
     """Head dimension 128 with 2-bit keys and values (the matrix-core kernel
