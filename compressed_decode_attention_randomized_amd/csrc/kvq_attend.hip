@@ -1023,8 +1023,8 @@ AttendArgs far_part(const AttendArgs &a) {
 const char *attend_kernel_name(const AttendArgs &a) {
   // NULL where launch_attend would return KVQ_EUNSUPPORTED
   const char *valu = valu_attend_supported(a) ? "attend_kernel" : nullptr;
-  if (a.qjl_proj) return valu;
-  if (a.outlier_idx) return (a.num_near_splits == 0 && wide_attend_supported(a)) ? "attend_wide_kernel" : valu;
+  if (a.qjl_proj || a.outlier_idx)
+    return (a.num_near_splits == 0 && wide_attend_supported(a)) ? "attend_wide_kernel" : valu;
   if (a.num_near_splits > 0) {
     if (pair_near_supported(a)) return "attend_pair_kernel";
     const AttendArgs f = far_part(a);
@@ -1044,11 +1044,11 @@ hipError_t launch_attend_gated(const AttendArgs &a, hipStream_t stream, bool *su
 }
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream, bool *supported) {
-  // The QJL sketch is scored by the VALU kernel only; the outlier stream
-  // beside 4-bit codes at d = 128 without a near tier by the two-wave-per-
-  // SIMD matrix-core kernel, otherwise by the VALU kernel.
-  if (a.qjl_proj) return launch_valu(a, stream, supported);
-  if (a.outlier_idx) {
+  // Key side streams: the outlier stream beside 4-bit codes and the QJL
+  // sketch beside 3-bit keys and 4-bit values (G >= 2), both at d = 128
+  // without a near tier, on the two-wave-per-SIMD matrix-core kernel;
+  // otherwise on the VALU kernel.
+  if (a.qjl_proj || a.outlier_idx) {
     if (a.num_near_splits == 0 && wide_attend_supported(a)) {
       *supported = true;
       return launch_attend_wide(a, stream);

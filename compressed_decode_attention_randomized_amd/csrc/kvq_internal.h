@@ -99,7 +99,7 @@ hipError_t launch_attend_pair(const AttendArgs &a, hipStream_t stream, int part_
 // Two-wave-per-SIMD pair-table variant: head_dim 256 (4-, 2-bit keys and
 // values at G <= 8, 3-bit at 2 <= G <= 8), or head_dim 128 with 4-bit codes
 // and the key outlier stream, or 3-bit keys beside 4-bit values at
-// 2 <= G <= 8; no near tier, no QJL sketch.
+// 2 <= G <= 8 (with or without the QJL sketch); no near tier.
 bool wide_attend_supported(const AttendArgs &a);
 hipError_t launch_attend_wide(const AttendArgs &a, hipStream_t stream, int part_base = 0);
 

@@ -182,7 +182,9 @@ def test_attention_kernel_choice():
     assert name(S=0) is None
     assert name(hq=2, k_format=3, v_format=3, near_len=4, near_k=0xC000, near_v=0xD000, SN=1) == "attend_kernel"
     qjl = dict(qjl_dim=128, qjl_proj=0xC000, qjl_signs=0xD000, qjl_norms=0xE000)
-    assert name(**qjl) == "attend_kernel"                                 # the QJL sketch: VALU kernel only
+    assert name(**qjl) == "attend_kernel"                                 # the QJL sketch beside 4-bit keys: VALU kernel
+    assert name(**qjl, k_format=3, v_format=4) == "attend_wide_kernel"    # the page's 68-byte key, G=2
+    assert name(**qjl, k_format=3, v_format=4, hq=2) == "attend_kernel"   # G=1
     out = dict(outlier_count=8, outlier_idx=0xC000, outlier_codes=0xD000, outlier_scales=0xE000)
     assert name(**out) == "attend_wide_kernel"                            # outlier stream, 4-bit, d=128, G=2
     assert name(**out, hq=16) == "attend_wide_kernel"                     # G=8

@@ -242,29 +242,33 @@ def test_distinct_value_codebook(dev, d, bits, kernel):
     _rows_close("distinct value codebook", out.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("hq,bits", [(8, 4), (16, 4), (24, 4), (64, 4), (16, 3), (24, 3), (32, 3), (64, 3),
-                                     (8, 2), (24, 2), (64, 2)])
-def test_head_dim_256_unit_groups(dev, hq, bits):
+@pytest.mark.parametrize("hq,bits,dtype", [(8, 4, "f16"), (16, 4, "f16"), (24, 4, "f16"), (64, 4, "f16"),
+                                           (16, 3, "f16"), (24, 3, "f16"), (32, 3, "f16"), (64, 3, "f16"),
+                                           (8, 2, "f16"), (24, 2, "f16"), (64, 2, "f16"), (16, 4, "f32")])
+def test_head_dim_256_unit_groups(dev, hq, bits, dtype):
     """Head dimension 256, 4-, 3- and 2-bit, G = 1 (4- and 2-bit), 2, 3, 4 (3-bit), 8
     query heads per KV head, with 512 (b * Hkv, split) units: more than the
     compute units, so a work-group serves several units (for G <= 4), with
     ragged and empty splits (200 tokens in chunks of 32 over 8 splits) and
     every head checked."""
-    wl = W.WORKLOADS["bitwidth_sweep"].scaled(batch=8, q_heads=hq, kv_heads=8, seq_len=200, splits=8).with_bits(bits)
+    wl = W.WORKLOADS["bitwidth_sweep"].scaled(batch=8, q_heads=hq, kv_heads=8, seq_len=200, splits=8,
+                                              dtype=dtype).with_bits(bits)
     cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, wl.seq_len, _fmt(bits), _fmt(bits),
                                  seed=W.SIGN_SEED, device=dev)
     assert cache.attention_kernel(wl.q_heads, wl.splits) == "attend_wide_kernel"
     run_case(dev, wl)
 
 
-@pytest.mark.parametrize("hq,kv,B,T,S", [(4, 2, 2, 1000, 4), (16, 8, 2, 613, 5), (32, 8, 2, 600, 3),
-                                         (64, 8, 2, 700, 3), (16, 8, 8, 300, 8)])
-def test_three_bit_keys_four_bit_values(dev, hq, kv, B, T, S):
+@pytest.mark.parametrize("hq,kv,B,T,S,dtype", [(4, 2, 2, 1000, 4, "f16"), (16, 8, 2, 613, 5, "f16"),
+                                               (32, 8, 2, 600, 3, "f16"), (64, 8, 2, 700, 3, "f16"),
+                                               (16, 8, 8, 300, 8, "f16"), (32, 8, 2, 600, 3, "f32")])
+def test_three_bit_keys_four_bit_values(dev, hq, kv, B, T, S, dtype):
     """3-bit keys beside 4-bit values at d = 128 (the key layout of the
     page's 68-byte TurboQuantProd key without its sketch) on the matrix-core
-    kernel: G = 2, 2, 4, 8 and 512 units; ragged last tiles; every split's
-    partial state checked."""
-    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=B, q_heads=hq, kv_heads=kv, seq_len=T, splits=S, k_bits=3)
+    kernel: G = 2, 2, 4, 8 and 512 units; ragged last tiles; an fp32 query;
+    every split's partial state checked."""
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=B, q_heads=hq, kv_heads=kv, seq_len=T, splits=S, k_bits=3,
+                                             dtype=dtype)
     cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, wl.head_dim, 8, _fmt(3), _fmt(4), seed=W.SIGN_SEED,
                                  device=dev)
     assert cache.attention_kernel(wl.q_heads, S) == "attend_wide_kernel"
@@ -503,17 +507,27 @@ def _check_sketch(name, cache, x, kb, d, S, T):
     return z, rn
 
 
-@pytest.mark.parametrize("d,kb,vb,hq,kv,dtype,near", [(128, 3, 4, 32, 8, "f16", False),
-                                                      (128, 4, 4, 4, 4, "f16", False),
-                                                      (256, 2, 2, 8, 4, "f16", False),
-                                                      (64, 3, 3, 4, 4, "f32", False),
-                                                      (128, 4, 4, 32, 8, "f16", True)])
-def test_qjl_residual_sketch(dev, d, kb, vb, hq, kv, dtype, near):
+@pytest.mark.parametrize("d,kb,vb,hq,kv,dtype,near,B,S,kernel", [
+    (128, 3, 4, 32, 8, "f16", False, 2, 3, "attend_wide_kernel"),
+    (128, 3, 4, 16, 8, "f16", False, 2, 5, "attend_wide_kernel"),
+    (128, 3, 4, 64, 8, "f16", False, 2, 3, "attend_wide_kernel"),
+    (128, 3, 4, 32, 8, "f32", False, 2, 3, "attend_wide_kernel"),
+    (128, 3, 4, 64, 8, "f32", False, 2, 3, "attend_wide_kernel"),
+    (128, 3, 4, 16, 8, "f16", False, 8, 8, "attend_wide_kernel"),
+    (128, 3, 4, 8, 8, "f16", False, 2, 3, "attend_kernel"),
+    (128, 4, 4, 4, 4, "f16", False, 2, 3, "attend_kernel"),
+    (256, 2, 2, 8, 4, "f16", False, 2, 3, "attend_kernel"),
+    (64, 3, 3, 4, 4, "f32", False, 2, 3, "attend_kernel"),
+    (128, 4, 4, 32, 8, "f16", True, 2, 3, "attend_kernel")])
+def test_qjl_residual_sketch(dev, d, kb, vb, hq, kv, dtype, near, B, S, kernel):
     """QJL residual sketch: appended keys carry the oracle's codes, sketch
     bits and residual norms; attention matches the oracle's corrected scores
-    (with a near tier: the fp16 decode buffer in the same launch)."""
+    (with a near tier: the fp16 decode buffer in the same launch).  The
+    page's 68-byte key (3-bit codes, sketch, two norms) beside 4-bit values
+    at d = 128 and G >= 2 runs on the matrix-core kernel: G = 2, 4, 8, an
+    fp32 query, a ragged last tile and 512 units."""
     base = W.WORKLOADS["decode_buffer" if near else "llama7b_layer"]
-    wl = base.scaled(batch=2, q_heads=hq, kv_heads=kv, head_dim=d, seq_len=600, splits=3, dtype=dtype,
+    wl = base.scaled(batch=B, q_heads=hq, kv_heads=kv, head_dim=d, seq_len=600, splits=S, dtype=dtype,
                      k_bits=kb, v_bits=vb, near_fraction=(64 / 600 if near else 0.0), near_splits=2)
     inp = W.generate(wl)
     S = W.qjl_projection(d)
@@ -528,7 +542,7 @@ def test_qjl_residual_sketch(dev, d, kb, vb, hq, kv, dtype, near):
                                  near_k=None if kn is None else _t(kn, dev),
                                  near_v=None if vn is None else _t(vn, dev),
                                  qjl_proj_t=_t(np.ascontiguousarray(S.T), dev))
-    assert cache.attention_kernel(wl.q_heads, wl.splits, 2 if near else 0) == "attend_kernel"
+    assert cache.attention_kernel(wl.q_heads, wl.splits, 2 if near else 0) == kernel
     cache.append(_t(kf, dev), _t(vf, dev), start_pos=0)
     SN = 2 if near else 0
     out = cache.decode(_t(inp.q, dev), T, wl.splits, SN).cpu().numpy()
