@@ -49,6 +49,10 @@ METRIC = "packed-KV decode-attention HBM GB/s (% of peak) + quantize-append toke
 TABLE = ("single_head_fp32", "llama7b_layer", "long_context", "bitwidth_sweep@b2", "bitwidth_sweep@b3",
          "bitwidth_sweep@b4", "decode_buffer", "two_tier")
 MAX_REPLICAS = 64
+# key side streams measured beside the table (llama7b_layer shapes): the
+# outlier stream beside 4-bit codes, and the QJL sketch beside 3-bit keys
+# (the page's 68-byte key) and 4-bit values
+SIDE_TABLE = (("llama7b_layer+outliers", dict(outliers=8), 4), ("llama7b_layer@k3+qjl", dict(qjl=True), 3))
 
 
 def cache_bytes(wl: W.Workload, outliers: int = 0, qjl: bool = False) -> dict:
@@ -457,6 +461,15 @@ def main(argv=None) -> int:
                 continue
             print(f"# table: {name}", file=sys.stderr, flush=True)
             r = measure(workload(name), plain, dev, steps=min(args.steps, 100), reps=args.reps)
+            table.append(r)
+            torch.cuda.empty_cache()
+        for label, kw, kbits in SIDE_TABLE:
+            print(f"# table: {label}", file=sys.stderr, flush=True)
+            side = argparse.Namespace(**{**vars(plain), **kw})
+            base = workload("llama7b_layer")
+            swl = dataclasses.replace(base, k_bits=kbits, name=label) if kbits != base.k_bits else base
+            r = measure(swl, side, dev, steps=min(args.steps, 100), reps=args.reps)
+            r["workload"] = label
             table.append(r)
             torch.cuda.empty_cache()
     print(f"# headline: {wl.name}: cache {cache_bytes(wl, args.outliers, args.qjl)['cache'] / 1e6:.1f} MB",
