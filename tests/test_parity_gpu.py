@@ -275,6 +275,22 @@ def test_three_bit_keys_four_bit_values(dev, hq, kv, B, T, S, dtype):
     run_case(dev, wl)
 
 
+@pytest.mark.parametrize("d,kb,vb,hq,kv,kernel", [(128, 4, 4, 8, 4, "attend_pair_kernel"),
+                                                 (128, 2, 2, 8, 4, "attend_mfma_kernel"),
+                                                 (128, 3, 3, 4, 4, "attend_kernel"),
+                                                 (64, 4, 4, 16, 4, "attend_kernel"),
+                                                 (256, 3, 3, 4, 4, "attend_kernel"),
+                                                 (256, 2, 2, 8, 4, "attend_wide_kernel")])
+def test_fp32_query_every_kernel(dev, d, kb, vb, hq, kv, kernel):
+    """An fp32 query (and fp32 keys and values) on every attention kernel:
+    query loads take another path than fp16 rows in each of them."""
+    wl = W.WORKLOADS["llama7b_layer"].scaled(batch=2, q_heads=hq, kv_heads=kv, head_dim=d, seq_len=333, splits=3,
+                                             dtype="f32", k_bits=kb, v_bits=vb)
+    cache = kvq.KVCache.allocate(wl.batch, wl.kv_heads, d, 8, _fmt(kb), _fmt(vb), seed=W.SIGN_SEED, device=dev)
+    assert cache.attention_kernel(wl.q_heads, wl.splits) == kernel
+    run_case(dev, wl)
+
+
 @pytest.mark.parametrize("hq,kv,T,splits", [(2, 2, 1000, 4), (8, 2, 1000, 7), (16, 2, 300, 16), (64, 8, 77, 3)])
 def test_head_dim_128_two_bit(dev, hq, kv, T, splits):
     """Head dimension 128 with 2-bit keys and values (the matrix-core kernel
