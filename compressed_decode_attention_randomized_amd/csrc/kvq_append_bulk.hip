@@ -30,7 +30,15 @@
 //     fp16 norm, within that bound of a decision is recomputed by the whole
 //     wave in float64 (2-4 coordinates per lane, butterflies across lanes by
 //     shuffles), so codes and norms equal the exact encoding everywhere
-//     outside the 1e-6 window of the parity contract.
+//     outside the 1e-6 window of the parity contract;
+//   * a key outlier stream ("Outlier Two-Stream Cache") is taken from the
+//     staged rows before the lanes read them: each lane reads its share of
+//     the vector's 8 channels, the vector's lanes reduce the largest
+//     magnitude, scale = that / 127 in fp32 and code = RNE(x / scale) in
+//     float64 (exact: an fp16 over an fp32 is a half-integer or at least
+//     2^-25 of itself away from one, far past float64's rounding), the codes
+//     and scale are stored, and the channels are zeroed in LDS so the
+//     encoding above sees the inlier key.
 // Sources: "The Engineering Behind AdapTQ", "The Math Fix" (sign flip + FWHT,
 // add/sub only); VeloxQuant-MLX "Stage 2" (normalise, fp16 norm, nearest
 // centroid) and "The Bit-Packing Problem" (LSB-first layout); "FoveatedKV",
@@ -88,6 +96,11 @@ struct StreamArgs {
   uint8_t *codes;            // [pairs][capacity][row]
   uint16_t *norms;           // [pairs][capacity] (Lloyd-Max formats)
   const float *centroids;    // [2^bits] (Lloyd-Max formats)
+  // key outlier stream (OUT kernels, keys only): channels [pairs][8],
+  // int8 codes [pairs][capacity][8], scales [pairs][capacity]
+  const int32_t *out_idx;
+  int8_t *out_codes;
+  float *out_scales;
 };
 
 struct BulkArgs {
@@ -217,7 +230,7 @@ __device__ inline float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_
 // ---- the exact path: one vector in float64, by the whole wave ----
 // (kept out of line: it is rare, and inlined its lane constants would be
 // hoisted out of the batch loop and held in registers the fast path needs)
-template <int D, int FMT>
+template <int D, int FMT, bool OUT>
 __device__ __attribute__((noinline)) void encode_exact(const StreamArgs &st, const int8_t *signs, const double *mids,
                                                        int pair, int t, int n_new, int capacity, int start_pos,
                                                        uint8_t *scratch) {
@@ -229,7 +242,12 @@ __device__ __attribute__((noinline)) void encode_exact(const StreamArgs &st, con
   double ss = 0.0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const double v = (double)(float)__builtin_bit_cast(_Float16, src[e]);
+    double v = (double)(float)__builtin_bit_cast(_Float16, src[e]);
+    if constexpr (OUT) {
+      // the outlier channels are zero in the inlier key
+#pragma unroll
+      for (int k = 0; k < kOutlierCount; ++k) v = (st.out_idx[pair * kOutlierCount + k] == lane * E + e) ? 0.0 : v;
+    }
     ss = fma(v, v, ss);
     x[e] = signs[lane * E + e] < 0 ? -v : v;
   }
@@ -305,9 +323,53 @@ __device__ __attribute__((noinline)) void encode_exact(const StreamArgs &st, con
 }
 
 // ---- the fast path: one batch of one stream ----
-template <int D, int FMT>
+// The outlier stream of one staged batch (see the file comment): lane
+// (v, h) takes channels k = KPL h .. KPL h + KPL-1 of vector v.
+template <int D>
+__device__ inline void outlier_batch(const StreamArgs &st, int pair, int t0, int n_new, int capacity, int start_pos,
+                                     uint8_t *buf, uint32_t drop) {
+  using S = Shape<D>;
+  constexpr int KPL = kOutlierCount / S::LPV;
+  const int lane = threadIdx.x & 63;
+  const int v = lane % S::VPB, h = lane / S::VPB;
+  const int j = v / S::VPI, a = v % S::VPI;
+  uint8_t *vb = buf + j * S::STRIDE + 16 * a;
+  const int32_t *idx = st.out_idx + (size_t)pair * kOutlierCount;
+  float xk[KPL];
+  uint32_t addr[KPL];
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) {
+    const uint32_t c = (uint32_t)idx[KPL * h + k] & (uint32_t)(D - 1);
+    addr[k] = 16u * S::VPI * (c >> 3) + 2u * (c & 7u);
+    xk[k] = (float)*reinterpret_cast<const _Float16 *>(vb + addr[k]);
+    amax = fmaxf(amax, fabsf(xk[k]));
+  }
+#pragma unroll
+  for (int hb = 1; hb < S::LPV; hb <<= 1) amax = fmaxf(amax, __shfl_xor(amax, hb * S::VPB));
+  const float scale = amax / 127.f;              // one float32 rounding
+  uint32_t cw[2] = {0u, 0u};                     // the lane's codes, four per word
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) {
+    const double u = (scale > 0.f) ? (double)xk[k] / (double)scale : 0.0;
+    const int c = (int)fmin(fmax(rint(u), -127.0), 127.0);
+    cw[k / 4] |= ((uint32_t)c & 0xFFu) << (8 * (k % 4));
+    *reinterpret_cast<uint16_t *>(vb + addr[k]) = 0;   // the inlier key has the channel zeroed
+  }
+  const __amdgpu_buffer_rsrc_t cr =
+      make_rsrc(st.out_codes + (size_t)pair * capacity * kOutlierCount, (uint32_t)capacity * kOutlierCount);
+  const uint32_t coff = ((uint32_t)(start_pos + t0 + v) * kOutlierCount + KPL * h) | drop;
+  if constexpr (KPL == 8) __builtin_amdgcn_raw_buffer_store_b64((uint2_t){cw[0], cw[1]}, cr, coff, 0, 0);
+  else if constexpr (KPL == 4) __builtin_amdgcn_raw_buffer_store_b32(cw[0], cr, coff, 0, 0);
+  else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)cw[0], cr, coff, 0, 0);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(st.out_scales + (size_t)pair * capacity, (uint32_t)capacity * 4u);
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, scale), sr,
+                                        ((uint32_t)(start_pos + t0 + v) * 4u) | drop | ((uint32_t)-h & kDrop), 0, 0);
+}
+
+template <int D, int FMT, bool OUT>
 __device__ void encode_batch(const StreamArgs &st, const int8_t *signs, const double *mids, int pair, int t0,
-                             int n_new, int capacity, int start_pos, const uint8_t *buf, const uint32_t *masks,
+                             int n_new, int capacity, int start_pos, uint8_t *buf, const uint32_t *masks,
                              const TableEntry *table, float mmax, bool force_exact, uint8_t *scratch, bool issue_next,
                              const StreamArgs &nst, int npair, int nt0, uint8_t *nbuf) {
   using S = Shape<D>;
@@ -321,6 +383,7 @@ __device__ void encode_batch(const StreamArgs &st, const int8_t *signs, const do
   // descriptor's size check), computed without a select the compiler could
   // turn into a branch
   const uint32_t drop = (uint32_t)(n_new - 1 - t) & kDrop;
+  if constexpr (OUT) outlier_batch<D>(st, pair, t0, n_new, capacity, start_pos, buf, drop);
 
   // the lane's fp16 pairs, sign-flipped (mask word e covers coordinates 2e, 2e + 1)
   uint32_t w[CPL / 2];
@@ -496,13 +559,13 @@ __device__ void encode_batch(const StreamArgs &st, const int8_t *signs, const do
   while (todo) {
     const int l = __builtin_ctzll(todo);
     todo &= todo - 1;
-    encode_exact<D, FMT>(st, signs, mids, pair, t0 + l, n_new, capacity, start_pos, scratch);
+    encode_exact<D, FMT, OUT>(st, signs, mids, pair, t0 + l, n_new, capacity, start_pos, scratch);
   }
 }
 
 // One stream (keys or values) per work-group: the batch loop of one format,
 // run by every wave of the work-group over its own batches.
-template <int D, int FMT>
+template <int D, int FMT, bool OUT>
 __device__ void run_stream(const StreamArgs &st, const BulkArgs &A, uint8_t *smem) {
   using S = Shape<D>;
   uint8_t *bufs = smem;                                                    // kWaves * BUF
@@ -543,8 +606,8 @@ __device__ void run_stream(const StreamArgs &st, const BulkArgs &A, uint8_t *sme
     const int npair = next ? nid / chunks : 0;
     const int nt0 = next ? (nid - npair * chunks) * S::VPB : 0;
     __builtin_amdgcn_s_waitcnt(0);          // vmcnt(0): this batch has landed in LDS
-    encode_batch<D, FMT>(st, lsigns, mids, pair, t0, A.n_new, A.capacity, A.start_pos, buf, masks, table, mmax,
-                         force_exact, scratch, next, st, npair, nt0, buf);
+    encode_batch<D, FMT, OUT>(st, lsigns, mids, pair, t0, A.n_new, A.capacity, A.start_pos, buf, masks, table, mmax,
+                              force_exact, scratch, next, st, npair, nt0, buf);
     pair = npair;
     t0 = nt0;
   }
@@ -553,19 +616,21 @@ __device__ void run_stream(const StreamArgs &st, const BulkArgs &A, uint8_t *sme
 template <int D>
 constexpr int kLdsBytes = kWaves * Shape<D>::BUF + kBins * (int)sizeof(TableEntry) + D / 2 * 4 + 16 * 8 + D + kWaves * D;
 
-template <int D, int KF, int VF>
+template <int D, int KF, int VF, bool OUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void append_bulk_kernel(BulkArgs A) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes<D>];
-  if (blockIdx.y == 0) run_stream<D, KF>(A.s[0], A, smem);
-  else run_stream<D, VF>(A.s[1], A, smem);
+  if (blockIdx.y == 0) run_stream<D, KF, OUT>(A.s[0], A, smem);
+  else run_stream<D, VF, false>(A.s[1], A, smem);
 }
 
 template <int D, int KF, int VF>
 hipError_t go(const AppendArgs &a, hipStream_t stream) {
   using S = Shape<D>;
   BulkArgs A;
-  A.s[0] = StreamArgs{static_cast<const uint16_t *>(a.k), a.k_codes, a.k_norms, a.k_centroids};
-  A.s[1] = StreamArgs{static_cast<const uint16_t *>(a.v), a.v_codes, a.v_norms, a.v_centroids};
+  A.s[0] = StreamArgs{static_cast<const uint16_t *>(a.k), a.k_codes, a.k_norms, a.k_centroids, a.outlier_idx,
+                      a.outlier_codes, a.outlier_scales};
+  A.s[1] = StreamArgs{static_cast<const uint16_t *>(a.v), a.v_codes, a.v_norms, a.v_centroids, nullptr, nullptr,
+                      nullptr};
   A.signs = a.signs;
   A.pairs = a.batch * a.kv_heads;
   A.n_new = a.n_new;
@@ -581,7 +646,13 @@ hipError_t go(const AppendArgs &a, hipStream_t stream) {
   // unit), half of them per stream
   const long long total = A.batches_per_stream;
   const int blocks = (int)std::min<long long>((total + kWaves - 1) / kWaves, 2ll * cus);
-  hipLaunchKernelGGL((append_bulk_kernel<D, KF, VF>), dim3(blocks, 2), dim3(kThreads), 0, stream, A);
+  if constexpr (KF != 8) {
+    if (a.outlier_idx) {
+      hipLaunchKernelGGL((append_bulk_kernel<D, KF, VF, true>), dim3(blocks, 2), dim3(kThreads), 0, stream, A);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((append_bulk_kernel<D, KF, VF, false>), dim3(blocks, 2), dim3(kThreads), 0, stream, A);
   return hipGetLastError();
 }
 
@@ -614,7 +685,8 @@ bool bulk_append_supported(const AppendArgs &a) {
   const bool vf = a.v_format >= 2 && a.v_format <= 4;
   const bool kf = (a.k_format >= 2 && a.k_format <= 4) || a.k_format == 8;
   return a.in_f16 && vf && kf && (a.head_dim == 64 || a.head_dim == 128 || a.head_dim == 256) && a.n_new >= 64 &&
-         a.outlier_idx == nullptr && a.qjl_proj == nullptr &&
+         (a.outlier_idx == nullptr || a.k_format != 8) && a.qjl_proj == nullptr &&
+         (long long)a.capacity * kOutlierCount < (1ll << 31) &&
          (long long)a.batch * a.kv_heads * ((a.n_new + 63) / 64) * 2 < (1ll << 31) &&
          (long long)a.capacity * a.head_dim < (1ll << 31);    // one (b, KV head) slice of codes within a buffer descriptor
 }
