@@ -174,7 +174,7 @@ def kernel_source_sha(kernel: str = "attend_pair_kernel") -> str:
 def read_traffic(workload: str, kernel_sha: str):
     """HBM bytes per attention launch from the committed counter summary, or
     None if it is missing or was taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"attend_{workload.replace('@', '_')}_hbm_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"attend_{workload.replace('@', '_').replace('+', '_')}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -451,6 +451,8 @@ def main(argv=None) -> int:
     if args.qjl and wl.k_bits == 8:
         print("--qjl needs Lloyd-Max keys", file=sys.stderr)
         return 2
+    if args.outliers or args.qjl:
+        wl = dataclasses.replace(wl, name=wl.name + ("+outliers" if args.outliers else "") + ("+qjl" if args.qjl else ""))
     variant = args.gate or args.outliers or args.qjl or args.k_bits or args.query_scale != 1.0
     table = []
     if not args.no_table and not variant:
@@ -467,7 +469,7 @@ def main(argv=None) -> int:
             print(f"# table: {label}", file=sys.stderr, flush=True)
             side = argparse.Namespace(**{**vars(plain), **kw})
             base = workload("llama7b_layer")
-            swl = dataclasses.replace(base, k_bits=kbits, name=label) if kbits != base.k_bits else base
+            swl = dataclasses.replace(base, k_bits=kbits, name=label)
             r = measure(swl, side, dev, steps=min(args.steps, 100), reps=args.reps)
             r["workload"] = label
             table.append(r)
