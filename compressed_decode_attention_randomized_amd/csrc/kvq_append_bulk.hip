@@ -227,35 +227,68 @@ __device__ inline void pair_sum_diff(uint32_t w, float &s, float &d) {
 __device__ inline float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
 __device__ inline float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
-// ---- the exact path: one vector in float64, by the whole wave ----
-// (kept out of line: it is rare, and inlined its lane constants would be
-// hoisted out of the batch loop and held in registers the fast path needs)
+// ---- the exact path: flagged vectors in float64, several per wave ----
+// A vector the fast path flags is queued (its input row in a per-wave LDS
+// list) and encoded later in a round of VPE vectors: lane (k, p) holds
+// coordinates 16 p .. 16 p + 15 of queued vector k in float64.  Sums of fp16
+// values are exact in float64 (each is an integer multiple of 2^-24 below
+// 2^16, and D of them stay below 2^53 such units), so the butterflies are
+// exact; the norm's sum of squares and the scaling round only at the level
+// of 1e-16, far inside the 1e-6 window.  Kept out of line: it is rare, and
+// inlined its constants would be hoisted into registers the fast path needs.
+template <int D>
+struct Exact {
+  static constexpr int CPE = 16;             // coordinates per lane
+  static constexpr int LPE = D / CPE;        // lanes per vector
+  static constexpr int VPE = 64 / LPE;       // vectors per round
+  // queue entries: a round's worth less one can wait, plus a whole batch
+  static constexpr int QUEUE = (VPE - 1 + Shape<D>::VPB + 3) & ~3;
+};
+
 template <int D, int FMT, bool OUT>
-__device__ __attribute__((noinline)) void encode_exact(const StreamArgs &st, const int8_t *signs, const double *mids,
-                                                       int pair, int t, int n_new, int capacity, int start_pos,
-                                                       uint8_t *scratch) {
-  using S = Shape<D>;
-  constexpr int E = S::EPL;
+__device__ __attribute__((noinline)) void exact_round(const uint16_t *in, uint8_t *codes, uint16_t *norms,
+                                                      const int32_t *out_idx, const int8_t *signs, const double *mids,
+                                                      const uint32_t *queue, int nvec, int n_new, int capacity,
+                                                      int start_pos) {
+  using E = Exact<D>;
+  constexpr int C = E::CPE;
   const int lane = threadIdx.x & 63;
-  const uint16_t *src = st.in + ((size_t)pair * n_new + t) * D + lane * E;
-  double x[E];
+  const int k = lane / E::LPE, p = lane % E::LPE;
+  const bool active = k < nvec;
+  const uint32_t id = queue[active ? k : 0];                 // input row: pair * n_new + t
+  const int pair = (int)(id / (uint32_t)n_new);
+  const int t = (int)id - pair * n_new;
+  const uint4 *src = reinterpret_cast<const uint4 *>(in + (size_t)id * D + C * p);
+  const uint4 w0 = src[0], w1 = src[1];
+  const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  const uint4 sg = *reinterpret_cast<const uint4 *>(signs + C * p);
+  const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
+  int32_t oidx[OUT ? kOutlierCount : 1];
+  if constexpr (OUT) {
+#pragma unroll
+    for (int q = 0; q < kOutlierCount; ++q) oidx[q] = out_idx[(size_t)pair * kOutlierCount + q];
+  }
+  double x[C];
   double ss = 0.0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    double v = (double)(float)__builtin_bit_cast(_Float16, src[e]);
+  for (int e = 0; e < C; ++e) {
+    const uint32_t bits = (wd[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+    double v = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)bits);
     if constexpr (OUT) {
       // the outlier channels are zero in the inlier key
 #pragma unroll
-      for (int k = 0; k < kOutlierCount; ++k) v = (st.out_idx[pair * kOutlierCount + k] == lane * E + e) ? 0.0 : v;
+      for (int q = 0; q < kOutlierCount; ++q) v = (oidx[q] == C * p + e) ? 0.0 : v;
     }
     ss = fma(v, v, ss);
-    x[e] = signs[lane * E + e] < 0 ? -v : v;
+    const bool neg = ((sw[e / 4] >> (8 * (e % 4))) & 0x80u) != 0u;
+    x[e] = neg ? -v : v;
   }
-  // butterflies inside the lane, then across lanes (coordinate lane*E + e)
+  // butterflies inside the lane (coordinate bits 0-3), then across the
+  // vector's lanes (coordinate bit 4 + log2 m pairs lanes p and p ^ m)
 #pragma unroll
-  for (int h = 1; h < E; h <<= 1) {
+  for (int h = 1; h < C; h <<= 1) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
+    for (int e = 0; e < C; ++e) {
       if (!(e & h)) {
         const double a = x[e], b = x[e + h];
         x[e] = a + b;
@@ -264,62 +297,62 @@ __device__ __attribute__((noinline)) void encode_exact(const StreamArgs &st, con
     }
   }
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
+  for (int m = 1; m < E::LPE; m <<= 1) {
+    const bool upper = (p & m) != 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
+    for (int e = 0; e < C; ++e) {
       const double o = __shfl_xor(x[e], m);
       x[e] = upper ? o - x[e] : x[e] + o;
     }
+    ss += __shfl_xor(ss, m);
   }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
   const size_t slot = (size_t)pair * capacity + start_pos + t;
   constexpr int ROW = FMT == 8 ? D : D * FMT / 8;
-  uint8_t *row = st.codes + slot * ROW;
+  uint8_t *row = codes + slot * ROW;
   if constexpr (FMT == 8) {
     const double rs = 1.0 / sqrt((double)D);
+    uint32_t cw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
+    for (int e = 0; e < C; ++e) {
       // y rounded once to fp32, then to E4M3 (the two roundings can differ
       // from one only within 2^-24 |y| of an E4M3 midpoint: inside the window)
       const float y = fminf(fmaxf((float)(x[e] * rs), -448.f), 448.f);
-      scratch[lane * E + e] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFF);
+      const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFFu;
+      cw[e / 4] |= c << (8 * (e % 4));
     }
+    if (active) *reinterpret_cast<uint4 *>(row + C * p) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
   } else {
     constexpr int L = 1 << FMT;
     const uint16_t n16 = norm_fp16(ss);
-    if (lane == 0) st.norms[slot] = n16;
+    if (active && p == 0) norms[slot] = n16;
+    const double inv = ss > 0.0 ? 1.0 / sqrt((double)D * ss) : 0.0;
+    uint32_t cw[2] = {0u, 0u};                              // 16 codes, LSB first
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
+    for (int e = 0; e < C; ++e) {
       uint32_t code = L / 2;
       if (ss > 0.0) {
-        const double u = x[e] / sqrt((double)D * ss);
+        // number of midpoints at or below u, by binary search over the
+        // ascending midpoints
+        const double u = x[e] * inv;
         code = 0;
 #pragma unroll
-        for (int i = 0; i + 1 < L; ++i) code += (u >= mids[i]) ? 1u : 0u;
+        for (int step = L / 2; step >= 1; step >>= 1) code += (u >= mids[code + step - 1]) ? (uint32_t)step : 0u;
       }
-      scratch[lane * E + e] = (uint8_t)code;
+      const int bit = FMT * e;
+      cw[bit / 32] |= code << (bit % 32);
+      if ((bit % 32) + FMT > 32) cw[bit / 32 + 1] |= code >> (32 - bit % 32);
+    }
+    if (active) {
+      uint8_t *dst = row + 2 * FMT * p;                    // 16 codes = 2 FMT bytes
+      if constexpr (FMT == 4) *reinterpret_cast<uint2 *>(dst) = make_uint2(cw[0], cw[1]);
+      else if constexpr (FMT == 2) *reinterpret_cast<uint32_t *>(dst) = cw[0];
+      else {
+        reinterpret_cast<uint16_t *>(dst)[0] = (uint16_t)(cw[0] & 0xFFFFu);
+        reinterpret_cast<uint16_t *>(dst)[1] = (uint16_t)(cw[0] >> 16);
+        reinterpret_cast<uint16_t *>(dst)[2] = (uint16_t)(cw[1] & 0xFFFFu);
+      }
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // pack: dword w of the row holds stream bits [32 w, 32 w + 32)
-  constexpr int B = FMT == 8 ? 8 : FMT;
-  if (lane < ROW / 4) {
-    uint32_t word = 0;
-    const int j0 = (32 * lane) / B;
-    for (int j = j0; j < D && j * B < 32 * lane + 32; ++j) {
-      const int bit = j * B - 32 * lane;
-      const uint32_t c = scratch[j];
-      word |= bit >= 0 ? (c << bit) : (c >> (-bit));
-    }
-    reinterpret_cast<uint32_t *>(row)[lane] = word;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ---- the fast path: one batch of one stream ----
@@ -370,7 +403,8 @@ __device__ inline void outlier_batch(const StreamArgs &st, int pair, int t0, int
 template <int D, int FMT, bool OUT>
 __device__ void encode_batch(const StreamArgs &st, const int8_t *signs, const double *mids, int pair, int t0,
                              int n_new, int capacity, int start_pos, uint8_t *buf, const uint32_t *masks,
-                             const TableEntry *table, float mmax, bool force_exact, uint8_t *scratch, bool issue_next,
+                             const TableEntry *table, float mmax, bool force_exact, uint32_t *queue, int &count,
+                             bool issue_next,
                              const StreamArgs &nst, int npair, int nt0, uint8_t *nbuf) {
   using S = Shape<D>;
   constexpr int CPL = S::CPL;
@@ -554,12 +588,14 @@ __device__ void encode_batch(const StreamArgs &st, const int8_t *signs, const do
       }
     }
   }
-  // the exact path for the flagged vectors of the batch, one at a time
-  uint64_t todo = __ballot(valid && near && h == 0);
-  while (todo) {
-    const int l = __builtin_ctzll(todo);
-    todo &= todo - 1;
-    encode_exact<D, FMT, OUT>(st, signs, mids, pair, t0 + l, n_new, capacity, start_pos, scratch);
+  // flagged vectors join the wave's queue for the exact path
+  const bool queued = valid && near && h == 0;
+  const uint64_t flagged = __ballot(queued);
+  if (flagged) {
+    const uint32_t rank =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(flagged >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)flagged, 0u));
+    if (queued) queue[count + (int)rank] = (uint32_t)(pair * n_new + t);
+    count += __popcll(flagged);
   }
 }
 
@@ -573,11 +609,12 @@ __device__ void run_stream(const StreamArgs &st, const BulkArgs &A, uint8_t *sme
   uint32_t *masks = reinterpret_cast<uint32_t *>(table + kBins);          // D / 2 words
   double *mids = reinterpret_cast<double *>(masks + D / 2);               // float64 decision midpoints
   int8_t *lsigns = reinterpret_cast<int8_t *>(mids + 16);                  // D signs
-  uint8_t *scr = reinterpret_cast<uint8_t *>(lsigns + D);                 // kWaves * D bytes
+  uint32_t *queues = reinterpret_cast<uint32_t *>(lsigns + D);           // kWaves * QUEUE entries
 
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // uniform: batch math in SGPRs
   uint8_t *buf = bufs + wave * S::BUF;
-  uint8_t *scratch = scr + wave * D;
+  uint32_t *queue = queues + wave * Exact<D>::QUEUE;
+  int count = 0;                            // wave-uniform: entries waiting in the queue
   const int chunks = (A.n_new + S::VPB - 1) / S::VPB;
   const int total = A.batches_per_stream;
   const int gw = blockIdx.x * kWaves + wave, nw = gridDim.x * kWaves;
@@ -607,14 +644,32 @@ __device__ void run_stream(const StreamArgs &st, const BulkArgs &A, uint8_t *sme
     const int nt0 = next ? (nid - npair * chunks) * S::VPB : 0;
     __builtin_amdgcn_s_waitcnt(0);          // vmcnt(0): this batch has landed in LDS
     encode_batch<D, FMT, OUT>(st, lsigns, mids, pair, t0, A.n_new, A.capacity, A.start_pos, buf, masks, table, mmax,
-                              force_exact, scratch, next, st, npair, nt0, buf);
+                              force_exact, queue, count, next, st, npair, nt0, buf);
+    // a full round of queued vectors goes through the exact path (the queue
+    // entries were written by other lanes of this wave)
+    while (count >= Exact<D>::VPE) {
+      count -= Exact<D>::VPE;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      exact_round<D, FMT, OUT>(st.in, st.codes, st.norms, st.out_idx, lsigns, mids, queue + count, Exact<D>::VPE,
+                               A.n_new, A.capacity, A.start_pos);
+    }
     pair = npair;
     t0 = nt0;
+  }
+  if (count > 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    exact_round<D, FMT, OUT>(st.in, st.codes, st.norms, st.out_idx, lsigns, mids, queue, count, A.n_new, A.capacity,
+                             A.start_pos);
   }
 }
 
 template <int D>
-constexpr int kLdsBytes = kWaves * Shape<D>::BUF + kBins * (int)sizeof(TableEntry) + D / 2 * 4 + 16 * 8 + D + kWaves * D;
+constexpr int kLdsBytes = kWaves * Shape<D>::BUF + kBins * (int)sizeof(TableEntry) + D / 2 * 4 + 16 * 8 + D +
+                          kWaves * Exact<D>::QUEUE * 4;
 
 template <int D, int KF, int VF, bool OUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void append_bulk_kernel(BulkArgs A) {
@@ -687,6 +742,7 @@ bool bulk_append_supported(const AppendArgs &a) {
   return a.in_f16 && vf && kf && (a.head_dim == 64 || a.head_dim == 128 || a.head_dim == 256) && a.n_new >= 64 &&
          (a.outlier_idx == nullptr || a.k_format != 8) && a.qjl_proj == nullptr &&
          (long long)a.capacity * kOutlierCount < (1ll << 31) &&
+         (long long)a.batch * a.kv_heads * a.n_new < (1ll << 31) &&     // exact-path queue entries: input rows
          (long long)a.batch * a.kv_heads * ((a.n_new + 63) / 64) * 2 < (1ll << 31) &&
          (long long)a.capacity * a.head_dim < (1ll << 31);    // one (b, KV head) slice of codes within a buffer descriptor
 }
