@@ -245,11 +245,32 @@ struct Exact {
   static constexpr int QUEUE = (VPE - 1 + Shape<D>::VPB + 3) & ~3;
 };
 
+// v from lane ^ m, for m < 32: row-local DPP moves for m = 1, 2, ds_swizzle
+// in xor mode above (no LDS access, no address registers).
+__device__ inline uint32_t xor_lane_u32(uint32_t v, int m) {
+  const int x = (int)v;
+  if (m == 1) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);     // quad_perm [1,0,3,2]
+  if (m == 2) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);     // quad_perm [2,3,0,1]
+  if (m == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x101F);
+  if (m == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x201F);
+  return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x401F);
+}
+
+__device__ inline double xor_lane(double v, int m) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = xor_lane_u32((uint32_t)b, m), hi = xor_lane_u32((uint32_t)(b >> 32), m);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 template <int D, int FMT, bool OUT>
 __device__ __attribute__((noinline)) void exact_round(const uint16_t *in, uint8_t *codes, uint16_t *norms,
-                                                      const int32_t *out_idx, const int8_t *signs, const double *mids,
-                                                      const uint32_t *queue, int nvec, int n_new, int capacity,
-                                                      int start_pos) {
+                                                      const int32_t *out_idx, const int8_t *signs_g,
+                                                      const double *mids_g, const uint32_t *queue_g, int nvec,
+                                                      int n_new, int capacity, int start_pos) {
+  // the sign, midpoint and queue arrays live in LDS
+  const auto *signs = (const __attribute__((address_space(3))) int8_t *)signs_g;
+  const auto *mids = (const __attribute__((address_space(3))) double *)mids_g;
+  const auto *queue = (const __attribute__((address_space(3))) uint32_t *)queue_g;
   using E = Exact<D>;
   constexpr int C = E::CPE;
   const int lane = threadIdx.x & 63;
@@ -261,8 +282,8 @@ __device__ __attribute__((noinline)) void exact_round(const uint16_t *in, uint8_
   const uint4 *src = reinterpret_cast<const uint4 *>(in + (size_t)id * D + C * p);
   const uint4 w0 = src[0], w1 = src[1];
   const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-  const uint4 sg = *reinterpret_cast<const uint4 *>(signs + C * p);
-  const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
+  const auto *sp = (const __attribute__((address_space(3))) uint32_t *)(signs + C * p);
+  const uint32_t sw[4] = {sp[0], sp[1], sp[2], sp[3]};
   int32_t oidx[OUT ? kOutlierCount : 1];
   if constexpr (OUT) {
 #pragma unroll
@@ -301,10 +322,10 @@ __device__ __attribute__((noinline)) void exact_round(const uint16_t *in, uint8_
     const bool upper = (p & m) != 0;
 #pragma unroll
     for (int e = 0; e < C; ++e) {
-      const double o = __shfl_xor(x[e], m);
+      const double o = xor_lane(x[e], m);
       x[e] = upper ? o - x[e] : x[e] + o;
     }
-    ss += __shfl_xor(ss, m);
+    ss += xor_lane(ss, m);
   }
   const size_t slot = (size_t)pair * capacity + start_pos + t;
   constexpr int ROW = FMT == 8 ? D : D * FMT / 8;
@@ -329,15 +350,13 @@ __device__ __attribute__((noinline)) void exact_round(const uint16_t *in, uint8_
     uint32_t cw[2] = {0u, 0u};                              // 16 codes, LSB first
 #pragma unroll
     for (int e = 0; e < C; ++e) {
-      uint32_t code = L / 2;
-      if (ss > 0.0) {
-        // number of midpoints at or below u, by binary search over the
-        // ascending midpoints
-        const double u = x[e] * inv;
-        code = 0;
+      // number of midpoints at or below u, by binary search over the
+      // ascending midpoints; a zero vector takes the middle code
+      const double u = x[e] * inv;
+      uint32_t code = 0;
 #pragma unroll
-        for (int step = L / 2; step >= 1; step >>= 1) code += (u >= mids[code + step - 1]) ? (uint32_t)step : 0u;
-      }
+      for (int step = L / 2; step >= 1; step >>= 1) code += (u >= mids[code + step - 1]) ? (uint32_t)step : 0u;
+      code = ss > 0.0 ? code : (uint32_t)(L / 2);
       const int bit = FMT * e;
       cw[bit / 32] |= code << (bit % 32);
       if ((bit % 32) + FMT > 32) cw[bit / 32 + 1] |= code >> (32 - bit % 32);
@@ -658,13 +677,27 @@ __device__ void run_stream(const StreamArgs &st, const BulkArgs &A, uint8_t *sme
     pair = npair;
     t0 = nt0;
   }
-  if (count > 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    exact_round<D, FMT, OUT>(st.in, st.codes, st.norms, st.out_idx, lsigns, mids, queue, count, A.n_new, A.capacity,
-                             A.start_pos);
+  // What is left in the waves' queues is pooled over the work-group (the
+  // staging buffers are free once every batch is done) and shared out in
+  // full rounds: every wave running its own, mostly empty, round at the end
+  // of the launch would cost more than the rounds the launch needs.
+  __shared__ int left[kWaves];
+  const int lane = threadIdx.x & 63;
+  if (lane == 0) left[wave] = count;
+  __syncthreads();
+  int base = 0, pooled = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = left[w];
+    base += w < wave ? c : 0;
+    pooled += c;
   }
+  uint32_t *pool = reinterpret_cast<uint32_t *>(bufs);
+  for (int j = lane; j < count; j += 64) pool[base + j] = queue[j];
+  __syncthreads();
+  for (int r = wave * Exact<D>::VPE; r < pooled; r += kWaves * Exact<D>::VPE)
+    exact_round<D, FMT, OUT>(st.in, st.codes, st.norms, st.out_idx, lsigns, mids, pool + r,
+                             min(Exact<D>::VPE, pooled - r), A.n_new, A.capacity, A.start_pos);
 }
 
 template <int D>
