@@ -518,6 +518,69 @@ __device__ void first_block(Tier &X, int t0, int t1) {
   if (t0 < t1) X.load(t < t1 ? t : t0, lane % LPT);
 }
 
+// Spike flags of one block: head h's bit of each of the wave's TPW tokens
+// (tw its first) whose score is above fg.spike[h], or-ed into the head's
+// flag words.
+template <int G, int LPT>
+__device__ inline void spike_flags(const FarGate<G> &fg, const float (&s)[G], int tw, int ds, int lane) {
+  constexpr int TPW = 64 / LPT;
+  if (!fg.bits) return;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint64_t ball = __builtin_amdgcn_ballot_w64(ds == 0 && s[h] > fg.spike[h]);
+    uint32_t m = 0u;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) m |= (uint32_t)((ball >> (k * LPT)) & 1ull) << k;
+    if (m != 0u && lane == 0) atomicOr(fg.bits + (size_t)h * fg.words + (tw >> 5), m << (tw & 31));
+  }
+}
+
+// Gated pass while nothing is gated: the ungated loop's schedule (a block's
+// key and value rows requested together, one block ahead of its
+// arithmetic), with the gate applied to the weights and the spike flags
+// set.  A wave leaves it after the first block in which some lane slot's
+// token is gated for every head, and returns where the rest of its range
+// starts (t1 if it got through): from there token_loop_gated requests only
+// the value rows some head keeps.  A pass that gates nothing so streams
+// like the ungated one.
+template <int G, int DPL, int LPT, typename Tier>
+__device__ int token_loop_spec(Tier &cur, const float (&qr)[G][DPL], State<G, DPL> &st, int t0, int t1,
+                               const FarGate<G> &fg) {
+  constexpr int TPW = 64 / LPT;
+  constexpr int TPB = TPW * kWaves;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ds = lane % LPT, ts = lane / LPT;
+  int t = t0 + wave * TPW + ts;
+  for (int base = t0; base < t1; base += TPB) {
+    const bool valid = t < t1;
+    const int tn = t + TPB;
+    Tier nxt = cur;
+    nxt.load(tn < t1 ? tn : t0, ds);
+    float part[G];
+    cur.score(qr, part);
+#pragma unroll
+    for (int h = 0; h < G; ++h) part[h] = lane_sum<LPT>(part[h]);
+    float s[G], p[G];
+    const float ks = cur.key_scale();
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
+    spike_flags<G, LPT>(fg, s, t - ts, ds, lane);
+    st.add_scores(s, p);
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const bool keep = s[h] >= fg.gate[h];
+      p[h] = keep ? p[h] : 0.f;
+      any = any || keep;
+    }
+    cur.accumulate(p, st);
+    cur = nxt;
+    t = tn;
+    if (__builtin_amdgcn_ballot_w64(valid && !any) != 0ull) return base + TPB;
+  }
+  return t1;
+}
+
 // Far-tier loop with the score gate and spike flags.  A token whose score is
 // below fg.gate[h] keeps its weight in l but adds nothing to head h's
 // values; a lane slot whose token every head gates does not even load its
@@ -551,17 +614,7 @@ __device__ void token_loop_gated(const Tier &proto, const float (&qr)[G][DPL], S
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = valid ? part[h] * ks : -INFINITY;
     if (vy) Y.accumulate(py, st);
-    if (fg.bits) {
-      const int tw = t - ts;                       // the wave's first token of the block
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint64_t ball = __builtin_amdgcn_ballot_w64(ds == 0 && s[h] > fg.spike[h]);
-        uint32_t m = 0u;
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) m |= (uint32_t)((ball >> (k * LPT)) & 1ull) << k;
-        if (m != 0u && lane == 0) atomicOr(fg.bits + (size_t)h * fg.words + (tw >> 5), m << (tw & 31));
-      }
-    }
+    spike_flags<G, LPT>(fg, s, t - ts, ds, lane);
     st.add_scores(s, px);
     bool any = false;
 #pragma unroll
@@ -786,7 +839,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     tier.zs0 = P.qjl_signs + (size_t)bh * P.capacity * (D / 8);
     tier.zn0 = P.qjl_norms + (size_t)bh * P.capacity;
   }
-  if constexpr (!GATED) first_block<LPTF>(tier, t0, t1);
+  first_block<LPTF>(tier, t0, t1);
 
   // ---- rotated query into LDS, centroid tables ----
   query_rows<D, G>(P, b, hkv, true, qs);
@@ -922,7 +975,8 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
     }
     fg.bits = P.spike_ref ? P.spike_bits + row0 * P.spike_words : nullptr;
     fg.words = P.spike_words;
-    token_loop_gated<G, DPLF, LPTF>(tier, qr, st, t0, t1, fg);
+    const int resume = token_loop_spec<G, DPLF, LPTF>(tier, qr, st, t0, t1, fg);
+    if (resume < t1) token_loop_gated<G, DPLF, LPTF>(tier, qr, st, resume, t1, fg);
   } else {
     token_loop<G, DPLF, LPTF>(tier, qr, st, t0, t1);
   }

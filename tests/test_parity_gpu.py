@@ -440,6 +440,14 @@ def test_score_gate_and_spike_flags(dev, name, hq, kv, d):
     plain = O.two_tier_attention(q64, kn.astype(np.float64), vn.astype(np.float64), k_rot, v_rot, s)
     assert np.abs(plain - ref2).max() > 5 * ATOL
     _rows_close(f"{name} hard gate", out2.cpu().numpy(), ref2)
+    # A reference 1000 below the top score gates nothing: the kernel then
+    # requests value rows together with the keys for the whole pass, and the
+    # result is plain attention.
+    none = (top - 1000.0).astype(np.float32)
+    part_o, part_ml = cache.attend(q, T, wl.splits, SN, gate_ref=_t(none, dev))
+    out3 = cache.merge(part_o, part_ml, wl.splits, SN)
+    torch.cuda.synchronize()
+    _rows_close(f"{name} no gated token", out3.cpu().numpy(), plain)
 
     want = O.spike_flags(q64, k_rot, s, spike.astype(np.float64))
     got_words = words.cpu().numpy().view(np.uint32)
