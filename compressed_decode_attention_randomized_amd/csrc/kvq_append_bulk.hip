@@ -131,13 +131,24 @@ __device__ inline uint16_t norm_fp16(double S) {
   return (uint16_t)h;
 }
 
-// True when S lies within rel * S of the squared midpoint on either side of
-// the fp16 value h (the rounding of sqrt(S) could go either way there).
-__device__ inline bool norm_near(double S, uint16_t h, double rel) {
-  if (h == 0 || h >= 0x7C00u) return true;
-  const double v = half_value(h);
-  const double lo = 0.5 * (half_value(h - 1u) + v), hi = 0.5 * (v + half_value(h + 1u));
-  return fabs(S - lo * lo) <= rel * S || fabs(S - hi * hi) <= rel * S;
+// The fast path's fp16 norm, in fp32: RNE_fp16 of n = sqrt(S) (v_sqrt_f32,
+// within 1 ulp) for an fp32 S whose relative error is at most eps, and
+// whether the exact root could lie on the other side of one of the two
+// rounding midpoints around that fp16 value: n within (eps/2 + 3u) n of one
+// (the root halves S's relative error, v_sqrt_f32 adds at most 2u, the
+// distance one more), with a quarter of headroom.  The midpoints of two
+// adjacent fp16 values are exact in fp32.  Zero, subnormal-rounded and
+// overflowing results are flagged too.
+__device__ inline float half_f(uint32_t bits) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits); }
+
+__device__ inline uint16_t norm_fp16_fast(float S, float eps, bool &near) {
+  const float n = __builtin_amdgcn_sqrtf(S);
+  const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)n);
+  const float v = half_f(h);
+  const float mlo = 0.5f * (half_f(h - 1u) + v), mhi = 0.5f * (v + half_f(h + 1u));
+  const float d = fminf(fabsf(n - mlo), fabsf(n - mhi));
+  near = near || h == 0u || h >= 0x7BFFu || !(d > 1.25f * (0.5f * eps + 3.f * kU) * n);
+  return (uint16_t)h;
 }
 
 // ---- the code table of one Lloyd-Max stream (t = z / ||x||, N(0,1) scale) ----
@@ -548,10 +559,7 @@ __device__ void encode_batch(const StreamArgs &st, const int8_t *signs, const do
     const float r = __builtin_amdgcn_rsqf(ss);
     const float rb = r * kBinScale;
     const float margin = 1.25f * kU * ((float)S::STAGES * sqrtf((float)D) + ((float)CPL / 16.f + 6.f) * mmax) + 1e-7f;
-    const double Sd = (double)ss;
-    const uint16_t n16 = norm_fp16(Sd);
-    near |= norm_near(Sd, n16, (double)((CPL / 8 + 6) * kU) * 1.25);
-    nstore = n16;
+    nstore = norm_fp16_fast(ss, (float)(CPL / 8 + 6) * kU, near);
     float nmin = INFINITY;                  // smallest |t - midpoint| over the lane's codes
     // 16 coordinates at a time (bounds the table reads in flight)
 #pragma unroll
