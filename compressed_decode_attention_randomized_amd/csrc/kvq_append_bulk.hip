@@ -274,10 +274,9 @@ __device__ inline double xor_lane(double v, int m) {
 }
 
 template <int D, int FMT, bool OUT>
-__device__ __attribute__((noinline)) void exact_round(const uint16_t *in, uint8_t *codes, uint16_t *norms,
-                                                      const int32_t *out_idx, const int8_t *signs_g,
-                                                      const double *mids_g, const uint32_t *queue_g, int nvec,
-                                                      int n_new, int capacity, int start_pos) {
+__device__ __attribute__((always_inline)) inline void exact_round_body(
+    const uint16_t *in, uint8_t *codes, uint16_t *norms, const int32_t *out_idx, const int8_t *signs_g,
+    const double *mids_g, const uint32_t *queue_g, int nvec, int n_new, int capacity, int start_pos) {
   // the sign, midpoint and queue arrays live in LDS
   const auto *signs = (const __attribute__((address_space(3))) int8_t *)signs_g;
   const auto *mids = (const __attribute__((address_space(3))) double *)mids_g;
@@ -383,6 +382,19 @@ __device__ __attribute__((noinline)) void exact_round(const uint16_t *in, uint8_
       }
     }
   }
+}
+
+// Out of line for the rounds inside the batch loop (inlined there, its
+// constants would be hoisted out of the loop into registers the fast path
+// needs); the end-of-launch rounds take the body inline, which spares the
+// call's register saves to scratch memory on the launch's critical path.
+template <int D, int FMT, bool OUT>
+__device__ __attribute__((noinline)) void exact_round(const uint16_t *in, uint8_t *codes, uint16_t *norms,
+                                                      const int32_t *out_idx, const int8_t *signs_g,
+                                                      const double *mids_g, const uint32_t *queue_g, int nvec,
+                                                      int n_new, int capacity, int start_pos) {
+  exact_round_body<D, FMT, OUT>(in, codes, norms, out_idx, signs_g, mids_g, queue_g, nvec, n_new, capacity,
+                                start_pos);
 }
 
 // ---- the fast path: one batch of one stream ----
@@ -704,8 +716,8 @@ __device__ void run_stream(const StreamArgs &st, const BulkArgs &A, uint8_t *sme
   for (int j = lane; j < count; j += 64) pool[base + j] = queue[j];
   __syncthreads();
   for (int r = wave * Exact<D>::VPE; r < pooled; r += kWaves * Exact<D>::VPE)
-    exact_round<D, FMT, OUT>(st.in, st.codes, st.norms, st.out_idx, lsigns, mids, pool + r,
-                             min(Exact<D>::VPE, pooled - r), A.n_new, A.capacity, A.start_pos);
+    exact_round_body<D, FMT, OUT>(st.in, st.codes, st.norms, st.out_idx, lsigns, mids, pool + r,
+                                  min(Exact<D>::VPE, pooled - r), A.n_new, A.capacity, A.start_pos);
 }
 
 template <int D>
