@@ -211,6 +211,10 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t q
  *   spike_bits  device uint32 [batch][q_heads][ceil(seq_len / 32)], zeroed by
  *               the caller before the call (bits are or-ed in); required
  *               exactly when spike_ref is given.
+ * The results do not depend on how rows are fetched; for speed, each wave
+ * requests value rows together with the keys until a block of its tokens
+ * has one gated for every head, and from then on skips the value rows of
+ * such tokens, so a pass that gates nothing costs about an ungated one.
  * At least one of gate_ref and spike_ref must be given.  All three are
  * caller-owned and 4-byte aligned.  Caches with an outlier stream or a QJL
  * sketch are not served (KVQ_EUNSUPPORTED).  Served by the VALU kernel for every
