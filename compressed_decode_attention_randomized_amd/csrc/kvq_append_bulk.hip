@@ -26,11 +26,14 @@
 //     clamped coordinate;
 //   * each result carries a rigorous bound on its fp32 error (transform
 //     rounding <= stages * 2^-24 * sum|x| <= stages * 2^-24 * sqrt(D) ||x||,
-//     the norm's and the scaling's roundings); a vector with any code, or its
-//     fp16 norm, within that bound of a decision is recomputed by the whole
-//     wave in float64 (2-4 coordinates per lane, butterflies across lanes by
-//     shuffles), so codes and norms equal the exact encoding everywhere
-//     outside the 1e-6 window of the parity contract;
+//     the norm's and the scaling's roundings; the fp16 norm is decided in
+//     fp32 against the rounding midpoints around it); a vector with any
+//     code, or its fp16 norm, within that bound of a decision is queued and
+//     recomputed in float64 with other queued vectors of the wave (16
+//     coordinates per lane, butterflies across lanes by DPP moves and
+//     ds_swizzle; what is left at the end is pooled over the work-group), so
+//     codes and norms equal the exact encoding everywhere outside the 1e-6
+//     window of the parity contract;
 //   * a key outlier stream ("Outlier Two-Stream Cache") is taken from the
 //     staged rows before the lanes read them: each lane reads its share of
 //     the vector's 8 channels, the vector's lanes reduce the largest
