@@ -87,6 +87,28 @@ __device__ inline uint32_t e4m3_from_double(double y) {
   return sign | code;
 }
 
+// v from lane ^ m (m < 32, within a vector's lanes): row-local DPP moves for
+// m = 1, 2 and ds_swizzle in xor mode above (no LDS access, no address
+// registers, shorter latency than a ds_bpermute shuffle).
+__device__ inline uint32_t swap_xor_u32(uint32_t v, int m) {
+  const int x = (int)v;
+  if (m == 1) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);     // quad_perm [1,0,3,2]
+  if (m == 2) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);     // quad_perm [2,3,0,1]
+  if (m == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x101F);
+  if (m == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x201F);
+  return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x401F);
+}
+
+__device__ inline float swap_xor(float v, int m) {
+  return __builtin_bit_cast(float, swap_xor_u32(__builtin_bit_cast(uint32_t, v), m));
+}
+
+__device__ inline double swap_xor(double v, int m) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = swap_xor_u32((uint32_t)b, m), hi = swap_xor_u32((uint32_t)(b >> 32), m);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 template <typename T>
 __device__ inline void load8(const T *p, double (&x)[8]);
 
@@ -181,7 +203,7 @@ __device__ void encode(const Stream &st, const int8_t *__restrict__ signs, int n
       if (which[e] >= 0) amax = fmaxf(amax, fabsf((float)x[e]));
     }
 #pragma unroll
-    for (int m = 1; m < LPV; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    for (int m = 1; m < LPV; m <<= 1) amax = fmaxf(amax, swap_xor(amax, m));
     const float scale = amax / 127.f;               // one float32 rounding
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -226,12 +248,12 @@ __device__ void encode(const Stream &st, const int8_t *__restrict__ signs, int n
     const bool upper = (lv & m) != 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double o = __shfl_xor(x[e], m);
+      const double o = swap_xor(x[e], m);
       x[e] = upper ? (o - x[e]) : (x[e] + o);
     }
   }
 #pragma unroll
-  for (int m = 1; m < LPV; m <<= 1) ss += __shfl_xor(ss, m);
+  for (int m = 1; m < LPV; m <<= 1) ss += swap_xor(ss, m);
 
   uint8_t *row = st.codes + slot * ROW;
 
@@ -292,7 +314,7 @@ __device__ void encode(const Stream &st, const int8_t *__restrict__ signs, int n
       resid[(lv * 8 + e) * VPB + vloc] = r;
     }
 #pragma unroll
-    for (int m = 1; m < LPV; m <<= 1) rss += __shfl_xor(rss, m);
+    for (int m = 1; m < LPV; m <<= 1) rss += swap_xor(rss, m);
     if (lv == 0) st.qjl_norms[slot] = fp16_norm(rss);
   }
 }
