@@ -115,7 +115,7 @@ WORKLOADS = {
                              splits=64, lognormal_sigma=1.0),
     "bitwidth_sweep": Workload("bitwidth_sweep", 4, batch=32, q_heads=16, kv_heads=16,
                                head_dim=256, seq_len=4096, k_bits=4, v_bits=4, dtype="f16",
-                               splits=4, outlier_channels=8, outlier_scale=10.0),
+                               splits=2, outlier_channels=8, outlier_scale=10.0),
     "two_tier": Workload("two_tier", 5, batch=16, q_heads=16, kv_heads=16, head_dim=128,
                          seq_len=16384, k_bits=8, v_bits=4, dtype="f16", splits=18,
                          near_fraction=0.1, near_splits=5),
