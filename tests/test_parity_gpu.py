@@ -981,3 +981,15 @@ def test_full_size_gate(dev):
         got = ((all_words[b, h][:, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(-1)[:T].astype(bool)
         near_thr = np.abs(sf[0, 0] - spike64[b, h]) <= 1e-3
         assert not ((got != want) & ~near_thr).any() and got.any()
+    # the unpeaked query against its own log-sum-exp gates nothing: the whole
+    # pass stays on the schedule that requests value rows with the keys, and
+    # equals the ungated decode
+    q1 = _t(inp.q, dev)
+    lse1 = torch.empty_like(lse)
+    plain = cache.decode(q1, T, wl.splits, SN, lse=lse1)
+    words.zero_()
+    po, pml = cache.attend(q1, T, wl.splits, SN, gate_ref=lse1, spike_ref=lse1 - 4.0, spike_bits=words)
+    gated = cache.merge(po, pml, wl.splits, SN)
+    torch.cuda.synchronize()
+    diff = (gated - plain).abs().max().item()
+    assert diff <= 1e-5, f"nothing gated: gated pass differs from the ungated decode by {diff:.3e}"
