@@ -763,8 +763,10 @@ __device__ void write_split(const Params &P, State<G, DPL> &st, int b, int hkv, 
 // NEAR: the launch has near-tier splits (without them the kernel carries no
 // registers for the near path).
 // GATED: score gate and spike flags; X: key side stream (none, outliers, QJL).
-template <int D, int KB, int VB, int G, bool NEAR, bool GATED, int X = kNoExtra>
-__global__ __launch_bounds__(kBlock) void attend_kernel(Params P) {
+// WPE: waves per SIMD the register allocation must leave room for (1: no
+// constraint).
+template <int D, int KB, int VB, int G, bool NEAR, bool GATED, int X = kNoExtra, int WPE = 1>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE))) void attend_kernel(Params P) {
   constexpr bool OUT = X == kOutliers, QJL = X == kQjl;
   // Coordinates per lane.  G = 1 without a near tier: 32 (two 16-byte fp8
   // or 32-bit-code slices per token, half the per-token softmax lanes of
@@ -1006,8 +1008,15 @@ hipError_t go(const AttendArgs &a, hipStream_t stream) {
       return hipGetLastError();
     }
   }
+  // G = 1 with a near tier (8 or 16 coordinates per lane), ungated, fits six
+  // waves per SIMD in 80 registers without spilling (two_tier 155.7 ->
+  // 153.4 us); its natural allocation, 88 registers, leaves room for five.
+  // The gated loop would spill there and keeps its allocation.
+  constexpr int kNearWaves = G == 1 ? 6 : 1;
   if (near && gated) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true, true>), grid, dim3(kBlock), 0, stream, P);
-  else if (near) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true, false>), grid, dim3(kBlock), 0, stream, P);
+  else if (near)
+    hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, true, false, kNoExtra, kNearWaves>), grid, dim3(kBlock), 0, stream,
+                       P);
   else if (gated) hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false, true>), grid, dim3(kBlock), 0, stream, P);
   else hipLaunchKernelGGL((attend_kernel<D, KB, VB, G, false, false>), grid, dim3(kBlock), 0, stream, P);
   return hipGetLastError();
