@@ -791,6 +791,46 @@ def test_empty_context_gives_zero(dev):
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("S,SN", [(1, 0), (5, 3), (8, 0), (9, 0), (18, 5), (40, 0), (59, 5), (64, 0),
+                                  (65, 0), (100, 30), (130, 0)])
+def test_merge_alone(dev, d, S, SN):
+    """The merge launch on seeded split states, against the oracle's merge
+    ([Foveated] "Making it fast": split-K states combined after the fused
+    pass): near splits are in the original domain; far splits are mapped
+    back by R^T first, which the merge may defer to one rotation of their
+    weighted sum since R^T is linear.  Every split-count branch of the
+    kernel (all rows in one request, up to 64 splits, more than 64) with
+    empty splits (m = -inf, l = 0) mixed in."""
+    rng = np.random.default_rng(7100 + 13 * d + 7 * S + SN)
+    B, Hkv, Hq, n = 2, 2, 4, S + SN
+    m = rng.normal(0.0, 3.0, (B, Hq, n))
+    l = rng.uniform(0.5, 50.0, (B, Hq, n))
+    o = rng.standard_normal((B, Hq, n, d))
+    empty = rng.random((B, Hq, n)) < 0.15
+    empty[np.arange(B)[:, None], np.arange(Hq)[None, :], rng.integers(0, n, (B, Hq))] = False
+    m[empty], l[empty], o[empty] = -np.inf, 0.0, 0.0
+    m, l, o = m.astype(np.float32), l.astype(np.float32), o.astype(np.float32)
+    ml = np.stack([m, l], axis=-1)
+
+    cache = kvq.KVCache.allocate(B, Hkv, d, 32, seed=W.SIGN_SEED, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    out = cache.merge(_t(o, dev), _t(ml, dev), S, SN, lse=lse)
+    torch.cuda.synchronize()
+
+    s = _signs(d)
+    ref = np.zeros((B, Hq, d))
+    ref_lse = np.zeros((B, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            orig = o[b, h].astype(np.float64)
+            orig[SN:] = O.rotate_inverse(orig[SN:], s)
+            ref[b, h], ref_lse[b, h] = O.merge_partials(m[b, h].astype(np.float64), l[b, h].astype(np.float64), orig)
+    got = out.cpu().numpy()
+    assert np.abs(got - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max()), f"S={S} SN={SN}: {np.abs(got - ref).max():.3e}"
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-5, f"S={S} SN={SN}: lse"
+
+
 # ---------------------------------------------------------------------------
 # full sizes, launch configuration of the benchmark, sampled checks
 # ---------------------------------------------------------------------------
