@@ -369,6 +369,7 @@ def cpu_baseline(wl: W.Workload, inputs, seconds: float = 12.0) -> dict:
     by = cache_bytes(wl)
     t_quant = t_att = 0.0
     n_pairs = 0
+    att_times = []
     for b, h in pairs:
         kf, vf = kf_d[b, h].cpu().numpy(), vf_d[b, h].cpu().numpy()
         if kn_d is not None:
@@ -394,6 +395,7 @@ def cpu_baseline(wl: W.Workload, inputs, seconds: float = 12.0) -> dict:
         t2 = time.perf_counter()
         t_quant += t1 - t0
         t_att += t2 - t1
+        att_times.append(t2 - t1)
         n_pairs += 1
         if t_quant + t_att >= seconds:
             break
@@ -419,6 +421,9 @@ def cpu_baseline(wl: W.Workload, inputs, seconds: float = 12.0) -> dict:
                   f"(value), oracle quantize of the same pairs' keys and values (append_tokens_per_s)",
         "append_tokens_per_s": round(n_pairs * wl.seq_len / t_quant, 2),
         "seconds": round(t_quant + t_att, 2),
+        # each pair is one repetition of the same work; the first warms up
+        "pair_median_value": round(pair_bytes / float(np.median(att_times[1:] or att_times)) / 1e9, 4),
+        "pair_reps": len(att_times[1:] or att_times),
     }
 
 
