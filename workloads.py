@@ -14,7 +14,7 @@ buffer:
                      context 8192, fp16 K/V ~N(0,1), 4 key channels/head x20
   long_context       batch 1, 32/8 heads, d=128, context 32768, fp16 K/V with
                      per-head lognormal(0,1) channel scales on K and on V,
-                     64 split-K partitions
+                     32 split-K partitions
   bitwidth_sweep     batch 32, 16/16 heads, d=256, context 4096, fp16 K/V,
                      8 key channels/head x10, 2/3/4-bit codes
   two_tier           batch 16, 16/16 heads, d=128, context 16384, fp16 K/V;
@@ -112,7 +112,7 @@ WORKLOADS = {
                               splits=4, outlier_channels=4, outlier_scale=20.0),
     "long_context": Workload("long_context", 3, batch=1, q_heads=32, kv_heads=8,
                              head_dim=128, seq_len=32768, k_bits=4, v_bits=4, dtype="f16",
-                             splits=64, lognormal_sigma=1.0),
+                             splits=32, lognormal_sigma=1.0),
     "bitwidth_sweep": Workload("bitwidth_sweep", 4, batch=32, q_heads=16, kv_heads=16,
                                head_dim=256, seq_len=4096, k_bits=4, v_bits=4, dtype="f16",
                                splits=2, outlier_channels=8, outlier_scale=10.0),
